@@ -1,0 +1,261 @@
+"""Thin ctypes binding of libfp8kv.so.
+
+The three calls keep the C names (fp8kv_quantize_rows, fp8kv_decode_attn,
+fp8kv_prefill_attn).  This module only marshals arguments: it takes torch
+device tensors, checks dtypes/shapes that the C ABI cannot see, passes raw
+pointers and the current stream, and raises on a non-OK status.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+
+`Fp8KvPool` allocates one layer of the page-size-1 FP8 row pool with torch
+(device memory plumbing) and exposes it as the C `fp8kv_pool_layer` struct.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HEAD_DIM = 128
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8kv.so")
+_HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp8kv.h")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class Fp8KvError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {status_string(status)} (status {status})")
+
+
+class PoolLayer(ctypes.Structure):
+    """Mirror of `fp8kv_pool_layer` in include/fp8kv.h."""
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("num_rows", ctypes.c_int64),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("code_row_stride", ctypes.c_int64),
+        ("scale_row_stride", ctypes.c_int64),
+    ]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def header_path() -> str:
+    return _HEADER
+
+
+def load() -> ctypes.CDLL:
+    """Load libfp8kv.so; fails loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(PoolLayer)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.fp8kv_quantize_rows.argtypes = [P, vp, vp, i64, vp, i32, vp]
+    L.fp8kv_quantize_rows.restype = ctypes.c_int
+    L.fp8kv_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    L.fp8kv_decode_workspace_bytes.restype = sz
+    L.fp8kv_decode_attn.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp, vp]
+    L.fp8kv_decode_attn.restype = ctypes.c_int
+    L.fp8kv_prefill_attn.argtypes = [P, vp, vp, vp, i32, i32, vp, i32, vp, vp, i64, f32, vp, vp]
+    L.fp8kv_prefill_attn.restype = ctypes.c_int
+    L.fp8kv_status_string.argtypes = [ctypes.c_int]
+    L.fp8kv_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def declared_symbols() -> list:
+    """Function names declared in include/fp8kv.h."""
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8kv_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return load().fp8kv_status_string(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise Fp8KvError(status, call)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_check(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensors are passed to the ABI as their 16-bit patterns."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+# ------------------------------------------------------------------- pool --
+
+class Fp8KvPool:
+    """One layer of the page-size-1 FP8 row pool, allocated on the current device.
+
+    layout="separate": k_codes/v_codes uint8 [R][Hkv][128], k_scales/v_scales
+      float32 [R][Hkv] (four allocations).
+    layout="interleaved": one record per row holding K codes, V codes, K scales,
+      V scales back to back (rounded up to 16 bytes), so every byte of a row is
+      in one contiguous span.
+    """
+
+    def __init__(self, num_rows: int, n_kv_heads: int, layout: str = "separate",
+                 device: Optional[torch.device] = None):
+        dev = device or torch.device("cuda", torch.cuda.current_device())
+        self.num_rows, self.n_kv_heads, self.layout = int(num_rows), int(n_kv_heads), layout
+        H, D = self.n_kv_heads, HEAD_DIM
+        if layout == "separate":
+            self.k_codes = torch.zeros((num_rows, H, D), dtype=torch.uint8, device=dev)
+            self.v_codes = torch.zeros((num_rows, H, D), dtype=torch.uint8, device=dev)
+            self.k_scales = torch.zeros((num_rows, H), dtype=torch.float32, device=dev)
+            self.v_scales = torch.zeros((num_rows, H), dtype=torch.float32, device=dev)
+            code_stride, scale_stride = H * D, H
+            ptrs = [t.data_ptr() for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales)]
+            self._buffers = [self.k_codes, self.v_codes, self.k_scales, self.v_scales]
+        elif layout == "interleaved":
+            rec = -(-(2 * H * D + 2 * H * 4) // 16) * 16
+            self.record = torch.zeros((num_rows, rec), dtype=torch.uint8, device=dev)
+            self.k_codes = self.record[:, :H * D].view(num_rows, H, D)
+            self.v_codes = self.record[:, H * D:2 * H * D].view(num_rows, H, D)
+            base = self.record.data_ptr()
+            self.k_scales = None  # views of the record; read back with scales()
+            self.v_scales = None
+            code_stride, scale_stride = rec, rec // 4
+            ptrs = [base, base + H * D, base + 2 * H * D, base + 2 * H * D + 4 * H]
+            self._buffers = [self.record]
+        else:
+            raise ValueError(f"unknown pool layout {layout!r}")
+        self.layer = PoolLayer(ptrs[0], ptrs[1], ptrs[2], ptrs[3], self.num_rows, H, D,
+                               code_stride, scale_stride)
+
+    def scales(self):
+        """(k_scales, v_scales) as float32 [R][Hkv] tensors (copies for the interleaved layout)."""
+        if self.layout == "separate":
+            return self.k_scales, self.v_scales
+        H = self.n_kv_heads
+        off = 2 * H * HEAD_DIM
+        ks = self.record[:, off:off + 4 * H].contiguous().view(torch.float32)
+        vs = self.record[:, off + 4 * H:off + 8 * H].contiguous().view(torch.float32)
+        return ks, vs
+
+    def codes(self):
+        return self.k_codes.contiguous(), self.v_codes.contiguous()
+
+    def byte_size(self) -> int:
+        return sum(b.numel() * b.element_size() for b in self._buffers)
+
+
+# ------------------------------------------------------------------ calls --
+
+def fp8kv_quantize_rows(pool: Fp8KvPool, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor,
+                        stream=None) -> None:
+    """Quantize bf16 K/V rows [N][Hkv][128] into pool rows slots[N] (int32)."""
+    _dev_check(k, "k", torch.bfloat16)
+    _dev_check(v, "v", torch.bfloat16)
+    _dev_check(slots, "slots", torch.int32)
+    n = int(slots.numel())
+    if k.shape != v.shape or k.dim() != 3 or k.shape[0] != n or k.shape[1:] != (pool.n_kv_heads, HEAD_DIM):
+        raise ValueError(f"k/v must be [{n}][{pool.n_kv_heads}][{HEAD_DIM}], got {tuple(k.shape)} / {tuple(v.shape)}")
+    if k.stride(2) != 1 or k.stride(1) != HEAD_DIM or v.stride() != k.stride():
+        raise ValueError("k and v need contiguous heads and the same token stride")
+    st = load().fp8kv_quantize_rows(ctypes.byref(pool.layer), _ptr(_bits(k)), _ptr(_bits(v)), k.stride(0),
+                                    _ptr(slots), n, _stream(stream))
+    _check(st, "fp8kv_quantize_rows")
+
+
+def fp8kv_decode_workspace_bytes(batch: int, n_q_heads: int, max_splits: int = 0) -> int:
+    return int(load().fp8kv_decode_workspace_bytes(batch, n_q_heads, max_splits))
+
+
+def decode_workspace(batch: int, n_q_heads: int, max_splits: int = 0, device=None) -> torch.Tensor:
+    nbytes = fp8kv_decode_workspace_bytes(batch, n_q_heads, max_splits)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+def fp8kv_decode_attn(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                      max_seq_len: int, sm_scale: float, max_splits: int = 0,
+                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Decode attention: q bf16 [B][Hq][128], row_table int32 [B][stride], seq_lens int32 [B]."""
+    _dev_check(q, "q", torch.bfloat16)
+    _dev_check(row_table, "row_table", torch.int32)
+    _dev_check(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][Hq][128] bf16 tensor")
+    B, Hq, _ = q.shape
+    if row_table.dim() != 2 or row_table.shape[0] != B or row_table.stride(1) != 1:
+        raise ValueError("row_table must be [B][stride] with unit inner stride")
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, max_splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().fp8kv_decode_attn(ctypes.byref(pool.layer), _ptr(_bits(q)), B, Hq, _ptr(row_table),
+                                  row_table.stride(0), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+                                  int(max_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _ptr(_bits(out)), _stream(stream))
+    _check(st, "fp8kv_decode_attn")
+    return out
+
+
+def fp8kv_prefill_attn(pool: Fp8KvPool, q: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor,
+                       prefix_rows: Optional[torch.Tensor], ws_k: Optional[torch.Tensor],
+                       ws_v: Optional[torch.Tensor], sm_scale: float, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Prefill attention of a bf16 chunk over historical FP8 rows prefix_rows (int32 [P]).
+
+    ws_k / ws_v: bf16 workspaces of at least P rows of [Hkv][128] (shared across layers).
+    """
+    for name, t in (("q", q), ("k_cur", k_cur), ("v_cur", v_cur)):
+        _dev_check(t, name, torch.bfloat16)
+        if not t.is_contiguous() or t.dim() != 3 or t.shape[2] != HEAD_DIM:
+            raise ValueError(f"{name} must be a contiguous [T][H][128] bf16 tensor")
+    T, Hq, _ = q.shape
+    if k_cur.shape != (T, pool.n_kv_heads, HEAD_DIM) or v_cur.shape != k_cur.shape:
+        raise ValueError("k_cur/v_cur must be [T][Hkv][128]")
+    P = 0 if prefix_rows is None else int(prefix_rows.numel())
+    cap = 0
+    if P > 0:
+        _dev_check(prefix_rows, "prefix_rows", torch.int32)
+        for name, t in (("ws_k", ws_k), ("ws_v", ws_v)):
+            _dev_check(t, name, torch.bfloat16)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        cap = min(ws_k.numel(), ws_v.numel()) // (pool.n_kv_heads * HEAD_DIM)
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().fp8kv_prefill_attn(ctypes.byref(pool.layer), _ptr(_bits(q)), _ptr(_bits(k_cur)), _ptr(_bits(v_cur)),
+                                   T, Hq, _ptr(prefix_rows) if P else None, P,
+                                   _ptr(_bits(ws_k)) if P else None, _ptr(_bits(ws_v)) if P else None, cap,
+                                   float(sm_scale), _ptr(_bits(out)), _stream(stream))
+    _check(st, "fp8kv_prefill_attn")
+    return out

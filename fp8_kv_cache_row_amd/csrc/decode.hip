@@ -1,0 +1,284 @@
+// decode.hip -- split-K GQA decode attention over the page-size-1 FP8 row pool.
+//
+// FreeToken PR #897 "perf(attention): add packed fp8 kv reads on gfx1201",
+// description and "Fresh R9700 stage-1 A/B": a first stage computes one
+// partial per (head group, split) over FP8 rows fetched through the row table
+// (page size 1, randomized physical slots), a merge kernel combines the
+// partials; packed 4-byte-granular code reads and native converts.  FreeToken
+// PR #853 "What changes": per-row FP32 scales stored next to the codes.
+//
+// gfx950 design (not the pages' RDNA4 kernel):
+//  * One wave owns 32 keys of one KV head per step.  QK^T runs on the bf16
+//    MFMA 16x16x32 with the E4M3 codes widened exactly to bf16 (every finite
+//    E4M3FN value is a bf16 value); the per-row K scale and the softmax scale
+//    multiply the 16x16 score tile afterwards.  S^T = K * Q^T puts keys on the
+//    MFMA rows and the G query heads of the group on the columns, so each
+//    lane ends up with 8 keys of one head: the per-head tile max needs only
+//    two cross-lane steps.
+//  * Those 8 keys are exactly the k-slots the lane feeds to the P*V MFMA, so
+//    the probabilities (times the per-row V scale, folded into P) never move
+//    between lanes.  V is fetched as 8-byte row segments (16 lanes cover a
+//    128-byte head row) and byte-transposed in registers.
+//  * Every code byte of a row is loaded exactly once, with 16-byte (K) and
+//    8-byte (V) vector loads that cover whole 128-byte head rows per 16 lanes.
+//  * Stage 2 merges the per-split (o, log2-sum-exp) partials.
+#include <math.h>
+
+#include "fp8kv_device.h"
+
+namespace fp8kv {
+
+namespace {
+
+constexpr int kBlock = kDecodeWaves * kWave;
+
+// Key order inside a 32-key step: k-group j of the P*V contraction holds keys
+// 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
+__device__ __forceinline__ int step_key(int j, int r) { return (r < 4) ? 4 * j + r : 12 + 4 * j + r; }
+
+template <int G>
+__global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
+    int64_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
+    const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
+    int32_t n_split, int32_t chunk, float qk_scale_log2, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
+  static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int n = lane & 15;
+  const int j = lane >> 4;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = seq_lens[b];
+  const int key_begin = split * chunk;
+  const int key_end = min(key_begin + chunk, L);
+  const int h0 = g * G;
+
+  // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
+  // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
+  bf16x8 qb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (n < G) {
+      const uint16_t* qp = q + ((int64_t)b * n_q_heads + h0 + n) * kHeadDim + 64 * (kk >> 1) + 16 * j + 8 * (kk & 1);
+      u = *reinterpret_cast<const uint4*>(qp);
+    }
+    qb[kk] = u4_as_bf16x8(u);
+  }
+
+  float m_run = -INFINITY;  // running max (log2 units) of head n
+  float l_part = 0.0f;      // running sum of p for head n over this lane's keys
+  f32x4 o[8];               // O[head 4j+i][d = 8n + nb]
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* kbase = k_codes + (int64_t)g * kHeadDim;
+  const uint8_t* vbase = v_codes + (int64_t)g * kHeadDim;
+  const float* ksb = k_scales + g;
+  const float* vsb = v_scales + g;
+  const int32_t* trow = table + (int64_t)b * table_stride;
+
+  for (int t0 = key_begin + wave * kDecodeTileKeys; t0 < key_end; t0 += kDecodeWaves * kDecodeTileKeys) {
+    // Row indices of the 32 keys (lanes 32..63 repeat 0..31); keys past the
+    // end reuse the last valid row and are masked out of the softmax.
+    const int kidx = min(t0 + (lane & 31), key_end - 1);
+    const int row_l = trow[kidx];
+
+    // K rows: lane (n, j) reads bytes [16j, 16j+16) and [64+16j, 64+16j+16)
+    // of key n (block 0) and key 16+n (block 1).
+    const int rk0 = __shfl(row_l, n);
+    const int rk1 = __shfl(row_l, 16 + n);
+    const uint8_t* kp0 = kbase + (int64_t)rk0 * code_row_stride + 16 * j;
+    const uint8_t* kp1 = kbase + (int64_t)rk1 * code_row_stride + 16 * j;
+    const uint4 ka0 = *reinterpret_cast<const uint4*>(kp0);
+    const uint4 kb0 = *reinterpret_cast<const uint4*>(kp0 + 64);
+    const uint4 ka1 = *reinterpret_cast<const uint4*>(kp1);
+    const uint4 kb1 = *reinterpret_cast<const uint4*>(kp1 + 64);
+
+    // V rows and both scales for the lane's 8 keys: bytes [8n, 8n+8) of each.
+    uint2 vr[8];
+    float ks[8], vs[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t rv = __shfl(row_l, step_key(j, r));
+      vr[r] = *reinterpret_cast<const uint2*>(vbase + rv * code_row_stride + 8 * n);
+      ks[r] = ksb[rv * scale_row_stride];
+      vs[r] = vsb[rv * scale_row_stride];
+    }
+
+    // S^T = K * Q^T for the two 16-key blocks.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = mfma16x16x32(fp8x8_to_bf16x8(ka0.x, ka0.y), qb[0], s0);
+    s0 = mfma16x16x32(fp8x8_to_bf16x8(ka0.z, ka0.w), qb[1], s0);
+    s0 = mfma16x16x32(fp8x8_to_bf16x8(kb0.x, kb0.y), qb[2], s0);
+    s0 = mfma16x16x32(fp8x8_to_bf16x8(kb0.z, kb0.w), qb[3], s0);
+    s1 = mfma16x16x32(fp8x8_to_bf16x8(ka1.x, ka1.y), qb[0], s1);
+    s1 = mfma16x16x32(fp8x8_to_bf16x8(ka1.z, ka1.w), qb[1], s1);
+    s1 = mfma16x16x32(fp8x8_to_bf16x8(kb1.x, kb1.y), qb[2], s1);
+    s1 = mfma16x16x32(fp8x8_to_bf16x8(kb1.z, kb1.w), qb[3], s1);
+
+    // Scores in log2 units for head n, keys step_key(j, r).
+    float sc[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float raw = (r < 4) ? s0[r] : s1[r - 4];
+      const bool valid = (t0 + step_key(j, r)) < key_end;
+      sc[r] = valid ? raw * ks[r] * qk_scale_log2 : -INFINITY;
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, sc[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+
+    float p[8], psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      p[r] = exp2f(sc[r] - m_new);
+      psum += p[r];
+    }
+    l_part = l_part * alpha + psum;
+
+    // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
+    uint4 pu;
+    pu.x = f32x2_to_bf16x2(p[0] * vs[0], p[1] * vs[1]);
+    pu.y = f32x2_to_bf16x2(p[2] * vs[2], p[3] * vs[3]);
+    pu.z = f32x2_to_bf16x2(p[4] * vs[4], p[5] * vs[5]);
+    pu.w = f32x2_to_bf16x2(p[6] * vs[6], p[7] * vs[7]);
+    const bf16x8 pa = u4_as_bf16x8(pu);
+
+    // Rescale O rows (heads 4j+i) by their head's alpha.
+    float ai[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
+    }
+
+    // V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
+    // V[key][d = 8n + nb] for the lane's 8 keys.
+    uint32_t lo[8], hi[8];
+    transpose4x4_bytes(vr[0].x, vr[1].x, vr[2].x, vr[3].x, lo[0], lo[1], lo[2], lo[3]);
+    transpose4x4_bytes(vr[4].x, vr[5].x, vr[6].x, vr[7].x, hi[0], hi[1], hi[2], hi[3]);
+    transpose4x4_bytes(vr[0].y, vr[1].y, vr[2].y, vr[3].y, lo[4], lo[5], lo[6], lo[7]);
+    transpose4x4_bytes(vr[4].y, vr[5].y, vr[6].y, vr[7].y, hi[4], hi[5], hi[6], hi[7]);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
+  }
+
+  // Per-head totals of this wave.
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+
+  __shared__ float sm_m[kDecodeWaves][16];
+  __shared__ float sm_l[kDecodeWaves][16];
+  __shared__ float sm_o[kDecodeWaves][G][kHeadDim];
+  if (j == 0) {
+    sm_m[wave][n] = m_run;
+    sm_l[wave][n] = l_tot;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int head = 4 * j + i;
+    if (head < G) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) sm_o[wave][head][8 * n + nb] = o[nb][i];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves of this workgroup into one partial per query head.
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kBlock) {
+    const int h = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float oval = 0.0f, lse = -INFINITY;
+    if (M != -INFINITY) {
+      float num = 0.0f, den = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float wt = exp2f(sm_m[w][h] - M);
+        num += wt * sm_o[w][h][d];
+        den += wt * sm_l[w][h];
+      }
+      oval = num / den;
+      lse = M + log2f(den);
+    }
+    const int64_t ph = ((int64_t)b * n_q_heads + h0 + h) * n_split + split;
+    part_o[ph * kHeadDim + d] = oval;
+    if (d == 0) part_lse[ph] = lse;
+  }
+}
+
+// Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
+__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* __restrict__ part_o,
+                                                                 const float* __restrict__ part_lse,
+                                                                 int32_t n_split, uint16_t* __restrict__ out) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* lse = part_lse + bh * n_split;
+  const float* po = part_o + bh * n_split * kHeadDim + d;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, lse[s]);
+  float r = 0.0f;
+  if (M != -INFINITY) {
+    float num = 0.0f, den = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+      const float w = exp2f(lse[s] - M);
+      num += w * po[(int64_t)s * kHeadDim];
+      den += w;
+    }
+    r = num / den;
+  }
+  const __bf16 h = (__bf16)r;
+  out[bh * kHeadDim + d] = __builtin_bit_cast(uint16_t, h);
+}
+
+template <int G>
+hipError_t launch_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                         const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                         float qk_scale_log2, const DecodeGeometry& geo, float* part_o, float* part_lse,
+                         hipStream_t stream) {
+  dim3 grid((unsigned)geo.n_split, (unsigned)pool.n_kv_heads, (unsigned)batch);
+  hipLaunchKernelGGL(decode_stage1_kernel<G>, grid, dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
+                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride, q, n_q_heads,
+                     row_table, table_stride, seq_lens, geo.n_split, geo.chunk, qk_scale_log2, part_o,
+                     part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                         const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                         float sm_scale, const DecodeGeometry& geo, float* part_o, float* part_lse,
+                         uint16_t* out, hipStream_t stream) {
+  const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
+  const int G = n_q_heads / pool.n_kv_heads;
+  hipError_t e;
+  switch (G) {
+    case 1: e = launch_stage1<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
+    case 2: e = launch_stage1<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
+    case 4: e = launch_stage1<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
+    case 8: e = launch_stage1<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
+    case 16: e = launch_stage1<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kHeadDim), 0,
+                     stream, part_o, part_lse, geo.n_split, out);
+  return hipGetLastError();
+}
+
+}  // namespace fp8kv

@@ -1,0 +1,195 @@
+// fp8kv_api.hip -- the extern "C" boundary of libfp8kv.so (declared in fp8kv.h).
+//
+// Every check that does not need device memory happens here, before anything
+// is enqueued (FreeToken PR #853, "What changes": unsupported combinations are
+// rejected up front; PR #897 description: the packed reader requires 16-byte
+// aligned bases and row strides).  Kernels live in quantize.hip, decode.hip and
+// prefill.hip.
+#include <mutex>
+#include <string.h>
+
+#include "fp8kv.h"
+#include "fp8kv_launch.h"
+
+namespace {
+
+using fp8kv::PoolView;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_group(int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return false;
+  const int32_t g = n_q_heads / n_kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+}
+
+fp8kv_status check_pool(const fp8kv_pool_layer* p) {
+  if (!p || !p->k_codes || !p->v_codes || !p->k_scales || !p->v_scales) return FP8KV_ERR_INVALID_ARG;
+  if (p->num_rows <= 0 || p->n_kv_heads <= 0) return FP8KV_ERR_INVALID_ARG;
+  if (p->head_dim != FP8KV_HEAD_DIM) return FP8KV_ERR_UNSUPPORTED;
+  if (p->code_row_stride < (int64_t)p->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
+  if (p->scale_row_stride < p->n_kv_heads) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(p->k_codes, 16) || !aligned(p->v_codes, 16) || (p->code_row_stride % 16) != 0)
+    return FP8KV_ERR_ALIGNMENT;
+  if (!aligned(p->k_scales, 4) || !aligned(p->v_scales, 4)) return FP8KV_ERR_ALIGNMENT;
+  return FP8KV_OK;
+}
+
+PoolView view_of(const fp8kv_pool_layer* p) {
+  return PoolView{p->k_codes, p->v_codes, p->k_scales, p->v_scales, p->code_row_stride, p->scale_row_stride,
+                  p->n_kv_heads};
+}
+
+// Per-device facts, queried once: gfx950 or not, and the compute-unit count.
+struct DeviceInfo {
+  bool known = false;
+  bool gfx950 = false;
+  int n_cu = 0;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+fp8kv_status current_device(int* n_cu) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8KV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& info = g_dev[dev];
+  if (!info.known) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8KV_ERR_HIP;
+    info.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    info.n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+    info.known = true;
+  }
+  if (!info.gfx950) return FP8KV_ERR_UNSUPPORTED;
+  if (n_cu) *n_cu = info.n_cu;
+  return FP8KV_OK;
+}
+
+int32_t split_cap(int32_t max_splits) {
+  return (max_splits > 0 && max_splits < FP8KV_MAX_SPLITS) ? max_splits : FP8KV_MAX_SPLITS;
+}
+
+// Split choice: about two stage-1 workgroups per compute unit across the
+// batch, each wave of a workgroup getting at least one 32-key step.
+fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
+                                      int32_t max_splits, int n_cu) {
+  const int64_t unit = (int64_t)fp8kv::kDecodeWaves * fp8kv::kDecodeTileKeys;
+  const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
+  const int64_t per = (int64_t)batch * n_kv_heads;
+  const int64_t target = 2 * (int64_t)n_cu;
+  int64_t want = (target + per - 1) / per;
+  if (want < 1) want = 1;
+  int64_t ns = want;
+  if (ns > split_cap(max_splits)) ns = split_cap(max_splits);
+  const int64_t useful = (L + unit - 1) / unit;
+  if (ns > useful) ns = useful;
+  int64_t chunk = (L + ns - 1) / ns;
+  chunk = (chunk + unit - 1) / unit * unit;
+  ns = (L + chunk - 1) / chunk;
+  return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk};
+}
+
+size_t partial_bytes(int64_t batch, int64_t n_q_heads, int64_t n_split) {
+  return (size_t)(batch * n_q_heads * n_split) * (FP8KV_HEAD_DIM + 1) * sizeof(float);
+}
+
+fp8kv_status from_hip(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+fp8kv_status fp8kv_quantize_rows(const fp8kv_pool_layer* pool, const uint16_t* k, const uint16_t* v,
+                                 int64_t src_token_stride, const int32_t* slots, int32_t n_tokens,
+                                 void* stream) {
+  fp8kv_status st = check_pool(pool);
+  if (st != FP8KV_OK) return st;
+  if (n_tokens < 0) return FP8KV_ERR_INVALID_ARG;
+  if (n_tokens == 0) return FP8KV_OK;
+  if (!k || !v || !slots) return FP8KV_ERR_INVALID_ARG;
+  if (src_token_stride < (int64_t)pool->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
+  if ((src_token_stride % 8) != 0 || !aligned(k, 16) || !aligned(v, 16)) return FP8KV_ERR_ALIGNMENT;
+  if (!aligned(slots, 4)) return FP8KV_ERR_ALIGNMENT;
+  st = current_device(nullptr);
+  if (st != FP8KV_OK) return st;
+  return from_hip(fp8kv::launch_quantize_rows(view_of(pool), k, v, src_token_stride, slots, n_tokens,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_splits) {
+  if (batch <= 0 || n_q_heads <= 0 || max_splits < 0) return 0;
+  return partial_bytes(batch, n_q_heads, split_cap(max_splits));
+}
+
+fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                               int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                               const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                               int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
+                               void* stream) {
+  fp8kv_status st = check_pool(pool);
+  if (st != FP8KV_OK) return st;
+  if (!q || !row_table || !seq_lens || !out) return FP8KV_ERR_INVALID_ARG;
+  if (batch <= 0 || max_seq_len < 0 || max_splits < 0 || table_stride < max_seq_len || table_stride <= 0)
+    return FP8KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
+  if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
+  if (!(sm_scale == sm_scale)) return FP8KV_ERR_INVALID_ARG;  // NaN
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4))
+    return FP8KV_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < fp8kv_decode_workspace_bytes(batch, n_q_heads, max_splits))
+    return FP8KV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return FP8KV_ERR_ALIGNMENT;
+  int n_cu = 0;
+  st = current_device(&n_cu);
+  if (st != FP8KV_OK) return st;
+  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + (size_t)batch * n_q_heads * geo.n_split * FP8KV_HEAD_DIM;
+  return from_hip(fp8kv::launch_decode(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
+                                       sm_scale, geo, part_o, part_lse, out, static_cast<hipStream_t>(stream)));
+}
+
+fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q, const uint16_t* k_cur,
+                                const uint16_t* v_cur, int32_t n_tokens, int32_t n_q_heads,
+                                const int32_t* prefix_rows, int32_t n_prefix, uint16_t* ws_k, uint16_t* ws_v,
+                                int64_t ws_capacity_rows, float sm_scale, uint16_t* out, void* stream) {
+  fp8kv_status st = check_pool(pool);
+  if (st != FP8KV_OK) return st;
+  if (!q || !k_cur || !v_cur || !out) return FP8KV_ERR_INVALID_ARG;
+  if (n_tokens <= 0 || n_prefix < 0) return FP8KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
+  if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
+  if (!(sm_scale == sm_scale)) return FP8KV_ERR_INVALID_ARG;
+  if (n_prefix > 0) {
+    if (!prefix_rows) return FP8KV_ERR_INVALID_ARG;
+    if (!ws_k || !ws_v || ws_capacity_rows < n_prefix) return FP8KV_ERR_WORKSPACE;
+    if (!aligned(ws_k, 16) || !aligned(ws_v, 16) || !aligned(prefix_rows, 4)) return FP8KV_ERR_ALIGNMENT;
+  }
+  if (!aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16) || !aligned(out, 16))
+    return FP8KV_ERR_ALIGNMENT;
+  st = current_device(nullptr);
+  if (st != FP8KV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_prefix > 0) {
+    hipError_t e = fp8kv::launch_reconstruct(view_of(pool), prefix_rows, n_prefix, ws_k, ws_v, s);
+    if (e != hipSuccess) return FP8KV_ERR_HIP;
+  }
+  return from_hip(fp8kv::launch_prefill_attention(q, ws_k, ws_v, k_cur, v_cur, n_prefix, n_tokens, n_q_heads,
+                                                  pool->n_kv_heads, sm_scale, out, s));
+}
+
+const char* fp8kv_status_string(fp8kv_status status) {
+  switch (status) {
+    case FP8KV_OK: return "FP8KV_OK";
+    case FP8KV_ERR_INVALID_ARG: return "FP8KV_ERR_INVALID_ARG: null pointer or invalid size";
+    case FP8KV_ERR_UNSUPPORTED: return "FP8KV_ERR_UNSUPPORTED: head_dim, GQA ratio or device not supported";
+    case FP8KV_ERR_ALIGNMENT: return "FP8KV_ERR_ALIGNMENT: pointer or stride breaks the alignment contract";
+    case FP8KV_ERR_WORKSPACE: return "FP8KV_ERR_WORKSPACE: workspace missing or too small";
+    case FP8KV_ERR_HIP: return "FP8KV_ERR_HIP: HIP runtime error";
+  }
+  return "FP8KV_ERR_UNKNOWN";
+}
+
+}  // extern "C"

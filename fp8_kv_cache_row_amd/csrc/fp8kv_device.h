@@ -1,0 +1,92 @@
+// fp8kv_device.h -- device-side helpers shared by the gfx950 kernels of libfp8kv.
+//
+// Everything here is CDNA4-specific: wave64, the packed FP8 <-> f32 / bf16
+// converts added for OCP E4M3FN on gfx950, and the bf16 MFMA 16x16x32 layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8kv_launch.h"
+
+namespace fp8kv {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kHeadDim = 128;
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> f32 (exact widening).
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two E4M3FN codes (bytes 0,1 or 2,3 of w) -> two bf16 packed in one dword.
+// Every finite E4M3FN value is exact in bf16, so this is an exact widening.
+// The scaled convert with scale 1.0 leaves values unchanged.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Four E4M3FN codes in one dword -> bf16 x4 in two dwords (byte k -> element k).
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  return make_uint2(fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w));
+}
+
+// Eight codes (two dwords) -> MFMA bf16x8 operand (byte k -> element k).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  uint2 a = fp8x4_to_bf16x4(lo), b = fp8x4_to_bf16x4(hi);
+  uint4 u = make_uint4(a.x, a.y, b.x, b.y);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 u4_as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Two f32 -> two bf16 (round to nearest even) packed in one dword.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  bf16x2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two f32 -> two E4M3FN codes written into half HI of `old` (round to
+// nearest even; callers clamp to +-448 first so saturation is explicit).
+template <bool HI>
+__device__ __forceinline__ uint32_t f32x2_to_fp8x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// Four E4M3FN codes in one dword -> four f32.
+__device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float* o) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
+}
+
+// v_mfma_f32_16x16x32_bf16: D(16x16) += A(16x32) * B(32x16).
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each as eight
+// consecutive k-slots of k-group (l / 16); it receives D rows 4*(l/16)+i,
+// column l % 16, i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4x4 byte transpose across four dwords: out[k] byte r = in[r] byte k.
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                   uint32_t& o0, uint32_t& o1, uint32_t& o2,
+                                                   uint32_t& o3) {
+  // __builtin_amdgcn_perm(hi, lo, sel): bytes 0-3 come from lo, 4-7 from hi.
+  uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  uint32_t ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  uint32_t cd01 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  uint32_t cd23 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o0 = __builtin_amdgcn_perm(cd01, ab01, 0x05040100u);       // a0 b0 c0 d0
+  o1 = __builtin_amdgcn_perm(cd01, ab01, 0x07060302u);       // a1 b1 c1 d1
+  o2 = __builtin_amdgcn_perm(cd23, ab23, 0x05040100u);       // a2 b2 c2 d2
+  o3 = __builtin_amdgcn_perm(cd23, ab23, 0x07060302u);       // a3 b3 c3 d3
+}
+
+}  // namespace fp8kv

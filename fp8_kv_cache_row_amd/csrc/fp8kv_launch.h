@@ -1,0 +1,47 @@
+// fp8kv_launch.h -- internal launch entry points of the gfx950 kernels.
+// The C ABI (fp8kv_api.hip) validates every argument before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8kv {
+
+struct PoolView {
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_scales;
+  float* v_scales;
+  int64_t code_row_stride;   // bytes
+  int64_t scale_row_stride;  // floats
+  int32_t n_kv_heads;
+};
+
+// Decode launch geometry: each workgroup covers `chunk` consecutive logical
+// rows of one (request, KV head); `n_split` workgroups per (request, KV head).
+struct DecodeGeometry {
+  int32_t n_split;
+  int32_t chunk;  // multiple of kDecodeTileKeys * kDecodeWaves
+};
+
+constexpr int kDecodeWaves = 4;      // waves per stage-1 workgroup
+constexpr int kDecodeTileKeys = 32;  // keys per wave per MFMA step
+
+hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const uint16_t* v,
+                                int64_t src_token_stride, const int32_t* slots, int32_t n_tokens,
+                                hipStream_t stream);
+
+hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, int32_t n_prefix,
+                              uint16_t* ws_k, uint16_t* ws_v, hipStream_t stream);
+
+hipError_t launch_decode(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                         const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                         float sm_scale, const DecodeGeometry& geo, float* part_o, float* part_lse,
+                         uint16_t* out, hipStream_t stream);
+
+hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* ws_k, const uint16_t* ws_v,
+                                    const uint16_t* k_cur, const uint16_t* v_cur, int32_t n_prefix,
+                                    int32_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                    float sm_scale, uint16_t* out, hipStream_t stream);
+
+}  // namespace fp8kv

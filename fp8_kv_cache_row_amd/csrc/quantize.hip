@@ -1,0 +1,125 @@
+// quantize.hip -- quantize-on-write of K/V rows and the prefill reconstruction.
+//
+// FreeToken PR #853 "opt-in FP8 KV cache", "What changes": each physical K/V
+// row stores E4M3 codes as bytes plus its own FP32 scale; the prefill path
+// rebuilds historical FP8 rows once per layer into a shared BF16 workspace.
+// "Follow-up model/workload search": the FP8 path quantizes every new K/V row.
+//
+// Both kernels give one 128-element row to 16 lanes (8 elements, 16 bytes of
+// bf16 or 8 bytes of codes per lane), so a wave handles 4 rows with fully
+// coalesced 256-byte / 128-byte row accesses and the row reduction stays
+// inside a 16-lane DPP row.
+#include "fp8kv_device.h"
+
+namespace fp8kv {
+
+namespace {
+
+constexpr int kLanesPerRow = 16;
+constexpr int kBlock = 256;
+constexpr int kRowsPerBlock = kBlock / kLanesPerRow;
+
+// Rows are enumerated as ((token * 2 + kv) * n_kv_heads + head), kv 0 = K, 1 = V.
+__global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_token_stride,
+    const int32_t* __restrict__ slots, int64_t n_rows, int32_t n_kv_heads, uint8_t* __restrict__ k_codes,
+    uint8_t* __restrict__ v_codes, float* __restrict__ k_scales, float* __restrict__ v_scales,
+    int64_t code_row_stride, int64_t scale_row_stride) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
+  const int sub = threadIdx.x % kLanesPerRow;
+  if (row >= n_rows) return;  // whole 16-lane groups leave together
+  const int32_t g = (int32_t)(row % n_kv_heads);
+  const int64_t tk = row / n_kv_heads;
+  const int kv = (int)(tk & 1);
+  const int64_t t = tk >> 1;
+
+  const uint16_t* src = (kv ? v : k) + t * src_token_stride + (int64_t)g * kHeadDim + sub * 8;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+  float x[8] = {bf16lo_to_f32(raw.x), bf16hi_to_f32(raw.x), bf16lo_to_f32(raw.y), bf16hi_to_f32(raw.y),
+                bf16lo_to_f32(raw.z), bf16hi_to_f32(raw.z), bf16lo_to_f32(raw.w), bf16hi_to_f32(raw.w)};
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kLanesPerRow));
+
+  // s = amax / 448 with an IEEE division (the library is built with correctly
+  // rounded fp32 division); each element is divided by s, again exactly
+  // rounded, clamped to the E4M3FN range and rounded to nearest even by the
+  // hardware convert.  An all-zero row keeps s = 0 and signed-zero codes.
+  const float s = amax / 448.0f;
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = (amax == 0.0f) ? x[i] : x[i] / s;
+    y[i] = fminf(fmaxf(q, -448.0f), 448.0f);
+  }
+  uint32_t lo = f32x2_to_fp8x2<false>(y[0], y[1], 0u);
+  lo = f32x2_to_fp8x2<true>(y[2], y[3], lo);
+  uint32_t hi = f32x2_to_fp8x2<false>(y[4], y[5], 0u);
+  hi = f32x2_to_fp8x2<true>(y[6], y[7], hi);
+
+  const int64_t slot = slots[t];
+  uint8_t* dst = (kv ? v_codes : k_codes) + slot * code_row_stride + (int64_t)g * kHeadDim + sub * 8;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  if (sub == 0) (kv ? v_scales : k_scales)[slot * scale_row_stride + g] = s;
+}
+
+// Rows enumerated as ((j * 2 + kv) * n_kv_heads + head) for prefix position j.
+// ws[j][head][d] = bf16_rne(fl32(decode(code) * scale)).
+__global__ __launch_bounds__(kBlock) void reconstruct_kernel(
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
+    int64_t scale_row_stride, const int32_t* __restrict__ prefix_rows, int64_t n_rows, int32_t n_kv_heads,
+    uint16_t* __restrict__ ws_k, uint16_t* __restrict__ ws_v) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
+  const int sub = threadIdx.x % kLanesPerRow;
+  if (row >= n_rows) return;
+  const int32_t g = (int32_t)(row % n_kv_heads);
+  const int64_t jk = row / n_kv_heads;
+  const int kv = (int)(jk & 1);
+  const int64_t j = jk >> 1;
+  const int64_t prow = prefix_rows[j];
+
+  const uint8_t* src = (kv ? v_codes : k_codes) + prow * code_row_stride + (int64_t)g * kHeadDim + sub * 8;
+  const uint2 c = *reinterpret_cast<const uint2*>(src);
+  const float s = (kv ? v_scales : k_scales)[prow * scale_row_stride + g];
+  float f[8];
+  fp8x4_to_f32x4(c.x, f);
+  fp8x4_to_f32x4(c.y, f + 4);
+  uint4 o;
+  o.x = f32x2_to_bf16x2(f[0] * s, f[1] * s);
+  o.y = f32x2_to_bf16x2(f[2] * s, f[3] * s);
+  o.z = f32x2_to_bf16x2(f[4] * s, f[5] * s);
+  o.w = f32x2_to_bf16x2(f[6] * s, f[7] * s);
+  uint16_t* dst = (kv ? ws_v : ws_k) + (j * n_kv_heads + g) * kHeadDim + sub * 8;
+  *reinterpret_cast<uint4*>(dst) = o;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const uint16_t* v,
+                                int64_t src_token_stride, const int32_t* slots, int32_t n_tokens,
+                                hipStream_t stream) {
+  const int64_t n_rows = (int64_t)n_tokens * 2 * pool.n_kv_heads;
+  if (n_rows == 0) return hipSuccess;
+  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
+                     src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
+                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, int32_t n_prefix,
+                              uint16_t* ws_k, uint16_t* ws_v, hipStream_t stream) {
+  const int64_t n_rows = (int64_t)n_prefix * 2 * pool.n_kv_heads;
+  if (n_rows == 0) return hipSuccess;
+  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(reconstruct_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, pool.k_codes,
+                     pool.v_codes, pool.k_scales, pool.v_scales, pool.code_row_stride,
+                     pool.scale_row_stride, prefix_rows, n_rows, pool.n_kv_heads, ws_k, ws_v);
+  return hipGetLastError();
+}
+
+}  // namespace fp8kv

@@ -1,0 +1,200 @@
+/*
+ * fp8kv.h -- C ABI of libfp8kv.so: an FP8 (OCP E4M3FN) per-row KV cache and the
+ * GQA attention that reads it, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow FreeToken PR #853 "opt-in FP8 KV cache", section "What
+ * changes": each physical K/V row stores E4M3 code bytes plus its own FP32
+ * scale; decode attention reads those rows directly; prefill rebuilds the
+ * historical FP8 rows once per layer into one shared BF16 workspace while the
+ * current chunk's K/V stay BF16.  FreeToken PR #897 "perf(attention): add packed
+ * fp8 kv reads on gfx1201" (description; "Fresh R9700 stage-1 A/B") fixes the
+ * decode case: BF16 query, head dim 128, GQA 4/8, page size 1 with randomized
+ * physical slots, a split-K first stage and a merge kernel.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, copies nothing between host and device and never
+ *    synchronizes.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    null stream) and the call returns immediately, so calls may be captured
+ *    into a HIP graph.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Every argument that can be checked without reading device memory is
+ *    checked on the host before anything is enqueued; on error nothing is
+ *    launched and nothing is written.  Device-resident contents (row indices in
+ *    tables and slot lists, sequence lengths, finiteness of inputs) are
+ *    preconditions: an out-of-range row index is undefined behaviour.
+ *  - Functions are stateless apart from a per-device cache of the compute-unit
+ *    count; they are thread-safe and may run concurrently on different streams
+ *    as long as their output buffers do not overlap.
+ *  - The library runs on gfx950 only; on other devices calls return
+ *    FP8KV_ERR_UNSUPPORTED.
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head dimension of every K/V row (the pages qualify only D = 128). */
+#define FP8KV_HEAD_DIM 128
+/* Largest finite E4M3FN magnitude; a row's scale is amax / FP8KV_E4M3_MAX. */
+#define FP8KV_E4M3_MAX 448.0f
+/* Upper bound on decode key-splits per (request, KV head). */
+#define FP8KV_MAX_SPLITS 256
+
+typedef enum fp8kv_status {
+    FP8KV_OK = 0,
+    FP8KV_ERR_INVALID_ARG = 1, /* null pointer, non-positive or inconsistent size */
+    FP8KV_ERR_UNSUPPORTED = 2, /* head_dim != 128, unsupported GQA ratio, not gfx950 */
+    FP8KV_ERR_ALIGNMENT = 3,   /* a base pointer or stride breaks the alignment contract */
+    FP8KV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    FP8KV_ERR_HIP = 5          /* the HIP runtime rejected a launch or a query */
+} fp8kv_status;
+
+/*
+ * One layer of the page-size-1 FP8 row pool (FreeToken PR #853, "What
+ * changes": every physical K/V row holds E4M3 code bytes plus its own FP32
+ * scale; issue #280, "Current proof-of-concept limitations": dynamic scales per
+ * token and per KV head).
+ *
+ * Physical row r, KV head g:
+ *   K codes   k_codes  + r * code_row_stride + g * 128   (128 bytes)
+ *   V codes   v_codes  + r * code_row_stride + g * 128   (128 bytes)
+ *   K scale   k_scales[r * scale_row_stride + g]         (fp32)
+ *   V scale   v_scales[r * scale_row_stride + g]         (fp32)
+ * Value of element d: decode_e4m3fn(code[d]) * scale.
+ *
+ * Alignment contract (FreeToken PR #897 description: packed reads need
+ * 16-byte-aligned bases and row/head strides): k_codes, v_codes and
+ * code_row_stride are multiples of 16 bytes; k_scales and v_scales are 4-byte
+ * aligned.  code_row_stride >= n_kv_heads * 128 and scale_row_stride >=
+ * n_kv_heads.  Strides let the four arrays be separate allocations or
+ * interleave inside one per-row record.
+ */
+typedef struct fp8kv_pool_layer {
+    uint8_t *k_codes;
+    uint8_t *v_codes;
+    float *k_scales;
+    float *v_scales;
+    int64_t num_rows;         /* physical rows in the pool */
+    int32_t n_kv_heads;       /* KV heads per row */
+    int32_t head_dim;         /* must be FP8KV_HEAD_DIM */
+    int64_t code_row_stride;  /* bytes between rows of k_codes / v_codes */
+    int64_t scale_row_stride; /* floats between rows of k_scales / v_scales */
+} fp8kv_pool_layer;
+
+/*
+ * fp8kv_quantize_rows -- quantize-on-write of new K/V rows (FreeToken PR #853,
+ * "Follow-up model/workload search": the FP8 path quantizes each new K/V row;
+ * "What changes": each row stores E4M3 codes plus its own FP32 scale).
+ *
+ * For token t in [0, n_tokens), KV head g, separately for K and V, with x the
+ * 128 bf16 values at k + t * src_token_stride + g * 128 (resp. v):
+ *   amax = max_d |x_d|;   s = fl32(amax / 448)   (IEEE fp32 division)
+ *   code_d = E4M3FN round-to-nearest-even of fl32(x_d / s), saturated to +-448
+ *   (a row with amax == 0 stores s = 0 and codes +0 / -0 following x_d's sign)
+ * and stores the codes and s at physical row slots[t].
+ *
+ * k, v:            device bf16 [n_tokens][n_kv_heads][128] with token stride
+ *                  src_token_stride elements (>= n_kv_heads*128, a multiple of
+ *                  8); bases 16-byte aligned.
+ * slots:           device int32 [n_tokens], each in [0, pool->num_rows); slots
+ *                  must be distinct within one call.
+ * n_tokens:        >= 0 (0 is a no-op).
+ * Errors: INVALID_ARG (null pointer, bad sizes), UNSUPPORTED, ALIGNMENT, HIP.
+ */
+fp8kv_status fp8kv_quantize_rows(const fp8kv_pool_layer *pool, const uint16_t *k, const uint16_t *v,
+                                 int64_t src_token_stride, const int32_t *slots, int32_t n_tokens,
+                                 void *stream);
+
+/*
+ * Bytes of device workspace fp8kv_decode_attn needs for `batch` requests of
+ * `n_q_heads` query heads with at most `max_splits` splits per request
+ * (0 = FP8KV_MAX_SPLITS).  Holds the split partials (an fp32 output vector and
+ * a log-sum-exp per request, query head and split).  Returns 0 for invalid
+ * arguments.
+ */
+size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_splits);
+
+/*
+ * fp8kv_decode_attn -- one-token-per-request GQA attention over the FP8 pool
+ * (FreeToken PR #897 description and "Fresh R9700 stage-1 A/B": BF16 query,
+ * D = 128, GQA 4/8, page size 1, split-K stage 1 timed apart from the merge
+ * kernel; PR #853 "What changes": rows hold E4M3 codes and per-row FP32 scales).
+ *
+ * For request b and query head h, with G = n_q_heads / n_kv_heads, KV head
+ * g = h / G, L = seq_lens[b] and rows r_t = row_table[b * table_stride + t]:
+ *   z_t   = sm_scale * sum_d q[b][h][d] * decode(Kcode[r_t][g][d]) * k_scale[r_t][g]
+ *   out[b][h] = sum_t softmax(z)_t * decode(Vcode[r_t][g]) * v_scale[r_t][g]
+ * rounded to bf16.  A request with L == 0 gets zeros.
+ *
+ * Stage 1 splits each request's rows into at most `max_splits` (0 = chosen
+ * from the device's compute-unit count and max_seq_len) ranges and writes one
+ * partial per (request, query head, split) into `workspace`; stage 2 merges
+ * them by log-sum-exp into `out`.  Results agree to rounding for every split
+ * count.
+ *
+ * q:            device bf16 [batch][n_q_heads][128], contiguous, 16-byte aligned.
+ * row_table:    device int32, row b at row_table + b * table_stride; entries
+ *               [0, seq_lens[b]) are physical rows of `pool`.
+ * seq_lens:     device int32 [batch], each in [0, max_seq_len].
+ * max_seq_len:  host-side upper bound on seq_lens (sizes the launch), >= 0,
+ *               <= table_stride.
+ * n_q_heads:    a multiple of pool->n_kv_heads with G in {1, 2, 4, 8, 16}.
+ * workspace:    device, 256-byte aligned, >= fp8kv_decode_workspace_bytes(
+ *               batch, n_q_heads, max_splits) bytes; contents are scratch.
+ * out:          device bf16 [batch][n_q_heads][128], 16-byte aligned.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP.
+ */
+fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                               int32_t n_q_heads, const int32_t *row_table, int64_t table_stride,
+                               const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                               int32_t max_splits, void *workspace, size_t workspace_bytes,
+                               uint16_t *out, void *stream);
+
+/*
+ * fp8kv_prefill_attn -- attention of one prefill chunk over historical FP8 rows
+ * (FreeToken PR #853, "What changes": the prefill path reconstructs historical
+ * FP8 rows once per layer into one shared BF16 workspace; current-chunk K/V
+ * remain BF16; "Paired end-to-end A/B": the 8K historical-prefix + 8K
+ * new-token operator).
+ *
+ * Step 1 (reconstruct): for j in [0, n_prefix), KV head g, d in [0, 128):
+ *   ws_k[j][g][d] = bf16_rne(fl32(decode(Kcode[prefix_rows[j]][g][d]) * k_scale))
+ *   and the same for ws_v from the V codes and scales.
+ * Step 2 (attention): chunk query i (absolute position n_prefix + i) attends
+ *   to keys/values [ws rows 0..n_prefix-1 ; chunk rows 0..i] (causal), with
+ *   KV head g = h / (n_q_heads / n_kv_heads) and softmax scale sm_scale;
+ *   out[i][h] is rounded to bf16.
+ * The chunk's own K/V are NOT written to the pool here; quantize them with
+ * fp8kv_quantize_rows (before or after: the slots must not be prefix rows).
+ *
+ * q:            device bf16 [n_tokens][n_q_heads][128], contiguous.
+ * k_cur, v_cur: device bf16 [n_tokens][n_kv_heads][128], contiguous.
+ * prefix_rows:  device int32 [n_prefix], physical rows of `pool`.
+ * ws_k, ws_v:   device bf16, each >= n_prefix * n_kv_heads * 128 elements
+ *               (ws_capacity_rows >= n_prefix rows); written by step 1, laid
+ *               out [n_prefix][n_kv_heads][128]; may be shared by all layers.
+ * out:          device bf16 [n_tokens][n_q_heads][128].
+ * All bf16 bases 16-byte aligned.  n_tokens >= 1, n_prefix >= 0.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE (ws too small), HIP.
+ */
+fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer *pool, const uint16_t *q, const uint16_t *k_cur,
+                                const uint16_t *v_cur, int32_t n_tokens, int32_t n_q_heads,
+                                const int32_t *prefix_rows, int32_t n_prefix, uint16_t *ws_k,
+                                uint16_t *ws_v, int64_t ws_capacity_rows, float sm_scale,
+                                uint16_t *out, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *fp8kv_status_string(fp8kv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_H */

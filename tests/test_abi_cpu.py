@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and every host-side validation error comes back as its status code before any
+HIP call is made."""
+import ctypes
+
+import pytest
+import torch
+
+from fp8_kv_cache_row_amd import binding as B
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = range(6)
+A = 1 << 20  # a fake, 256-byte-aligned "device address"; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = B.declared_symbols()
+    assert set(names) >= {"fp8kv_quantize_rows", "fp8kv_decode_attn", "fp8kv_prefill_attn",
+                          "fp8kv_decode_workspace_bytes", "fp8kv_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert B.status_string(s).startswith("FP8KV_")
+    assert "UNKNOWN" in B.status_string(99)
+
+
+def _pool(**kw):
+    p = dict(k_codes=A, v_codes=2 * A, k_scales=3 * A, v_scales=4 * A, num_rows=100, n_kv_heads=4,
+             head_dim=128, code_row_stride=512, scale_row_stride=4)
+    p.update(kw)
+    return B.PoolLayer(p["k_codes"], p["v_codes"], p["k_scales"], p["v_scales"], p["num_rows"],
+                       p["n_kv_heads"], p["head_dim"], p["code_row_stride"], p["scale_row_stride"])
+
+
+def _quant(lib, pool, k=A, v=A, stride=512, slots=A, n=4):
+    return lib.fp8kv_quantize_rows(ctypes.byref(pool), k, v, stride, slots, n, None)
+
+
+def _decode(lib, pool, q=A, batch=1, hq=32, table=A, tstride=1024, lens=A, maxlen=1000, sm=0.088,
+            splits=0, ws=A, wsb=None, out=A):
+    if wsb is None:
+        wsb = lib.fp8kv_decode_workspace_bytes(batch, hq, splits)
+    return lib.fp8kv_decode_attn(ctypes.byref(pool), q, batch, hq, table, tstride, lens, maxlen, sm, splits,
+                                 ws, wsb, out, None)
+
+
+def _prefill(lib, pool, q=A, kc=A, vc=A, T=16, hq=32, rows=A, P=8, wsk=A, wsv=A, cap=8, sm=0.088, out=A):
+    return lib.fp8kv_prefill_attn(ctypes.byref(pool), q, kc, vc, T, hq, rows, P, wsk, wsv, cap, sm, out, None)
+
+
+def test_quantize_validation(lib):
+    assert lib.fp8kv_quantize_rows(None, A, A, 512, A, 4, None) == INVALID
+    assert _quant(lib, _pool(k_codes=0)) == INVALID
+    assert _quant(lib, _pool(head_dim=64)) == UNSUPPORTED
+    assert _quant(lib, _pool(num_rows=0)) == INVALID
+    assert _quant(lib, _pool(code_row_stride=256)) == INVALID        # < Hkv * 128
+    assert _quant(lib, _pool(scale_row_stride=2)) == INVALID
+    assert _quant(lib, _pool(k_codes=A + 4)) == ALIGN                # codes need 16 B
+    assert _quant(lib, _pool(code_row_stride=520)) == ALIGN
+    assert _quant(lib, _pool(v_scales=4 * A + 2)) == ALIGN
+    assert _quant(lib, _pool(), k=0) == INVALID
+    assert _quant(lib, _pool(), n=-1) == INVALID
+    assert _quant(lib, _pool(), n=0) == OK                           # no-op, nothing launched
+    assert _quant(lib, _pool(), stride=256) == INVALID
+    assert _quant(lib, _pool(), stride=516) == ALIGN
+    assert _quant(lib, _pool(), k=A + 8) == ALIGN
+
+
+def test_decode_validation(lib):
+    p = _pool()
+    assert _decode(lib, _pool(v_scales=0)) == INVALID
+    assert _decode(lib, p, q=0) == INVALID
+    assert _decode(lib, p, batch=0) == INVALID
+    assert _decode(lib, p, hq=30) == INVALID                         # not a multiple of Hkv
+    assert _decode(lib, p, hq=12) == UNSUPPORTED                     # G = 3
+    assert _decode(lib, p, hq=128) == UNSUPPORTED                    # G = 32
+    assert _decode(lib, p, tstride=500) == INVALID                   # table row shorter than max_seq_len
+    assert _decode(lib, p, maxlen=-1) == INVALID
+    assert _decode(lib, p, sm=float("nan")) == INVALID
+    assert _decode(lib, p, q=A + 2) == ALIGN
+    assert _decode(lib, p, out=A + 8) == ALIGN
+    assert _decode(lib, p, table=A + 2) == ALIGN
+    assert _decode(lib, p, ws=0) == WORKSPACE
+    assert _decode(lib, p, wsb=100) == WORKSPACE
+    assert _decode(lib, p, ws=A + 16) == ALIGN
+    assert _decode(lib, _pool(head_dim=256)) == UNSUPPORTED
+
+
+def test_decode_workspace_bytes(lib):
+    f = lib.fp8kv_decode_workspace_bytes
+    assert f(1, 32, 64) == 1 * 32 * 64 * 129 * 4
+    assert f(2, 16, 0) == 2 * 16 * 256 * 129 * 4                     # 0 = the library's cap
+    assert f(1, 8, 10_000) == 1 * 8 * 256 * 129 * 4
+    assert f(0, 8, 1) == 0 and f(1, 0, 1) == 0 and f(1, 8, -1) == 0
+
+
+def test_prefill_validation(lib):
+    p = _pool()
+    assert _prefill(lib, _pool(k_scales=0)) == INVALID
+    assert _prefill(lib, p, q=0) == INVALID
+    assert _prefill(lib, p, T=0) == INVALID
+    assert _prefill(lib, p, P=-1) == INVALID
+    assert _prefill(lib, p, hq=24) == UNSUPPORTED                    # G = 6
+    assert _prefill(lib, p, rows=0) == INVALID
+    assert _prefill(lib, p, wsk=0) == WORKSPACE
+    assert _prefill(lib, p, cap=7) == WORKSPACE
+    assert _prefill(lib, p, wsv=A + 2) == ALIGN
+    assert _prefill(lib, p, kc=A + 4) == ALIGN
+    assert _prefill(lib, p, sm=float("nan")) == INVALID
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="valid-looking fake pointers must never reach a real GPU")
+def test_valid_arguments_reach_the_device_check(lib):
+    """With all arguments valid the call gets as far as the device query, which
+    fails (no GPU here) with FP8KV_ERR_HIP; only runs where no device is visible."""
+    assert _quant(lib, _pool()) == HIP
+    assert _decode(lib, _pool()) == HIP
+    assert _prefill(lib, _pool()) == HIP

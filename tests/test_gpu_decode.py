@@ -1,0 +1,239 @@
+"""GPU parity: split-K FP8 decode attention against the fp64 oracle.
+
+Covers the tiny case, the 32K-context single layer, the 48-layer 40K step
+(quantize-on-write per layer), the 16-request batch, ragged and degenerate
+lengths, every supported GQA ratio, split caps 1/8/64/auto, row-permutation
+invariance, the exact V path for every finite code, both pool layouts and
+HIP-graph replay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_kv_cache_row_amd as fk
+from fp8_kv_cache_row_amd import workloads as wl
+
+from gpu_common import (DEV, assert_bits_equal, assert_close, bf16_to_f64, build_pool, oracle_pool,
+                        pool_arrays, run_decode, say, to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+def _oracle_decode(case, pools=None, q=None, table=None, seq_lens=None):
+    kc, vc, ks, vs = pools if pools is not None else oracle_pool(case)
+    return oracle.decode_attention(case.q if q is None else q, kc, vc, ks, vs,
+                                   case.table if table is None else table,
+                                   case.seq_lens if seq_lens is None else seq_lens,
+                                   case.sm_scale, case.n_kv_heads)
+
+
+@pytest.mark.parametrize("layout", ["separate", "interleaved"])
+def test_tiny_gqa8(layout):
+    say(f"decode tiny GQA-8 256 rows, layout={layout}")
+    case = wl.tiny_decode(0)
+    pool = build_pool(case, layout)
+    out = run_decode(pool, case)
+    assert_close(bf16_to_f64(out), _oracle_decode(case), "tiny")
+
+
+def test_layer_32k_all_split_caps():
+    say("decode 32K context, 32 q / 4 KV heads, pool 33,059 rows")
+    case = wl.layer_decode(0, with_new_token=False)
+    pool = build_pool(case)
+    ref_pools = oracle_pool(case)
+    kc, vc, ks, vs = pool_arrays(pool)
+    assert_bits_equal(kc, ref_pools[0], "K codes")
+    assert_bits_equal(vs, ref_pools[3], "V scales")
+    ref = _oracle_decode(case, ref_pools)
+    outs = {}
+    for cap in (0, 1, 8, 64):
+        say(f"  max_splits={cap}")
+        outs[cap] = bf16_to_f64(run_decode(pool, case, max_splits=cap))
+        assert_close(outs[cap], ref, f"32K cap={cap}")
+    for cap in (1, 8, 64):
+        assert np.abs(outs[cap] - outs[0]).max() <= 2e-2
+
+
+def test_layer_32k_interleaved_pool_matches_separate():
+    say("decode 32K, interleaved pool layout")
+    case = wl.layer_decode(1, with_new_token=False)
+    pool = build_pool(case, "interleaved")
+    assert_close(bf16_to_f64(run_decode(pool, case)), _oracle_decode(case), "32K interleaved")
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 17, 31, 32, 33, 127, 129, 513, 1000, 4097])
+def test_ragged_lengths(L):
+    say(f"decode L={L}")
+    case = wl.layer_decode(2, ctx=max(L, 1), pool_rows=5000, n_q_heads=32, n_kv_heads=4, with_new_token=False)
+    pool = build_pool(case)
+    lens = np.array([L], np.int32)
+    out = bf16_to_f64(run_decode(pool, case, seq_lens=lens, max_seq_len=L))
+    if L == 0:
+        assert np.all(out == 0.0)
+        return
+    ref = _oracle_decode(case, seq_lens=lens)
+    assert_close(out, ref, f"L={L}")
+
+
+def test_single_row_returns_that_row():
+    say("decode L=1 returns the dequantized V row")
+    case = wl.layer_decode(3, ctx=1, pool_rows=100, with_new_token=False)
+    pool = build_pool(case)
+    out = bf16_to_f64(run_decode(pool, case))
+    kc, vc, ks, vs = oracle_pool(case)
+    row = case.table[0, 0]
+    vhat = oracle.dequantize(vc, vs)[row]  # [Hkv][D]
+    expect = np.repeat(vhat, 8, axis=0)[None]
+    # the only roundings are p * v_scale to bf16 (p = 1) and the bf16 output
+    assert np.all(np.abs(out - expect) <= np.abs(expect) * 2.0 ** -7 + 1e-30)
+    assert_close(out, expect, "L=1")
+
+
+def test_every_finite_code_through_the_v_path():
+    """One row, unit V scale: the output is decode(code) exactly (rounded to bf16, which is exact)."""
+    say("decode: all 254 finite codes through the V path")
+    R, H = 4, 2
+    pool = fk.Fp8KvPool(R, H, device=DEV)
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    codes[(codes & 0x7F) == 0x7F] = 0x00
+    vc = np.zeros((R, H, D), np.uint8)
+    vc[1, 0] = codes[0]
+    vc[1, 1] = codes[1]
+    pool.v_codes.copy_(to_dev(vc))
+    pool.k_codes.fill_(0x38)
+    pool.k_scales.fill_(0.5)
+    pool.v_scales.fill_(1.0)
+    q = wl.bf16_bits(np.random.default_rng(0).standard_normal((1, 4, D)).astype(np.float32))
+    out = fk.fp8kv_decode_attn(pool, to_dev_bf16(q), to_dev(np.array([[1]], np.int32)),
+                               to_dev(np.array([1], np.int32)), 1, 0.0883883)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(out)[0]
+    dec = oracle.e4m3_decode_table()[codes]
+    assert np.array_equal(got[0], dec[0]) and np.array_equal(got[1], dec[0])
+    assert np.array_equal(got[2], dec[1]) and np.array_equal(got[3], dec[1])
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 8), (2, 4), (4, 4), (8, 4), (16, 2)])
+def test_gqa_ratios(G, Hkv):
+    say(f"decode GQA ratio {G} with {Hkv} KV heads")
+    case = wl.layer_decode(4, ctx=3001, pool_rows=4000, n_q_heads=G * Hkv, n_kv_heads=Hkv, with_new_token=False)
+    pool = build_pool(case)
+    assert_close(bf16_to_f64(run_decode(pool, case)), _oracle_decode(case), f"G={G}")
+
+
+def test_row_permutation_invariance():
+    say("decode: permuting the physical rows (and the table) leaves the output unchanged")
+    case = wl.layer_decode(5, ctx=2000, pool_rows=2500, with_new_token=False)
+    pool = build_pool(case)
+    base = bf16_to_f64(run_decode(pool, case))
+    perm = np.random.default_rng(9).permutation(case.pool_rows)
+    inv = np.argsort(perm)
+    case2 = wl.DecodeCase(case.name, case.n_q_heads, case.n_kv_heads, case.pool_rows, case.k_rows[perm],
+                          case.v_rows[perm], case.q, inv[case.table].astype(np.int32), case.seq_lens,
+                          case.sm_scale)
+    pool2 = build_pool(case2)
+    out2 = bf16_to_f64(run_decode(pool2, case2))
+    assert np.abs(out2 - base).max() <= 1e-2
+    assert_close(out2, _oracle_decode(case), "permuted")
+
+
+def test_batched_16_requests_gqa4():
+    say("decode 16 requests, lengths 1,024..32,768, GQA 4")
+    case = wl.batched_decode(0)
+    assert int(case.seq_lens.sum()) == 272568
+    pool = build_pool(case)
+    ref = _oracle_decode(case)
+    for cap in (0, 8):
+        out = bf16_to_f64(run_decode(pool, case, max_splits=cap))
+        assert_close(out, ref, f"batched cap={cap}")
+        for b in range(case.batch):
+            assert_close(out[b], ref[b], f"  request {b} (L={case.seq_lens[b]})")
+
+
+def test_model_step_48_layers_40k():
+    """48 layers x (quantize the new token's K/V into slot table[39999], then
+    decode over 40,000 rows); the pool holds 40,290 rows per layer."""
+    say("decode 48-layer step at 40,000 context (2.04 GB pool)")
+    table = wl.model_step_table(0)
+    t_dev = to_dev(table)
+    lens = to_dev(np.array([table.shape[1]], np.int32))
+    new_slot = to_dev(table[:, -1].copy())
+    check_layers = {0, 23, 47}
+    outs = {}
+    for layer in range(48):
+        case = wl.model_step_layer(layer, table)
+        pool = build_pool(case)
+        fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.new_k), to_dev_bf16(case.new_v), new_slot)
+        out = fk.fp8kv_decode_attn(pool, to_dev_bf16(case.q), t_dev, lens, table.shape[1], case.sm_scale)
+        torch.cuda.synchronize()
+        kc, vc, ks, vs = pool_arrays(pool)
+        nkc, nks = oracle.quantize_rows(case.new_k)
+        nvc, nvs = oracle.quantize_rows(case.new_v)
+        row = int(table[0, -1])
+        assert_bits_equal(kc[row], nkc[0], f"layer {layer} new K codes")
+        assert_bits_equal(vc[row], nvc[0], f"layer {layer} new V codes")
+        assert_bits_equal(ks[row], nks[0], f"layer {layer} new K scales")
+        assert_bits_equal(vs[row], nvs[0], f"layer {layer} new V scales")
+        if layer in check_layers:
+            okc, ovc, oks, ovs = oracle_pool(case)
+            okc[row], ovc[row], oks[row], ovs[row] = nkc[0], nvc[0], nks[0], nvs[0]
+            assert_bits_equal(kc, okc, f"layer {layer} K codes")
+            assert_bits_equal(vs, ovs, f"layer {layer} V scales")
+            outs[layer] = (bf16_to_f64(out), _oracle_decode(case, (okc, ovc, oks, ovs)))
+        del pool
+    for layer, (got, ref) in outs.items():
+        assert_close(got, ref, f"layer {layer}")
+
+
+def test_graph_replay_matches_eager():
+    say("decode + quantize captured in a HIP graph, replayed 5 times")
+    case = wl.layer_decode(6, ctx=8192, pool_rows=9000)
+    pool = build_pool(case)
+    q = to_dev_bf16(case.q)
+    t = to_dev(case.table)
+    sl = to_dev(case.seq_lens)
+    nk, nv = to_dev_bf16(case.new_k), to_dev_bf16(case.new_v)
+    slot = to_dev(case.table[:, -1].copy())
+    ws = fk.decode_workspace(1, case.n_q_heads)
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fk.fp8kv_quantize_rows(pool, nk, nv, slot)
+        fk.fp8kv_decode_attn(pool, q, t, sl, case.max_seq_len, case.sm_scale, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fk.fp8kv_quantize_rows(pool, nk, nv, slot)
+        fk.fp8kv_decode_attn(pool, q, t, sl, case.max_seq_len, case.sm_scale, workspace=ws, out=out)
+    for i in range(5):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs"
+        _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
+    ref = oracle_pool(case)
+    kc, vc, ks, vs = ref
+    row = int(case.table[0, -1])
+    nkc, nks = oracle.quantize_rows(case.new_k)
+    nvc, nvs = oracle.quantize_rows(case.new_v)
+    kc[row], vc[row], ks[row], vs[row] = nkc[0], nvc[0], nks[0], nvs[0]
+    assert_close(bf16_to_f64(eager), _oracle_decode(case, (kc, vc, ks, vs)), "graph")
+
+
+def test_output_guard_bands_untouched():
+    say("decode writes only its output rows")
+    case = wl.layer_decode(7, ctx=777, pool_rows=1000, with_new_token=False)
+    pool = build_pool(case)
+    n = case.q.size
+    buf = torch.full((n + 2 * 64,), -3.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[64:64 + n].view(case.q.shape)
+    fk.fp8kv_decode_attn(pool, to_dev_bf16(case.q), to_dev(case.table), to_dev(case.seq_lens), case.max_seq_len,
+                         case.sm_scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:64] == -3.0) and torch.all(buf[64 + n:] == -3.0)
+    assert_close(bf16_to_f64(out), _oracle_decode(case), "guarded")

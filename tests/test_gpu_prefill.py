@@ -1,0 +1,81 @@
+"""GPU parity: chunked prefill (reconstruct + causal bf16 MFMA attention) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_kv_cache_row_amd as fk
+from fp8_kv_cache_row_amd import workloads as wl
+
+from gpu_common import DEV, assert_bits_equal, assert_close, bf16_to_f64, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+def _run(case, layout="separate", q_idx=None, check_ws=True):
+    """Quantize the prefix into the pool, run prefill, then quantize the chunk; compare."""
+    P, T, H = case.prefix_k.shape[0], case.q.shape[0], case.n_kv_heads
+    pool = fk.Fp8KvPool(case.pool_rows, H, layout=layout, device=DEV)
+    if P:
+        fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.prefix_k), to_dev_bf16(case.prefix_v), to_dev(case.prefix_rows))
+    ws_k = torch.empty((max(P, 1), H, D), dtype=torch.bfloat16, device=DEV)
+    ws_v = torch.empty_like(ws_k)
+    out = fk.fp8kv_prefill_attn(pool, to_dev_bf16(case.q), to_dev_bf16(case.k_cur), to_dev_bf16(case.v_cur),
+                                to_dev(case.prefix_rows) if P else None, ws_k, ws_v, case.sm_scale)
+    fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.k_cur), to_dev_bf16(case.v_cur), to_dev(case.chunk_slots))
+    torch.cuda.synchronize()
+
+    # oracle: its own codes, its own reconstruction, fp64 attention
+    okc, oks = oracle.quantize_rows(case.prefix_k)
+    ovc, ovs = oracle.quantize_rows(case.prefix_v)
+    R = case.pool_rows
+    pk = np.zeros((R, H, D), np.uint8)
+    pv = np.zeros((R, H, D), np.uint8)
+    sk = np.zeros((R, H), np.float32)
+    sv = np.zeros((R, H), np.float32)
+    pk[case.prefix_rows], pv[case.prefix_rows], sk[case.prefix_rows], sv[case.prefix_rows] = okc, ovc, oks, ovs
+    ows_k = oracle.reconstruct(pk, sk, case.prefix_rows, H) if P else None
+    ows_v = oracle.reconstruct(pv, sv, case.prefix_rows, H) if P else None
+    if P and check_ws:
+        assert_bits_equal(ws_k[:P].view(torch.int16).cpu().numpy().view(np.uint16), ows_k, "ws_k")
+        assert_bits_equal(ws_v[:P].view(torch.int16).cpu().numpy().view(np.uint16), ows_v, "ws_v")
+    # the chunk's own rows landed in the pool bit-exactly
+    ck, cs = oracle.quantize_rows(case.k_cur)
+    kc_dev, _ = pool.codes()
+    ks_dev, _ = pool.scales()
+    assert_bits_equal(kc_dev.cpu().numpy()[case.chunk_slots], ck, "chunk K codes")
+    assert_bits_equal(ks_dev.cpu().numpy()[case.chunk_slots], cs, "chunk K scales")
+    idx = np.arange(T, dtype=np.int32) if q_idx is None else np.asarray(q_idx, np.int32)
+    ref = oracle.prefill_attention(case.q, ows_k, ows_v, case.k_cur, case.v_cur, case.sm_scale, q_idx=idx)
+    got = bf16_to_f64(out)[idx]
+    return got, ref
+
+
+@pytest.mark.parametrize("P,T,Hq,Hkv", [(0, 1, 8, 1), (0, 37, 32, 4), (64, 1, 32, 4), (100, 37, 32, 4),
+                                         (257, 130, 16, 4), (1000, 300, 8, 8), (33, 65, 32, 2),
+                                         (500, 200, 4, 4)])
+def test_small_prefills(P, T, Hq, Hkv):
+    say(f"prefill P={P} T={T} Hq={Hq} Hkv={Hkv}")
+    case = wl.chunked_prefill(seed=P + T, n_prefix=P, n_chunk=T, n_q_heads=Hq, n_kv_heads=Hkv)
+    got, ref = _run(case)
+    assert_close(got, ref, f"P={P} T={T} G={Hq // Hkv}")
+
+
+def test_small_prefill_interleaved_pool():
+    say("prefill P=300 T=100, interleaved pool")
+    case = wl.chunked_prefill(seed=11, n_prefix=300, n_chunk=100)
+    got, ref = _run(case, layout="interleaved")
+    assert_close(got, ref, "interleaved")
+
+
+def test_chunked_prefill_8k_prefix_8k_chunk():
+    """8,192 historical FP8 rows + 8,192 bf16 chunk tokens, 32 q / 4 KV heads:
+    workspace bit-exact for all rows, attention checked on sampled query rows
+    (every 256th plus the last 8) against the fp64 oracle."""
+    say("prefill 8K prefix + 8K chunk (sampled rows vs oracle)")
+    case = wl.chunked_prefill(0)
+    T = case.q.shape[0]
+    idx = np.unique(np.concatenate([np.arange(0, T, 256), np.arange(T - 8, T)]))
+    got, ref = _run(case, q_idx=idx)
+    assert_close(got, ref, "8K+8K sampled")
