@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""FP8-KV GQA decode attention at 32K context on one MI355X.
+
+Workload: one layer of batch-1 decode with 32 query / 4 KV heads (GQA 8),
+head dim 128, 32,768 cached rows scattered over a 33,059-row page-size-1 FP8
+pool (seeded permutation), K ~ N(0,1) with 4 x8 outlier channels per head,
+V ~ 0.5 N(0,1), bf16 before quantization.  One step = quantize the new
+token's K/V row into the pool (its slot is the last table entry) + split-K
+stage 1 + merge, i.e. one decode layer.
+
+Cold HBM: the step rotates over `--pools` identical copies of the layer's pool
+(12 x 34.9 MB = 419 MB, more than the 256 MB Infinity Cache), as a multi-layer
+model does, so each step reads its KV rows from HBM.  Steps are captured in a
+HIP graph and replayed, so host launch overhead is not timed.
+
+Prints one JSON line.  `value` is the effective KV bandwidth of the whole step
+(algorithmic KV bytes / step time); `roofline` is for the dominant kernel
+(stage 1), timed on its own the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8-KV GQA decode attention: us/layer and KV HBM GB/s (% of peak) at 32K ctx"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+KV_BYTES_PER_ROW_HEAD = 2 * (128 + 4)   # K and V: 128 code bytes + one fp32 scale each
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stage1_32k_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240, help="timed decode steps (layers)")
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--pools", type=int, default=12, help="pool copies rotated per step (cold HBM)")
+    ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--layout", default="separate", choices=["separate", "interleaved"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) instead")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_kv_cache_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_hint: int):
+    """HBM bytes per stage-1 launch from the committed rocprofv3 counter runs,
+    or None when they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle (as it stands) on the host: quantize the new K/V row + fp64
+    decode attention over all 32,768 rows, repeated until the time budget."""
+    import numpy as np
+
+    import oracle
+    kc, ks = oracle.quantize_rows(case.k_rows)
+    vc, vs = oracle.quantize_rows(case.v_rows)
+    row = int(case.table[0, -1])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        nkc, nks = oracle.quantize_rows(case.new_k)
+        nvc, nvs = oracle.quantize_rows(case.new_v)
+        kc[row], ks[row], vc[row], vs[row] = nkc[0], nks[0], nvc[0], nvs[0]
+        oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale, case.n_kv_heads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    kv = case.max_seq_len * case.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+    return {"value": round(kv * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"full 32K-context layer step (quantize new K/V row + fp64 decode attention, "
+                      f"32 q heads x 32,768 rows) repeated {reps} times in {el:.1f} s",
+            "us_per_layer": round(el / reps * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); this "
+              "path has no multi-GPU decomposition to time.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_kv_cache_row_amd as fk
+    from fp8_kv_cache_row_amd import binding as B
+    from fp8_kv_cache_row_amd import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    case = wl.layer_decode(0)  # 32,768 of 33,059 rows, 32 q / 4 KV heads
+    L, Hq, Hkv = case.max_seq_len, case.n_q_heads, case.n_kv_heads
+    kv_bytes = L * Hkv * KV_BYTES_PER_ROW_HEAD
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base = fk.Fp8KvPool(case.pool_rows, Hkv, layout=args.layout, device=dev)
+    fk.fp8kv_quantize_rows(base, bf(case.k_rows), bf(case.v_rows),
+                           torch.arange(case.pool_rows, dtype=torch.int32, device=dev))
+    n_pools = 1 if args.warm else max(1, args.pools)
+    pools = [base]
+    for _ in range(n_pools - 1):
+        p = fk.Fp8KvPool(case.pool_rows, Hkv, layout=args.layout, device=dev)
+        for dst, src in zip(p._buffers, base._buffers):
+            dst.copy_(src)
+        pools.append(p)
+    q = bf(case.q)
+    table = torch.from_numpy(case.table).to(dev)
+    lens = torch.from_numpy(case.seq_lens).to(dev)
+    new_k, new_v = bf(case.new_k), bf(case.new_v)
+    slot = torch.from_numpy(case.table[:, -1].copy()).to(dev)
+    ws = fk.decode_workspace(1, Hq, args.max_splits, dev)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    lib = B.load()
+    stream = torch.cuda.Stream(device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    wsb = ws.numel()
+
+    def quant(p):
+        return lib.fp8kv_quantize_rows(ctypes.byref(p.layer), new_k.data_ptr(), new_v.data_ptr(), Hkv * 128,
+                                       slot.data_ptr(), 1, sp)
+
+    def stage1(p):
+        return lib.fp8kv_decode_stage1(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,
+                                       lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb, sp)
+
+    def merge():
+        return lib.fp8kv_decode_merge(1, Hq, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp)
+
+    def decode(p):
+        return lib.fp8kv_decode_attn(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,
+                                     lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb,
+                                     out.data_ptr(), sp)
+
+    def step(i):
+        p = pools[i % n_pools]
+        st = quant(p) or decode(p)
+        if st:
+            raise B.Fp8KvError(st, "decode step")
+
+    def capture(body, n):
+        """A HIP graph of n calls body(i) on `stream`."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(n):          # untimed eager pass (also allocator warm-up)
+                body(i)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                body(i)
+        return g
+
+    def timed(g, per_graph, total):
+        reps = max(1, -(-total // per_graph))
+        for _ in range(max(1, -(-args.warmup // per_graph))):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per_graph), reps * per_graph  # ms per call
+
+    per = n_pools if n_pools > 1 else 12
+    g_step = capture(step, per)
+    step_ms, steps_done = timed(g_step, per, args.steps)
+    g_s1 = capture(lambda i: stage1(pools[i % n_pools]), per)
+    s1_ms, _ = timed(g_s1, per, args.steps)
+    g_m = capture(lambda i: merge(), per)
+    m_ms, _ = timed(g_m, per, args.steps)
+    g_q = capture(lambda i: quant(pools[i % n_pools]), per)
+    q_ms, _ = timed(g_q, per, args.steps)
+
+    # correctness guard on the benchmarked configuration (cheap: compares to a second split choice)
+    step(0)
+    torch.cuda.synchronize()
+    ref = fk.fp8kv_decode_attn(pools[0], q, table, lens, L, case.sm_scale, max_splits=8)
+    torch.cuda.synchronize()
+    if not torch.allclose(out.float(), ref.float(), atol=2e-2, rtol=0):
+        print("bench: split-count cross-check failed", file=sys.stderr)
+        sys.exit(1)
+
+    s1_gbps = kv_bytes / (s1_ms * 1e-3) / 1e9
+    step_gbps = kv_bytes / (step_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps_done,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "single-layer batch-1 GQA-8 FP8 decode at 32K context",
+            "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "context": L,
+            "pool_rows": case.pool_rows, "page_size": 1, "pool_layout": args.layout,
+            "kv_cache": "E4M3FN codes + fp32 per-row scales", "query": "bf16",
+            "hbm_state": "warm (one pool)" if args.warm else f"cold ({n_pools} pool copies rotated)",
+            "step": "quantize new K/V row + split-K stage 1 + merge (HIP graph replay)",
+        },
+        "us_per_layer": round(step_ms * 1e3, 3),
+        "pct_hbm_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
+        "kv_bytes_per_layer": kv_bytes,
+        "kernels_us": {"quantize_new_row": round(q_ms * 1e3, 3), "decode_stage1": round(s1_ms * 1e3, 3),
+                       "decode_merge": round(m_ms * 1e3, 3)},
+        "roofline": {
+            "kernel": "decode_stage1",
+            "bound": "hbm",
+            "achieved": round(s1_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(kv_bytes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,6 +70,10 @@ def load() -> ctypes.CDLL:
     L.fp8kv_decode_workspace_bytes.restype = sz
     L.fp8kv_decode_attn.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp, vp]
     L.fp8kv_decode_attn.restype = ctypes.c_int
+    L.fp8kv_decode_stage1.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
+    L.fp8kv_decode_stage1.restype = ctypes.c_int
+    L.fp8kv_decode_merge.argtypes = [i32, i32, i32, vp, sz, vp, vp]
+    L.fp8kv_decode_merge.restype = ctypes.c_int
     L.fp8kv_prefill_attn.argtypes = [P, vp, vp, vp, i32, i32, vp, i32, vp, vp, i64, f32, vp, vp]
     L.fp8kv_prefill_attn.restype = ctypes.c_int
     L.fp8kv_status_string.argtypes = [ctypes.c_int]
@@ -81,7 +85,8 @@ def load() -> ctypes.CDLL:
 def declared_symbols() -> list:
     """Function names declared in include/fp8kv.h."""
     text = open(_HEADER).read()
-    return sorted(set(re.findall(r"\b(fp8kv_[a-z_]+)\s*\(", text)))
+    decl = r"^(?:fp8kv_status|size_t|const char \*)\s*(fp8kv_\w+)\s*\("
+    return sorted(set(re.findall(decl, text, flags=re.M)))
 
 
 def status_string(status: int) -> str:
@@ -184,9 +189,13 @@ def fp8kv_quantize_rows(pool: Fp8KvPool, k: torch.Tensor, v: torch.Tensor, slots
     n = int(slots.numel())
     if k.shape != v.shape or k.dim() != 3 or k.shape[0] != n or k.shape[1:] != (pool.n_kv_heads, HEAD_DIM):
         raise ValueError(f"k/v must be [{n}][{pool.n_kv_heads}][{HEAD_DIM}], got {tuple(k.shape)} / {tuple(v.shape)}")
-    if k.stride(2) != 1 or k.stride(1) != HEAD_DIM or v.stride() != k.stride():
-        raise ValueError("k and v need contiguous heads and the same token stride")
-    st = load().fp8kv_quantize_rows(ctypes.byref(pool.layer), _ptr(_bits(k)), _ptr(_bits(v)), k.stride(0),
+    if k.stride(2) != 1 or k.stride(1) != HEAD_DIM or v.stride(2) != 1 or v.stride(1) != HEAD_DIM:
+        raise ValueError("k and v need contiguous [Hkv][128] rows")
+    # a single token may carry any token stride (even 0); only token 0 is read
+    stride = k.stride(0) if n > 1 else pool.n_kv_heads * HEAD_DIM
+    if n > 1 and v.stride(0) != stride:
+        raise ValueError("k and v need the same token stride")
+    st = load().fp8kv_quantize_rows(ctypes.byref(pool.layer), _ptr(_bits(k)), _ptr(_bits(v)), stride,
                                     _ptr(slots), n, _stream(stream))
     _check(st, "fp8kv_quantize_rows")
 
@@ -200,11 +209,7 @@ def decode_workspace(batch: int, n_q_heads: int, max_splits: int = 0, device=Non
     return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
 
 
-def fp8kv_decode_attn(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
-                      max_seq_len: int, sm_scale: float, max_splits: int = 0,
-                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                      stream=None) -> torch.Tensor:
-    """Decode attention: q bf16 [B][Hq][128], row_table int32 [B][stride], seq_lens int32 [B]."""
+def _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace):
     _dev_check(q, "q", torch.bfloat16)
     _dev_check(row_table, "row_table", torch.int32)
     _dev_check(seq_lens, "seq_lens", torch.int32)
@@ -217,13 +222,46 @@ def fp8kv_decode_attn(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor,
         raise ValueError("seq_lens must have B entries")
     if workspace is None:
         workspace = decode_workspace(B, Hq, max_splits, q.device)
+    # a size-1 batch dimension may carry any stride (even 0); only row 0 is read
+    table_stride = row_table.stride(0) if B > 1 else max(int(row_table.shape[1]), 1)
+    args = [ctypes.byref(pool.layer), _ptr(_bits(q)), B, Hq, _ptr(row_table), table_stride, _ptr(seq_lens),
+            int(max_seq_len), float(sm_scale), int(max_splits), _ptr(workspace),
+            workspace.numel() * workspace.element_size()]
+    return args, workspace
+
+
+def fp8kv_decode_attn(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                      max_seq_len: int, sm_scale: float, max_splits: int = 0,
+                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Decode attention: q bf16 [B][Hq][128], row_table int32 [B][stride], seq_lens int32 [B]."""
+    args, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
     if out is None:
         out = torch.empty_like(q)
-    st = load().fp8kv_decode_attn(ctypes.byref(pool.layer), _ptr(_bits(q)), B, Hq, _ptr(row_table),
-                                  row_table.stride(0), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
-                                  int(max_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _ptr(_bits(out)), _stream(stream))
+    st = load().fp8kv_decode_attn(*args, _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_decode_attn")
+    return out
+
+
+def fp8kv_decode_stage1(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                        max_seq_len: int, sm_scale: float, max_splits: int = 0,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """First (split-K) stage only; returns the workspace holding the partials."""
+    args, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
+    st = load().fp8kv_decode_stage1(*args, _stream(stream))
+    _check(st, "fp8kv_decode_stage1")
+    return workspace
+
+
+def fp8kv_decode_merge(workspace: torch.Tensor, batch: int, n_q_heads: int, max_splits: int = 0,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Merge the partials of a preceding fp8kv_decode_stage1 into bf16 out [B][Hq][128]."""
+    if out is None:
+        out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=workspace.device)
+    st = load().fp8kv_decode_merge(batch, n_q_heads, max_splits, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _ptr(_bits(out)),
+                                   _stream(stream))
+    _check(st, "fp8kv_decode_merge")
     return out
 
 

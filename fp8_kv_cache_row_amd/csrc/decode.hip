@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
     int64_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
-    int32_t n_split, int32_t chunk, float qk_scale_log2, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2, int32_t* __restrict__ header,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int key_begin = split * chunk;
   const int key_end = min(key_begin + chunk, L);
   const int h0 = g * G;
+  if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 
   // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
   // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
@@ -215,20 +216,23 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
       oval = num / den;
       lse = M + log2f(den);
     }
-    const int64_t ph = ((int64_t)b * n_q_heads + h0 + h) * n_split + split;
+    const int64_t ph = ((int64_t)b * n_q_heads + h0 + h) * split_stride + split;
     part_o[ph * kHeadDim + d] = oval;
     if (d == 0) part_lse[ph] = lse;
   }
 }
 
-// Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
-__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* __restrict__ part_o,
+// Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), over the
+// n_split partials that stage 1 recorded in the workspace header.
+__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const int32_t* __restrict__ header,
+                                                                 const float* __restrict__ part_o,
                                                                  const float* __restrict__ part_lse,
-                                                                 int32_t n_split, uint16_t* __restrict__ out) {
+                                                                 int32_t split_stride, uint16_t* __restrict__ out) {
   const int64_t bh = blockIdx.x;
   const int d = threadIdx.x;
-  const float* lse = part_lse + bh * n_split;
-  const float* po = part_o + bh * n_split * kHeadDim + d;
+  const int n_split = header[0];
+  const float* lse = part_lse + bh * split_stride;
+  const float* po = part_o + bh * split_stride * kHeadDim + d;
   float M = -INFINITY;
   for (int s = 0; s < n_split; ++s) M = fmaxf(M, lse[s]);
   float r = 0.0f;
@@ -246,38 +250,39 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* _
 }
 
 template <int G>
-hipError_t launch_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                         const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                         float qk_scale_log2, const DecodeGeometry& geo, float* part_o, float* part_lse,
-                         hipStream_t stream) {
+hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                           const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                           float qk_scale_log2, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                           hipStream_t stream) {
   dim3 grid((unsigned)geo.n_split, (unsigned)pool.n_kv_heads, (unsigned)batch);
   hipLaunchKernelGGL(decode_stage1_kernel<G>, grid, dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
                      pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride, q, n_q_heads,
-                     row_table, table_stride, seq_lens, geo.n_split, geo.chunk, qk_scale_log2, part_o,
-                     part_lse);
+                     row_table, table_stride, seq_lens, geo.n_split, geo.chunk, ws.split_stride, qk_scale_log2,
+                     ws.header, ws.part_o, ws.part_lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                         const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                         float sm_scale, const DecodeGeometry& geo, float* part_o, float* part_lse,
-                         uint16_t* out, hipStream_t stream) {
+hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                                const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                                float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                                hipStream_t stream) {
   const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
-  const int G = n_q_heads / pool.n_kv_heads;
-  hipError_t e;
-  switch (G) {
-    case 1: e = launch_stage1<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
-    case 2: e = launch_stage1<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
-    case 4: e = launch_stage1<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
-    case 8: e = launch_stage1<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
-    case 16: e = launch_stage1<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, part_o, part_lse, stream); break;
+  switch (n_q_heads / pool.n_kv_heads) {
+    case 1: return launch_stage1_g<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
+    case 2: return launch_stage1_g<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
+    case 4: return launch_stage1_g<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
+    case 8: return launch_stage1_g<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
+    case 16: return launch_stage1_g<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kHeadDim), 0,
-                     stream, part_o, part_lse, geo.n_split, out);
+}
+
+hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, uint16_t* out,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kHeadDim), 0, stream,
+                     ws.header, ws.part_o, ws.part_lse, ws.split_stride, out);
   return hipGetLastError();
 }
 

@@ -91,8 +91,37 @@ fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t
   return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk};
 }
 
-size_t partial_bytes(int64_t batch, int64_t n_q_heads, int64_t n_split) {
-  return (size_t)(batch * n_q_heads * n_split) * (FP8KV_HEAD_DIM + 1) * sizeof(float);
+size_t partial_bytes(int64_t batch, int64_t n_q_heads, int64_t split_stride) {
+  return fp8kv::kDecodeHeaderBytes +
+         (size_t)(batch * n_q_heads * split_stride) * (FP8KV_HEAD_DIM + 1) * sizeof(float);
+}
+
+fp8kv::DecodeWorkspace workspace_view(void* workspace, int32_t batch, int32_t n_q_heads, int32_t max_splits) {
+  const int32_t stride = split_cap(max_splits);
+  char* base = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(base + fp8kv::kDecodeHeaderBytes);
+  float* part_lse = part_o + (size_t)batch * n_q_heads * stride * FP8KV_HEAD_DIM;
+  return fp8kv::DecodeWorkspace{reinterpret_cast<int32_t*>(base), part_o, part_lse, stride};
+}
+
+// Checks shared by the full decode call and its first stage.
+fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                               const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                               int32_t max_seq_len, float sm_scale, int32_t max_splits, const void* workspace,
+                               size_t workspace_bytes) {
+  fp8kv_status st = check_pool(pool);
+  if (st != FP8KV_OK) return st;
+  if (!q || !row_table || !seq_lens) return FP8KV_ERR_INVALID_ARG;
+  if (batch <= 0 || max_seq_len < 0 || max_splits < 0 || table_stride < max_seq_len || table_stride <= 0)
+    return FP8KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
+  if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
+  if (!(sm_scale == sm_scale)) return FP8KV_ERR_INVALID_ARG;  // NaN
+  if (!aligned(q, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4)) return FP8KV_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < partial_bytes(batch, n_q_heads, split_cap(max_splits)))
+    return FP8KV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return FP8KV_ERR_ALIGNMENT;
+  return FP8KV_OK;
 }
 
 fp8kv_status from_hip(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_ERR_HIP; }
@@ -123,32 +152,56 @@ size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t ma
   return partial_bytes(batch, n_q_heads, split_cap(max_splits));
 }
 
+fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                                 int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                                 const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, int32_t max_splits,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  fp8kv_status st = check_decode_args(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
+                                      sm_scale, max_splits, workspace, workspace_bytes);
+  if (st != FP8KV_OK) return st;
+  int n_cu = 0;
+  st = current_device(&n_cu);
+  if (st != FP8KV_OK) return st;
+  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
+  return from_hip(fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride,
+                                              seq_lens, sm_scale, geo,
+                                              workspace_view(workspace, batch, n_q_heads, max_splits),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_splits, const void* workspace,
+                                size_t workspace_bytes, uint16_t* out, void* stream) {
+  if (batch <= 0 || n_q_heads <= 0 || max_splits < 0 || !out) return FP8KV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < partial_bytes(batch, n_q_heads, split_cap(max_splits)))
+    return FP8KV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256) || !aligned(out, 16)) return FP8KV_ERR_ALIGNMENT;
+  fp8kv_status st = current_device(nullptr);
+  if (st != FP8KV_OK) return st;
+  return from_hip(fp8kv::launch_decode_merge(
+      batch, n_q_heads, workspace_view(const_cast<void*>(workspace), batch, n_q_heads, max_splits), out,
+      static_cast<hipStream_t>(stream)));
+}
+
 fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
                                int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
                                const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                                int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
                                void* stream) {
-  fp8kv_status st = check_pool(pool);
+  fp8kv_status st = check_decode_args(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
+                                      sm_scale, max_splits, workspace, workspace_bytes);
   if (st != FP8KV_OK) return st;
-  if (!q || !row_table || !seq_lens || !out) return FP8KV_ERR_INVALID_ARG;
-  if (batch <= 0 || max_seq_len < 0 || max_splits < 0 || table_stride < max_seq_len || table_stride <= 0)
-    return FP8KV_ERR_INVALID_ARG;
-  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
-  if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
-  if (!(sm_scale == sm_scale)) return FP8KV_ERR_INVALID_ARG;  // NaN
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4))
-    return FP8KV_ERR_ALIGNMENT;
-  if (!workspace || workspace_bytes < fp8kv_decode_workspace_bytes(batch, n_q_heads, max_splits))
-    return FP8KV_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return FP8KV_ERR_ALIGNMENT;
+  if (!out) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(out, 16)) return FP8KV_ERR_ALIGNMENT;
   int n_cu = 0;
   st = current_device(&n_cu);
   if (st != FP8KV_OK) return st;
   const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = part_o + (size_t)batch * n_q_heads * geo.n_split * FP8KV_HEAD_DIM;
-  return from_hip(fp8kv::launch_decode(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
-                                       sm_scale, geo, part_o, part_lse, out, static_cast<hipStream_t>(stream)));
+  const fp8kv::DecodeWorkspace ws = workspace_view(workspace, batch, n_q_heads, max_splits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
+                                             sm_scale, geo, ws, s);
+  if (e != hipSuccess) return FP8KV_ERR_HIP;
+  return from_hip(fp8kv::launch_decode_merge(batch, n_q_heads, ws, out, s));
 }
 
 fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q, const uint16_t* k_cur,

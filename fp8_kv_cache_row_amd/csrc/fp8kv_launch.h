@@ -34,10 +34,24 @@ hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const u
 hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, int32_t n_prefix,
                               uint16_t* ws_k, uint16_t* ws_v, hipStream_t stream);
 
-hipError_t launch_decode(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                         const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                         float sm_scale, const DecodeGeometry& geo, float* part_o, float* part_lse,
-                         uint16_t* out, hipStream_t stream);
+// Split-K partials in the caller's workspace: a 256-byte header whose first
+// int32 is the split count of the last stage-1 launch, then o[B][Hq][split_stride][128]
+// and lse[B][Hq][split_stride] (fp32, log2 units).
+struct DecodeWorkspace {
+  int32_t* header;
+  float* part_o;
+  float* part_lse;
+  int32_t split_stride;
+};
+constexpr size_t kDecodeHeaderBytes = 256;
+
+hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                                const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                                float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                                hipStream_t stream);
+
+hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, uint16_t* out,
+                               hipStream_t stream);
 
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* ws_k, const uint16_t* ws_v,
                                     const uint16_t* k_cur, const uint16_t* v_cur, int32_t n_prefix,

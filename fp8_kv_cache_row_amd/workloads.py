@@ -130,7 +130,7 @@ def tiny_decode(seed: int = 0) -> DecodeCase:
     v = draw_normal(rng, (n, 1, HEAD_DIM))
     q = draw_normal(rng, (1, 8, HEAD_DIM))
     return DecodeCase("tiny_gqa8_256", 8, 1, n, bf16_bits(k), bf16_bits(v), bf16_bits(q),
-                      np.arange(n, dtype=np.int32)[None, :], np.array([n], np.int32),
+                      np.arange(n, dtype=np.int32).reshape(1, n), np.array([n], np.int32),
                       softmax_scale())
 
 
@@ -146,7 +146,7 @@ def layer_decode(seed: int = 0, ctx: int = 32768, pool_rows: int = 33059,
     k = draw_k(rng, pool_rows, n_kv_heads, out)
     v = draw_normal(rng, (pool_rows, n_kv_heads, HEAD_DIM), 0.5)
     q = draw_normal(rng, (1, n_q_heads, HEAD_DIM))
-    table = rng.permutation(pool_rows)[:ctx].astype(np.int32)[None, :]
+    table = rng.permutation(pool_rows)[:ctx].astype(np.int32).reshape(1, ctx)
     nk = nv = None
     if with_new_token:
         nk = bf16_bits(draw_k(rng, 1, n_kv_heads, out))
@@ -159,7 +159,7 @@ def layer_decode(seed: int = 0, ctx: int = 32768, pool_rows: int = 33059,
 def model_step_table(seed: int = 0, ctx: int = 40000, pool_rows: int = 40290) -> np.ndarray:
     """Row table shared by all layers of the 48-layer step."""
     rng = np.random.default_rng(seed)
-    return rng.permutation(pool_rows)[:ctx].astype(np.int32)[None, :]
+    return rng.permutation(pool_rows)[:ctx].astype(np.int32).reshape(1, ctx)
 
 
 def model_step_layer(layer: int, table: np.ndarray, seed: int = 0, pool_rows: int = 40290,

@@ -113,19 +113,19 @@ fp8kv_status fp8kv_quantize_rows(const fp8kv_pool_layer *pool, const uint16_t *k
                                  void *stream);
 
 /*
- * Bytes of device workspace fp8kv_decode_attn needs for `batch` requests of
+ * Bytes of device workspace the decode calls need for `batch` requests of
  * `n_q_heads` query heads with at most `max_splits` splits per request
- * (0 = FP8KV_MAX_SPLITS).  Holds the split partials (an fp32 output vector and
- * a log-sum-exp per request, query head and split).  Returns 0 for invalid
- * arguments.
+ * (0 = FP8KV_MAX_SPLITS): a 256-byte header, then one fp32 output vector and
+ * one log-sum-exp per request, query head and split slot.  Returns 0 for
+ * invalid arguments.
  */
 size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_splits);
 
 /*
  * fp8kv_decode_attn -- one-token-per-request GQA attention over the FP8 pool
  * (FreeToken PR #897 description and "Fresh R9700 stage-1 A/B": BF16 query,
- * D = 128, GQA 4/8, page size 1, split-K stage 1 timed apart from the merge
- * kernel; PR #853 "What changes": rows hold E4M3 codes and per-row FP32 scales).
+ * D = 128, GQA 4/8, page size 1, split-K stage 1 followed by a merge kernel;
+ * PR #853 "What changes": rows hold E4M3 codes and per-row FP32 scales).
  *
  * For request b and query head h, with G = n_q_heads / n_kv_heads, KV head
  * g = h / G, L = seq_lens[b] and rows r_t = row_table[b * table_stride + t]:
@@ -133,11 +133,12 @@ size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t ma
  *   out[b][h] = sum_t softmax(z)_t * decode(Vcode[r_t][g]) * v_scale[r_t][g]
  * rounded to bf16.  A request with L == 0 gets zeros.
  *
- * Stage 1 splits each request's rows into at most `max_splits` (0 = chosen
- * from the device's compute-unit count and max_seq_len) ranges and writes one
- * partial per (request, query head, split) into `workspace`; stage 2 merges
- * them by log-sum-exp into `out`.  Results agree to rounding for every split
- * count.
+ * Equivalent to fp8kv_decode_stage1 followed by fp8kv_decode_merge on the same
+ * stream.  Stage 1 splits each request's rows into at most `max_splits`
+ * (0 = chosen from the device's compute-unit count and max_seq_len) ranges and
+ * writes one partial per (request, query head, split) into `workspace`; the
+ * merge combines them by log-sum-exp.  Results agree to rounding for every
+ * split count.
  *
  * q:            device bf16 [batch][n_q_heads][128], contiguous, 16-byte aligned.
  * row_table:    device int32, row b at row_table + b * table_stride; entries
@@ -156,6 +157,29 @@ fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer *pool, const uint16_t *q, 
                                const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                                int32_t max_splits, void *workspace, size_t workspace_bytes,
                                uint16_t *out, void *stream);
+
+/*
+ * fp8kv_decode_stage1 -- the split-K first stage of fp8kv_decode_attn alone
+ * (FreeToken PR #897, "Fresh R9700 stage-1 A/B": stage 1 is timed apart from
+ * the merge kernel).  Same arguments and checks as fp8kv_decode_attn without
+ * `out`; writes the partials and the split count into `workspace`.
+ */
+fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                                 int32_t n_q_heads, const int32_t *row_table, int64_t table_stride,
+                                 const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                                 int32_t max_splits, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * fp8kv_decode_merge -- the merge (stage 2) of fp8kv_decode_attn: combines the
+ * partials a preceding fp8kv_decode_stage1 on the same stream wrote into
+ * `workspace` (called with the same batch, n_q_heads and max_splits) by
+ * log-sum-exp and writes bf16 out[batch][n_q_heads][128].
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, HIP.
+ */
+fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_splits,
+                                const void *workspace, size_t workspace_bytes, uint16_t *out,
+                                void *stream);
 
 /*
  * fp8kv_prefill_attn -- attention of one prefill chunk over historical FP8 rows

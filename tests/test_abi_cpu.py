@@ -20,6 +20,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = B.declared_symbols()
     assert set(names) >= {"fp8kv_quantize_rows", "fp8kv_decode_attn", "fp8kv_prefill_attn",
+                          "fp8kv_decode_stage1", "fp8kv_decode_merge",
                           "fp8kv_decode_workspace_bytes", "fp8kv_status_string"}
     for n in names:
         assert hasattr(lib, n), n
@@ -93,11 +94,29 @@ def test_decode_validation(lib):
     assert _decode(lib, _pool(head_dim=256)) == UNSUPPORTED
 
 
+def test_decode_stage_validation(lib):
+    p = _pool()
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
+    s1 = lambda **kw: lib.fp8kv_decode_stage1(ctypes.byref(p), kw.get("q", A), 1, kw.get("hq", 32), A, 1024, A,
+                                              1000, 0.088, 0, kw.get("ws", A), kw.get("wsb", wsb), None)
+    assert s1(q=0) == INVALID
+    assert s1(hq=12) == UNSUPPORTED
+    assert s1(wsb=wsb - 1) == WORKSPACE
+    assert s1(ws=A + 64) == ALIGN
+    m = lambda **kw: lib.fp8kv_decode_merge(kw.get("b", 1), 32, kw.get("splits", 0), kw.get("ws", A),
+                                            kw.get("wsb", wsb), kw.get("out", A), None)
+    assert m(b=0) == INVALID
+    assert m(out=0) == INVALID
+    assert m(ws=0) == WORKSPACE
+    assert m(splits=300, wsb=100) == WORKSPACE
+    assert m(out=A + 2) == ALIGN
+
+
 def test_decode_workspace_bytes(lib):
     f = lib.fp8kv_decode_workspace_bytes
-    assert f(1, 32, 64) == 1 * 32 * 64 * 129 * 4
-    assert f(2, 16, 0) == 2 * 16 * 256 * 129 * 4                     # 0 = the library's cap
-    assert f(1, 8, 10_000) == 1 * 8 * 256 * 129 * 4
+    assert f(1, 32, 64) == 256 + 1 * 32 * 64 * 129 * 4
+    assert f(2, 16, 0) == 256 + 2 * 16 * 256 * 129 * 4               # 0 = the library's cap
+    assert f(1, 8, 10_000) == 256 + 1 * 8 * 256 * 129 * 4
     assert f(0, 8, 1) == 0 and f(1, 0, 1) == 0 and f(1, 8, -1) == 0
 
 
@@ -124,3 +143,6 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert _quant(lib, _pool()) == HIP
     assert _decode(lib, _pool()) == HIP
     assert _prefill(lib, _pool()) == HIP
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
+    assert lib.fp8kv_decode_stage1(ctypes.byref(_pool()), A, 1, 32, A, 1024, A, 1000, 0.088, 0, A, wsb, None) == HIP
+    assert lib.fp8kv_decode_merge(1, 32, 0, A, wsb, A, None) == HIP

@@ -237,3 +237,16 @@ def test_output_guard_bands_untouched():
     torch.cuda.synchronize()
     assert torch.all(buf[:64] == -3.0) and torch.all(buf[64 + n:] == -3.0)
     assert_close(bf16_to_f64(out), _oracle_decode(case), "guarded")
+
+
+def test_stage1_then_merge_equals_full_call():
+    say("decode: stage 1 + merge as separate calls == fp8kv_decode_attn (bit-exact)")
+    case = wl.layer_decode(8, ctx=5000, pool_rows=6000, with_new_token=False)
+    pool = build_pool(case)
+    q, t, sl = to_dev_bf16(case.q), to_dev(case.table), to_dev(case.seq_lens)
+    for cap in (0, 3, 64):
+        full = fk.fp8kv_decode_attn(pool, q, t, sl, case.max_seq_len, case.sm_scale, max_splits=cap)
+        ws = fk.fp8kv_decode_stage1(pool, q, t, sl, case.max_seq_len, case.sm_scale, max_splits=cap)
+        two = fk.fp8kv_decode_merge(ws, 1, case.n_q_heads, max_splits=cap)
+        torch.cuda.synchronize()
+        assert torch.equal(full.view(torch.int16), two.view(torch.int16)), cap
