@@ -31,10 +31,17 @@ namespace fp8kv {
 namespace {
 
 constexpr int kBlock = kDecodeWaves * kWave;
+constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave loads at once
 
 // Key order inside a 32-key step: k-group j of the P*V contraction holds keys
 // 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
 __device__ __forceinline__ int step_key(int j, int r) { return (r < 4) ? 4 * j + r : 12 + 4 * j + r; }
+
+// Raw codes of one 32-key step as this lane needs them.
+struct StepCodes {
+  uint4 ka0, kb0, ka1, kb1;  // K: bytes [16j,16j+16) and [64+16j,+16) of keys n and 16+n
+  uint2 vr[8];               // V: bytes [8n, 8n+8) of keys step_key(j, r)
+};
 
 template <int G>
 __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
@@ -58,6 +65,11 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int h0 = g * G;
   if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 
+  // Per-wave staging of the row indices and (k_scale, v_scale) of the keys the
+  // wave is working on, so each lane reads what it needs with a few LDS reads.
+  __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kGroupKeys];
+  __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kGroupKeys];
+
   // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
   // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
   bf16x8 qb[4];
@@ -79,101 +91,120 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 
   const uint8_t* kbase = k_codes + (int64_t)g * kHeadDim;
   const uint8_t* vbase = v_codes + (int64_t)g * kHeadDim;
-  const float* ksb = k_scales + g;
-  const float* vsb = v_scales + g;
   const int32_t* trow = table + (int64_t)b * table_stride;
 
-  for (int t0 = key_begin + wave * kDecodeTileKeys; t0 < key_end; t0 += kDecodeWaves * kDecodeTileKeys) {
-    // Row indices of the 32 keys (lanes 32..63 repeat 0..31); keys past the
-    // end reuse the last valid row and are masked out of the softmax.
-    const int kidx = min(t0 + (lane & 31), key_end - 1);
-    const int row_l = trow[kidx];
-
-    // K rows: lane (n, j) reads bytes [16j, 16j+16) and [64+16j, 64+16j+16)
-    // of key n (block 0) and key 16+n (block 1).
-    const int rk0 = __shfl(row_l, n);
-    const int rk1 = __shfl(row_l, 16 + n);
-    const uint8_t* kp0 = kbase + (int64_t)rk0 * code_row_stride + 16 * j;
-    const uint8_t* kp1 = kbase + (int64_t)rk1 * code_row_stride + 16 * j;
-    const uint4 ka0 = *reinterpret_cast<const uint4*>(kp0);
-    const uint4 kb0 = *reinterpret_cast<const uint4*>(kp0 + 64);
-    const uint4 ka1 = *reinterpret_cast<const uint4*>(kp1);
-    const uint4 kb1 = *reinterpret_cast<const uint4*>(kp1 + 64);
-
-    // V rows and both scales for the lane's 8 keys: bytes [8n, 8n+8) of each.
-    uint2 vr[8];
-    float ks[8], vs[8];
+  for (int k0 = key_begin + wave * kGroupKeys; k0 < key_end; k0 += kDecodeWaves * kGroupKeys) {
+    // 1. Row indices and scales of the group's keys (keys past the end reuse
+    //    the last valid row and are masked out of the softmax).
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t rv = __shfl(row_l, step_key(j, r));
-      vr[r] = *reinterpret_cast<const uint2*>(vbase + rv * code_row_stride + 8 * n);
-      ks[r] = ksb[rv * scale_row_stride];
-      vs[r] = vsb[rv * scale_row_stride];
+    for (int c = 0; c < kGroupKeys; c += kWave) {
+      if (c + lane < kGroupKeys) {
+        const int key = min(k0 + c + lane, key_end - 1);
+        const int64_t row = trow[key];
+        s_rows[wave][c + lane] = (int32_t)row;
+        s_sc[wave][c + lane] = make_float2(k_scales[row * scale_row_stride + g], v_scales[row * scale_row_stride + g]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // 2. Issue every code load of the group before any math.
+    StepCodes sc[kDecodeTilesPerWave];
+#pragma unroll
+    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+      const int32_t* rows = &s_rows[wave][t * kDecodeTileKeys];
+      const uint8_t* kp0 = kbase + (int64_t)rows[n] * code_row_stride + 16 * j;
+      const uint8_t* kp1 = kbase + (int64_t)rows[16 + n] * code_row_stride + 16 * j;
+      sc[t].ka0 = *reinterpret_cast<const uint4*>(kp0);
+      sc[t].kb0 = *reinterpret_cast<const uint4*>(kp0 + 64);
+      sc[t].ka1 = *reinterpret_cast<const uint4*>(kp1);
+      sc[t].kb1 = *reinterpret_cast<const uint4*>(kp1 + 64);
+      const int4 r03 = *reinterpret_cast<const int4*>(&rows[4 * j]);
+      const int4 r47 = *reinterpret_cast<const int4*>(&rows[16 + 4 * j]);
+      const int rv[8] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        sc[t].vr[r] = *reinterpret_cast<const uint2*>(vbase + (int64_t)rv[r] * code_row_stride + 8 * n);
     }
 
-    // S^T = K * Q^T for the two 16-key blocks.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(ka0.x, ka0.y), qb[0], s0);
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(ka0.z, ka0.w), qb[1], s0);
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(kb0.x, kb0.y), qb[2], s0);
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(kb0.z, kb0.w), qb[3], s0);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(ka1.x, ka1.y), qb[0], s1);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(ka1.z, ka1.w), qb[1], s1);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(kb1.x, kb1.y), qb[2], s1);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(kb1.z, kb1.w), qb[3], s1);
-
-    // Scores in log2 units for head n, keys step_key(j, r).
-    float sc[8];
+    // 3. One MFMA step per 32 keys.
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float raw = (r < 4) ? s0[r] : s1[r - 4];
-      const bool valid = (t0 + step_key(j, r)) < key_end;
-      sc[r] = valid ? raw * ks[r] * qk_scale_log2 : -INFINITY;
+    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+      const int t0 = k0 + t * kDecodeTileKeys;
+      if (t0 >= key_end) break;  // wave-uniform
+      const float2* scp = &s_sc[wave][t * kDecodeTileKeys];
+      const float4 s01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
+      const float4 s23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
+      const float4 s45 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j]);
+      const float4 s67 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j + 2]);
+      const float ks[8] = {s01.x, s01.z, s23.x, s23.z, s45.x, s45.z, s67.x, s67.z};
+      const float vs[8] = {s01.y, s01.w, s23.y, s23.w, s45.y, s45.w, s67.y, s67.w};
+
+      // S^T = K * Q^T for the two 16-key blocks.
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].ka0.x, sc[t].ka0.y), qb[0], s0);
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].ka0.z, sc[t].ka0.w), qb[1], s0);
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].kb0.x, sc[t].kb0.y), qb[2], s0);
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].kb0.z, sc[t].kb0.w), qb[3], s0);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].ka1.x, sc[t].ka1.y), qb[0], s1);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].ka1.z, sc[t].ka1.w), qb[1], s1);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].kb1.x, sc[t].kb1.y), qb[2], s1);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(sc[t].kb1.z, sc[t].kb1.w), qb[3], s1);
+
+      // Scores in log2 units for head n, keys step_key(j, r).
+      float sv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float raw = (r < 4) ? s0[r] : s1[r - 4];
+        const bool valid = (t0 + step_key(j, r)) < key_end;
+        sv[r] = valid ? raw * ks[r] * qk_scale_log2 : -INFINITY;
+      }
+      float tmax = sv[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, sv[r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+
+      float p[8], psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        p[r] = exp2f(sv[r] - m_new);
+        psum += p[r];
+      }
+      l_part = l_part * alpha + psum;
+
+      // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
+      uint4 pu;
+      pu.x = f32x2_to_bf16x2(p[0] * vs[0], p[1] * vs[1]);
+      pu.y = f32x2_to_bf16x2(p[2] * vs[2], p[3] * vs[3]);
+      pu.z = f32x2_to_bf16x2(p[4] * vs[4], p[5] * vs[5]);
+      pu.w = f32x2_to_bf16x2(p[6] * vs[6], p[7] * vs[7]);
+      const bf16x8 pa = u4_as_bf16x8(pu);
+
+      // Rescale O rows (heads 4j+i) by their head's alpha.
+      float ai[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
+      }
+
+      // V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
+      // V[key][d = 8n + nb] for the lane's 8 keys.
+      uint32_t lo[8], hi[8];
+      const uint2* vr = sc[t].vr;
+      transpose4x4_bytes(vr[0].x, vr[1].x, vr[2].x, vr[3].x, lo[0], lo[1], lo[2], lo[3]);
+      transpose4x4_bytes(vr[4].x, vr[5].x, vr[6].x, vr[7].x, hi[0], hi[1], hi[2], hi[3]);
+      transpose4x4_bytes(vr[0].y, vr[1].y, vr[2].y, vr[3].y, lo[4], lo[5], lo[6], lo[7]);
+      transpose4x4_bytes(vr[4].y, vr[5].y, vr[6].y, vr[7].y, hi[4], hi[5], hi[6], hi[7]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
     }
-    float tmax = sc[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, sc[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-
-    float p[8], psum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p[r] = exp2f(sc[r] - m_new);
-      psum += p[r];
-    }
-    l_part = l_part * alpha + psum;
-
-    // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
-    uint4 pu;
-    pu.x = f32x2_to_bf16x2(p[0] * vs[0], p[1] * vs[1]);
-    pu.y = f32x2_to_bf16x2(p[2] * vs[2], p[3] * vs[3]);
-    pu.z = f32x2_to_bf16x2(p[4] * vs[4], p[5] * vs[5]);
-    pu.w = f32x2_to_bf16x2(p[6] * vs[6], p[7] * vs[7]);
-    const bf16x8 pa = u4_as_bf16x8(pu);
-
-    // Rescale O rows (heads 4j+i) by their head's alpha.
-    float ai[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
-    }
-
-    // V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
-    // V[key][d = 8n + nb] for the lane's 8 keys.
-    uint32_t lo[8], hi[8];
-    transpose4x4_bytes(vr[0].x, vr[1].x, vr[2].x, vr[3].x, lo[0], lo[1], lo[2], lo[3]);
-    transpose4x4_bytes(vr[4].x, vr[5].x, vr[6].x, vr[7].x, hi[0], hi[1], hi[2], hi[3]);
-    transpose4x4_bytes(vr[0].y, vr[1].y, vr[2].y, vr[3].y, lo[4], lo[5], lo[6], lo[7]);
-    transpose4x4_bytes(vr[4].y, vr[5].y, vr[6].y, vr[7].y, hi[4], hi[5], hi[6], hi[7]);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
+    __builtin_amdgcn_wave_barrier();  // this group's LDS entries are consumed
   }
 
   // Per-head totals of this wave.
@@ -223,30 +254,64 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 }
 
 // Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), over the
-// n_split partials that stage 1 recorded in the workspace header.
-__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const int32_t* __restrict__ header,
-                                                                 const float* __restrict__ part_o,
-                                                                 const float* __restrict__ part_lse,
-                                                                 int32_t split_stride, uint16_t* __restrict__ out) {
+// n_split partials that stage 1 recorded in the workspace header.  One
+// workgroup per (request, query head): the split weights are formed once in
+// LDS, then four waves each sum a quarter of the splits (two d per lane).
+constexpr int kMergeBlock = 256;
+static_assert(FP8KV_MAX_SPLITS_INTERNAL <= kMergeBlock, "one merge thread per split");
+
+__global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t* __restrict__ header,
+                                                                  const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_lse,
+                                                                  int32_t split_stride, uint16_t* __restrict__ out) {
+  __shared__ float s_w[kMergeBlock];
+  __shared__ float s_red[kMergeBlock / kWave];
+  __shared__ float2 s_acc[kMergeBlock / kWave][kWave];
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int n_split = header[0];
-  const float* lse = part_lse + bh * split_stride;
-  const float* po = part_o + bh * split_stride * kHeadDim + d;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, lse[s]);
-  float r = 0.0f;
-  if (M != -INFINITY) {
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-      const float w = exp2f(lse[s] - M);
-      num += w * po[(int64_t)s * kHeadDim];
-      den += w;
-    }
-    r = num / den;
+
+  const float lse = (tid < n_split) ? part_lse[bh * split_stride + tid] : -INFINITY;
+  float m = lse;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeBlock / kWave; ++w) M = fmaxf(M, s_red[w]);
+  const float wt = (tid < n_split && M != -INFINITY) ? exp2f(lse - M) : 0.0f;
+  s_w[tid] = wt;
+  __syncthreads();
+
+  const float* po = part_o + bh * split_stride * kHeadDim + 2 * lane;
+  float2 acc = make_float2(0.f, 0.f);
+  float den = 0.f;
+#pragma unroll 4
+  for (int s = wave; s < n_split; s += kMergeBlock / kWave) {
+    const float2 v = *reinterpret_cast<const float2*>(po + (int64_t)s * kHeadDim);
+    const float w = s_w[s];
+    acc.x += w * v.x;
+    acc.y += w * v.y;
   }
-  const __bf16 h = (__bf16)r;
-  out[bh * kHeadDim + d] = __builtin_bit_cast(uint16_t, h);
+  for (int s = lane; s < n_split; s += kWave) den += s_w[s];
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  s_acc[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    float2 t = s_acc[0][lane];
+#pragma unroll
+    for (int w = 1; w < kMergeBlock / kWave; ++w) {
+      t.x += s_acc[w][lane].x;
+      t.y += s_acc[w][lane].y;
+    }
+    const float inv = (den > 0.f) ? 1.0f / den : 0.0f;
+    const uint32_t packed = f32x2_to_bf16x2(t.x * inv, t.y * inv);
+    *reinterpret_cast<uint32_t*>(out + bh * kHeadDim + 2 * lane) = packed;
+  }
 }
 
 template <int G>
@@ -281,7 +346,7 @@ hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t
 
 hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, uint16_t* out,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kHeadDim), 0, stream,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0, stream,
                      ws.header, ws.part_o, ws.part_lse, ws.split_stride, out);
   return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 #include "fp8kv.h"
 #include "fp8kv_launch.h"
 
+static_assert(FP8KV_MAX_SPLITS == FP8KV_MAX_SPLITS_INTERNAL, "split cap mismatch");
+
 namespace {
 
 using fp8kv::PoolView;
@@ -71,14 +73,15 @@ int32_t split_cap(int32_t max_splits) {
   return (max_splits > 0 && max_splits < FP8KV_MAX_SPLITS) ? max_splits : FP8KV_MAX_SPLITS;
 }
 
-// Split choice: about two stage-1 workgroups per compute unit across the
-// batch, each wave of a workgroup getting at least one 32-key step.
+// Split choice: about one stage-1 workgroup per compute unit across the batch
+// (a workgroup has kDecodeWaves waves), each wave getting at least one group
+// of kDecodeTilesPerWave 32-key steps.
 fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
                                       int32_t max_splits, int n_cu) {
-  const int64_t unit = (int64_t)fp8kv::kDecodeWaves * fp8kv::kDecodeTileKeys;
+  const int64_t unit = (int64_t)fp8kv::kDecodeWaves * fp8kv::kDecodeTilesPerWave * fp8kv::kDecodeTileKeys;
   const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t per = (int64_t)batch * n_kv_heads;
-  const int64_t target = 2 * (int64_t)n_cu;
+  const int64_t target = (int64_t)n_cu;
   int64_t want = (target + per - 1) / per;
   if (want < 1) want = 1;
   int64_t ns = want;
