@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) instead")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 8K-prefix + 8K-chunk prefill timing")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run plain 64 MiB device copies (a known-size kernel for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -72,6 +75,66 @@ def measured_traffic(launch_bytes_hint: int):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def prefill_timing(fk, wl, dev, reps: int = 5):
+    """8,192 historical FP8 rows + an 8,192-token bf16 chunk (32 q / 4 KV heads):
+    reconstruct + causal attention in one call, then quantize the chunk."""
+    import numpy as np
+    import torch
+
+    case = wl.chunked_prefill(0)
+    P, T, Hq, Hkv = case.prefix_k.shape[0], case.q.shape[0], case.n_q_heads, case.n_kv_heads
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    pool = fk.Fp8KvPool(case.pool_rows, Hkv, device=dev)
+    fk.fp8kv_quantize_rows(pool, bf(case.prefix_k), bf(case.prefix_v), torch.from_numpy(case.prefix_rows).to(dev))
+    q, kc, vc = bf(case.q), bf(case.k_cur), bf(case.v_cur)
+    rows = torch.from_numpy(case.prefix_rows).to(dev)
+    slots = torch.from_numpy(case.chunk_slots).to(dev)
+    ws_k = torch.empty((P, Hkv, 128), dtype=torch.bfloat16, device=dev)
+    ws_v = torch.empty_like(ws_k)
+    out = torch.empty_like(q)
+
+    def attn():
+        fk.fp8kv_prefill_attn(pool, q, kc, vc, rows, ws_k, ws_v, case.sm_scale, out=out)
+
+    def quant():
+        fk.fp8kv_quantize_rows(pool, kc, vc, slots)
+
+    def t(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = t(attn)
+    qms = t(quant)
+    pairs = T * P + T * (T + 1) // 2            # causal (query, key) pairs per head
+    flop = 4.0 * 128 * pairs * Hq               # QK^T and PV, 2 flop per MAC
+    tflops = flop / (ms * 1e-3) / 1e12
+    return {"workload": "8,192 FP8 prefix rows + 8,192-token bf16 chunk, causal, 32 q / 4 KV heads",
+            "reconstruct_plus_attention_ms": round(ms, 4), "attention_flop": flop,
+            "tflops": round(tflops, 2), "mfma_bf16_frac_of_2500": round(tflops / 2500.0, 4),
+            "quantize_chunk_us": round(qms * 1e3, 3)}
+
+
+def calibration_copies(dev, mib: int = 64, n: int = 4):
+    """Plain device-to-device copies of known size, so that rocprofv3 byte
+    counters of the decode kernel can be scaled against a kernel whose traffic
+    is known (read mib MiB + write mib MiB per copy)."""
+    import torch
+    bufs = [torch.empty(mib << 20, dtype=torch.uint8, device=dev) for _ in range(2 * n)]
+    for i in range(n):
+        bufs[2 * i + 1].copy_(bufs[2 * i])
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(case, budget_s: float):
@@ -118,6 +181,8 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.calibration_copy:
+        calibration_copies(dev)
     case = wl.layer_decode(0)  # 32,768 of 33,059 rows, 32 q / 4 KV heads
     L, Hq, Hkv = case.max_seq_len, case.n_q_heads, case.n_kv_heads
     kv_bytes = L * Hkv * KV_BYTES_PER_ROW_HEAD
@@ -255,6 +320,8 @@ def main():
             "traffic": measured_traffic(kv_bytes),
         },
     }
+    if not args.no_prefill:
+        res["prefill"] = prefill_timing(fk, wl, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(res), flush=True)
