@@ -73,15 +73,16 @@ int32_t split_cap(int32_t max_splits) {
   return (max_splits > 0 && max_splits < FP8KV_MAX_SPLITS) ? max_splits : FP8KV_MAX_SPLITS;
 }
 
-// Split choice: about one stage-1 workgroup per compute unit across the batch
-// (a workgroup has kDecodeWaves waves), each wave getting at least one group
-// of kDecodeTilesPerWave 32-key steps.
+// Split choice: about one stage-1 workgroup (kDecodeWaves waves, one LDS-full
+// workgroup per CU) per compute unit across the batch; a split covers a
+// multiple of 32 keys.
 fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
                                       int32_t max_splits, int n_cu) {
-  const int64_t unit = (int64_t)fp8kv::kDecodeWaves * fp8kv::kDecodeTilesPerWave * fp8kv::kDecodeTileKeys;
+  const int64_t unit = fp8kv::kDecodeTileKeys;
   const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t per = (int64_t)batch * n_kv_heads;
-  const int64_t target = (int64_t)n_cu;
+  const int64_t per_cu = fp8kv::kDecodeWaves >= 16 ? 1 : 16 / fp8kv::kDecodeWaves;  // LDS-limited residency
+  const int64_t target = (int64_t)n_cu * per_cu;
   int64_t want = (target + per - 1) / per;
   if (want < 1) want = 1;
   int64_t ns = want;
