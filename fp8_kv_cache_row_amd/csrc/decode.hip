@@ -32,6 +32,8 @@ namespace {
 
 constexpr int kBlock = kDecodeWaves * kWave;
 constexpr int kTileBytes = kDecodeTileKeys * kHeadDim;  // one 32-key step of K (or V) codes
+constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave stages at once
+static_assert(kGroupKeys % kWave == 0, "a group covers whole waves of row indices");
 
 // Key order inside a 32-key step: k-group j of the P*V contraction holds keys
 // 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2, int32_t* __restrict__ header,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
-  static_assert(kDecodeWaves * G * kHeadDim * 4 <= kDecodeWaves * 2 * kTileBytes, "merge buffer reuses the tiles");
+  static_assert(G * kHeadDim * 4 <= kDecodeTilesPerWave * 2 * kTileBytes, "merge buffer reuses the tiles");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n = lane & 15;
@@ -65,12 +67,11 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int h0 = g * G;
   if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 
-  // LDS: per wave one step of K and V codes, its row indices and (k, v) scales.
-  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kDecodeWaves][2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kDecodeTileKeys];
-  __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kDecodeTileKeys];
-  uint8_t* const s_k = s_tiles[wave][0];
-  uint8_t* const s_v = s_tiles[wave][1];
+  // LDS: per wave kDecodeTilesPerWave steps of K and V codes, their row
+  // indices and (k, v) scales.
+  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kDecodeWaves][kDecodeTilesPerWave][2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kGroupKeys];
+  __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kGroupKeys];
 
   // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
   // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
@@ -95,113 +96,130 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const uint8_t* vbase = v_codes + (int64_t)g * kHeadDim;
   const int32_t* trow = table + (int64_t)b * table_stride;
 
-  for (int t0 = key_begin + wave * kDecodeTileKeys; t0 < key_end; t0 += kDecodeWaves * kDecodeTileKeys) {
-    // 1. Row indices and scales of the step's 32 keys (keys past the end reuse
-    //    the last valid row and are masked out of the softmax).
-    if (lane < kDecodeTileKeys) {
-      const int key = min(t0 + lane, key_end - 1);
+  for (int k0 = key_begin + wave * kGroupKeys; k0 < key_end; k0 += kDecodeWaves * kGroupKeys) {
+    // 1. Row indices of the group's keys (keys past the end reuse the last
+    //    valid row and are masked out of the softmax).  The scale loads are
+    //    issued here but written to LDS only after the code loads are in
+    //    flight, so the two memory round trips overlap.
+    float ksc[kGroupKeys / kWave], vsc[kGroupKeys / kWave];
+#pragma unroll
+    for (int c = 0; c < kGroupKeys / kWave; ++c) {
+      const int key = min(k0 + c * kWave + lane, key_end - 1);
       const int64_t row = trow[key];
-      s_rows[wave][lane] = (int32_t)row;
-      s_sc[wave][lane] = make_float2(k_scales[row * scale_row_stride + g], v_scales[row * scale_row_stride + g]);
+      ksc[c] = k_scales[row * scale_row_stride + g];
+      vsc[c] = v_scales[row * scale_row_stride + g];
+      s_rows[wave][c * kWave + lane] = (int32_t)row;
     }
     __builtin_amdgcn_wave_barrier();
 
-    // 2. Whole 128-byte head rows: 8 lanes x 16 B per row, 8 rows per load.
-    uint4 kr[4], vr[4];
+    // 2. Whole 128-byte head rows: 8 lanes x 16 B per row, 8 rows per load;
+    //    every load of the group is issued before the first wait.
+    uint4 kr[kDecodeTilesPerWave][4], vr[kDecodeTilesPerWave][4];
 #pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx) {
-      const int64_t row = s_rows[wave][sidx * 8 + (lane >> 3)];
-      kr[sidx] = *reinterpret_cast<const uint4*>(kbase + row * code_row_stride + 16 * (lane & 7));
-      vr[sidx] = *reinterpret_cast<const uint4*>(vbase + row * code_row_stride + 16 * (lane & 7));
+    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+#pragma unroll
+      for (int sidx = 0; sidx < 4; ++sidx) {
+        const int64_t row = s_rows[wave][t * kDecodeTileKeys + sidx * 8 + (lane >> 3)];
+        kr[t][sidx] = *reinterpret_cast<const uint4*>(kbase + row * code_row_stride + 16 * (lane & 7));
+        vr[t][sidx] = *reinterpret_cast<const uint4*>(vbase + row * code_row_stride + 16 * (lane & 7));
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx) {
-      const int key = sidx * 8 + (lane >> 3);
-      *reinterpret_cast<uint4*>(s_k + kswz(key, lane & 7)) = kr[sidx];
-      *reinterpret_cast<uint4*>(s_v + key * kHeadDim + 16 * (lane & 7)) = vr[sidx];
+    for (int c = 0; c < kGroupKeys / kWave; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
+#pragma unroll
+    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+#pragma unroll
+      for (int sidx = 0; sidx < 4; ++sidx) {
+        const int key = sidx * 8 + (lane >> 3);
+        *reinterpret_cast<uint4*>(s_tiles[wave][t][0] + kswz(key, lane & 7)) = kr[t][sidx];
+        *reinterpret_cast<uint4*>(s_tiles[wave][t][1] + key * kHeadDim + 16 * (lane & 7)) = vr[t][sidx];
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
-    // 3. Operands from LDS. K: lane (n, j) takes chunks j and 4+j of keys n and 16+n.
-    const uint4 ka0 = *reinterpret_cast<const uint4*>(s_k + kswz(n, j));
-    const uint4 kb0 = *reinterpret_cast<const uint4*>(s_k + kswz(n, 4 + j));
-    const uint4 ka1 = *reinterpret_cast<const uint4*>(s_k + kswz(16 + n, j));
-    const uint4 kb1 = *reinterpret_cast<const uint4*>(s_k + kswz(16 + n, 4 + j));
-    uint2 vv[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) vv[r] = *reinterpret_cast<const uint2*>(s_v + step_key(j, r) * kHeadDim + 8 * n);
-    const float2* scp = s_sc[wave];
-    const float4 s01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
-    const float4 s23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
-    const float4 s45 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j]);
-    const float4 s67 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j + 2]);
-    const float ks[8] = {s01.x, s01.z, s23.x, s23.z, s45.x, s45.z, s67.x, s67.z};
-    const float vs[8] = {s01.y, s01.w, s23.y, s23.w, s45.y, s45.w, s67.y, s67.w};
+    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+      const int t0 = k0 + t * kDecodeTileKeys;
+      if (t0 >= key_end) break;  // wave-uniform
+      const uint8_t* s_k = s_tiles[wave][t][0];
+      const uint8_t* s_v = s_tiles[wave][t][1];
+        // 3. S^T = K * Q^T from LDS. K: lane (n, j) takes chunks j and 4+j of
+      //    keys n (block 0) and 16+n (block 1).
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      {
+        const uint4 ka = *reinterpret_cast<const uint4*>(s_k + kswz(n, j));
+        const uint4 kb = *reinterpret_cast<const uint4*>(s_k + kswz(n, 4 + j));
+        s0 = mfma16x16x32(fp8x8_to_bf16x8(ka.x, ka.y), qb[0], s0);
+        s0 = mfma16x16x32(fp8x8_to_bf16x8(ka.z, ka.w), qb[1], s0);
+        s0 = mfma16x16x32(fp8x8_to_bf16x8(kb.x, kb.y), qb[2], s0);
+        s0 = mfma16x16x32(fp8x8_to_bf16x8(kb.z, kb.w), qb[3], s0);
+      }
+      {
+        const uint4 ka = *reinterpret_cast<const uint4*>(s_k + kswz(16 + n, j));
+        const uint4 kb = *reinterpret_cast<const uint4*>(s_k + kswz(16 + n, 4 + j));
+        s1 = mfma16x16x32(fp8x8_to_bf16x8(ka.x, ka.y), qb[0], s1);
+        s1 = mfma16x16x32(fp8x8_to_bf16x8(ka.z, ka.w), qb[1], s1);
+        s1 = mfma16x16x32(fp8x8_to_bf16x8(kb.x, kb.y), qb[2], s1);
+        s1 = mfma16x16x32(fp8x8_to_bf16x8(kb.z, kb.w), qb[3], s1);
+      }
+      const float2* scp = &s_sc[wave][t * kDecodeTileKeys];
 
-    // S^T = K * Q^T for the two 16-key blocks.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(ka0.x, ka0.y), qb[0], s0);
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(ka0.z, ka0.w), qb[1], s0);
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(kb0.x, kb0.y), qb[2], s0);
-    s0 = mfma16x16x32(fp8x8_to_bf16x8(kb0.z, kb0.w), qb[3], s0);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(ka1.x, ka1.y), qb[0], s1);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(ka1.z, ka1.w), qb[1], s1);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(kb1.x, kb1.y), qb[2], s1);
-    s1 = mfma16x16x32(fp8x8_to_bf16x8(kb1.z, kb1.w), qb[3], s1);
+      // Scores in log2 units for head n, keys step_key(j, r).
+      float sv[8];
+  #pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float raw = (r < 4) ? s0[r] : s1[r - 4];
+        const bool valid = (t0 + step_key(j, r)) < key_end;
+        sv[r] = valid ? raw * scp[step_key(j, r)].x * qk_scale_log2 : -INFINITY;
+      }
+      float tmax = sv[0];
+  #pragma unroll
+      for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, sv[r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
 
-    // Scores in log2 units for head n, keys step_key(j, r).
-    float sv[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float raw = (r < 4) ? s0[r] : s1[r - 4];
-      const bool valid = (t0 + step_key(j, r)) < key_end;
-      sv[r] = valid ? raw * ks[r] * qk_scale_log2 : -INFINITY;
+      float psum = 0.0f;
+      uint32_t pw[4];
+  #pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const float p0 = exp2f(sv[r] - m_new), p1 = exp2f(sv[r + 1] - m_new);
+        psum += p0 + p1;
+        // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
+        pw[r / 2] = f32x2_to_bf16x2(p0 * scp[step_key(j, r)].y, p1 * scp[step_key(j, r + 1)].y);
+      }
+      l_part = l_part * alpha + psum;
+      const bf16x8 pa = u4_as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+
+      // Rescale O rows (heads 4j+i) by their head's alpha.
+      float ai[4];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+  #pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
+      }
+
+      // V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
+      // V[key][d = 8n + nb] for the lane's 8 keys (byte-transposed in registers).
+      uint32_t lo[8], hi[8];
+      {
+        uint2 vv[8];
+  #pragma unroll
+        for (int r = 0; r < 8; ++r) vv[r] = *reinterpret_cast<const uint2*>(s_v + step_key(j, r) * kHeadDim + 8 * n);
+        transpose4x4_bytes(vv[0].x, vv[1].x, vv[2].x, vv[3].x, lo[0], lo[1], lo[2], lo[3]);
+        transpose4x4_bytes(vv[4].x, vv[5].x, vv[6].x, vv[7].x, hi[0], hi[1], hi[2], hi[3]);
+        transpose4x4_bytes(vv[0].y, vv[1].y, vv[2].y, vv[3].y, lo[4], lo[5], lo[6], lo[7]);
+        transpose4x4_bytes(vv[4].y, vv[5].y, vv[6].y, vv[7].y, hi[4], hi[5], hi[6], hi[7]);
+      }
+  #pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
     }
-    float tmax = sv[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, sv[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-
-    float p[8], psum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p[r] = exp2f(sv[r] - m_new);
-      psum += p[r];
-    }
-    l_part = l_part * alpha + psum;
-
-    // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
-    uint4 pu;
-    pu.x = f32x2_to_bf16x2(p[0] * vs[0], p[1] * vs[1]);
-    pu.y = f32x2_to_bf16x2(p[2] * vs[2], p[3] * vs[3]);
-    pu.z = f32x2_to_bf16x2(p[4] * vs[4], p[5] * vs[5]);
-    pu.w = f32x2_to_bf16x2(p[6] * vs[6], p[7] * vs[7]);
-    const bf16x8 pa = u4_as_bf16x8(pu);
-
-    // Rescale O rows (heads 4j+i) by their head's alpha.
-    float ai[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
-    }
-
-    // V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
-    // V[key][d = 8n + nb] for the lane's 8 keys.
-    uint32_t lo[8], hi[8];
-    transpose4x4_bytes(vv[0].x, vv[1].x, vv[2].x, vv[3].x, lo[0], lo[1], lo[2], lo[3]);
-    transpose4x4_bytes(vv[4].x, vv[5].x, vv[6].x, vv[7].x, hi[0], hi[1], hi[2], hi[3]);
-    transpose4x4_bytes(vv[0].y, vv[1].y, vv[2].y, vv[3].y, lo[4], lo[5], lo[6], lo[7]);
-    transpose4x4_bytes(vv[4].y, vv[5].y, vv[6].y, vv[7].y, hi[4], hi[5], hi[6], hi[7]);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
-    __builtin_amdgcn_wave_barrier();  // this step's LDS is consumed before the next overwrites it
+    __builtin_amdgcn_wave_barrier();  // this group's LDS is consumed before the next overwrites it
   }
 
   // Per-head totals of this wave.
@@ -211,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __syncthreads();  // every wave is done with its tiles; reuse them for the merge
-  float* sm_o = reinterpret_cast<float*>(&s_tiles[0][0][0]);  // [wave][G][128]
+  float* sm_o = reinterpret_cast<float*>(&s_tiles[0][0][0][0]);  // [wave][G][128]
   if (j == 0) {
     sm_m[wave][n] = m_run;
     sm_l[wave][n] = l_tot;

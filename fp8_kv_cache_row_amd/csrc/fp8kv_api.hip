@@ -81,7 +81,9 @@ fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t
   const int64_t unit = fp8kv::kDecodeTileKeys;
   const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t per = (int64_t)batch * n_kv_heads;
-  const int64_t per_cu = fp8kv::kDecodeWaves >= 16 ? 1 : 16 / fp8kv::kDecodeWaves;  // LDS-limited residency
+  // LDS holds kDecodeTilesPerWave steps per wave; 128 KB of staging fits one workgroup per CU
+  const int64_t staged = (int64_t)fp8kv::kDecodeWaves * fp8kv::kDecodeTilesPerWave;
+  const int64_t per_cu = staged >= 16 ? 1 : 16 / staged;
   const int64_t target = (int64_t)n_cu * per_cu;
   int64_t want = (target + per - 1) / per;
   if (want < 1) want = 1;

@@ -25,13 +25,17 @@ struct DecodeGeometry {
 };
 
 #ifndef FP8KV_DECODE_WAVES
-#define FP8KV_DECODE_WAVES 16
+#define FP8KV_DECODE_WAVES 8
+#endif
+#ifndef FP8KV_DECODE_TILES_PER_WAVE
+#define FP8KV_DECODE_TILES_PER_WAVE 2
 #endif
 // Must equal FP8KV_MAX_SPLITS of the public header (checked in the C ABI).
 #define FP8KV_MAX_SPLITS_INTERNAL 256
 
-constexpr int kDecodeWaves = FP8KV_DECODE_WAVES;  // waves per stage-1 workgroup
-constexpr int kDecodeTileKeys = 32;               // keys per wave per MFMA step
+constexpr int kDecodeWaves = FP8KV_DECODE_WAVES;                 // waves per stage-1 workgroup
+constexpr int kDecodeTileKeys = 32;                              // keys per wave per MFMA step
+constexpr int kDecodeTilesPerWave = FP8KV_DECODE_TILES_PER_WAVE;  // steps a wave stages in LDS at once
 
 hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const uint16_t* v,
                                 int64_t src_token_stride, const int32_t* slots, int32_t n_tokens,
