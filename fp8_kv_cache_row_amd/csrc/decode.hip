@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
     int64_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
-    int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2, int32_t* __restrict__ header,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
+    int32_t* __restrict__ header, float* __restrict__ part_o, float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
   static_assert(G * kHeadDim * 4 <= kDecodeTilesPerWave * 2 * kTileBytes, "merge buffer reuses the tiles");
   const int lane = threadIdx.x & (kWave - 1);
@@ -61,8 +61,9 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = seq_lens[b];
+  const int L = seq_lens[b];  // its load overlaps the first (speculative) table loads
   const int key_begin = split * chunk;
+  const int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
   const int key_end = min(key_begin + chunk, L);
   const int h0 = g * G;
   if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
@@ -96,21 +97,36 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const uint8_t* vbase = v_codes + (int64_t)g * kHeadDim;
   const int32_t* trow = table + (int64_t)b * table_stride;
 
-  for (int k0 = key_begin + wave * kGroupKeys; k0 < key_end; k0 += kDecodeWaves * kGroupKeys) {
-    // 1. Row indices of the group's keys (keys past the end reuse the last
-    //    valid row and are masked out of the softmax).  The scale loads are
-    //    issued here but written to LDS only after the code loads are in
-    //    flight, so the two memory round trips overlap.
+  for (int k0 = key_begin + wave * kGroupKeys; k0 < key_bound; k0 += kDecodeWaves * kGroupKeys) {
+    // 1. Row indices of the group's keys.  The table is read speculatively up
+    //    to the host-side bound (always inside the table), so the load does not
+    //    wait for seq_lens; keys at or past the request's length then take the
+    //    row of its last key (in bounds, finite codes) and are masked out of
+    //    the softmax.
+    int32_t row_s[kGroupKeys / kWave];
+#pragma unroll
+    for (int c = 0; c < kGroupKeys / kWave; ++c) row_s[c] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
+    if (k0 >= key_end) break;  // wave-uniform: nothing of this request left here
+#pragma unroll
+    for (int c = 0; c < kGroupKeys / kWave; ++c) s_rows[wave][c * kWave + lane] = row_s[c];
+    __builtin_amdgcn_wave_barrier();
+    const int last = key_end - 1 - k0;  // index of the request's last key in this group
+    if (last < kGroupKeys - 1) {
+      const int32_t last_row = s_rows[wave][last];
+#pragma unroll
+      for (int c = 0; c < kGroupKeys / kWave; ++c)
+        if (c * kWave + lane > last) s_rows[wave][c * kWave + lane] = last_row;
+      __builtin_amdgcn_wave_barrier();
+    }
+    // The scale loads are issued here but written to LDS only after the code
+    // loads are in flight, so the two memory round trips overlap.
     float ksc[kGroupKeys / kWave], vsc[kGroupKeys / kWave];
 #pragma unroll
     for (int c = 0; c < kGroupKeys / kWave; ++c) {
-      const int key = min(k0 + c * kWave + lane, key_end - 1);
-      const int64_t row = trow[key];
+      const int64_t row = s_rows[wave][c * kWave + lane];
       ksc[c] = k_scales[row * scale_row_stride + g];
       vsc[c] = v_scales[row * scale_row_stride + g];
-      s_rows[wave][c * kWave + lane] = (int32_t)row;
     }
-    __builtin_amdgcn_wave_barrier();
 
     // 2. Whole 128-byte head rows: 8 lanes x 16 B per row, 8 rows per load;
     //    every load of the group is issued before the first wait.
@@ -127,23 +143,21 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < kGroupKeys / kWave; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
-#pragma unroll
-    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
-#pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) {
-        const int key = sidx * 8 + (lane >> 3);
-        *reinterpret_cast<uint4*>(s_tiles[wave][t][0] + kswz(key, lane & 7)) = kr[t][sidx];
-        *reinterpret_cast<uint4*>(s_tiles[wave][t][1] + key * kHeadDim + 16 * (lane & 7)) = vr[t][sidx];
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
 
 #pragma unroll
     for (int t = 0; t < kDecodeTilesPerWave; ++t) {
       const int t0 = k0 + t * kDecodeTileKeys;
       if (t0 >= key_end) break;  // wave-uniform
-      const uint8_t* s_k = s_tiles[wave][t][0];
-      const uint8_t* s_v = s_tiles[wave][t][1];
+      uint8_t* s_k = s_tiles[wave][t][0];
+      uint8_t* s_v = s_tiles[wave][t][1];
+      // stage this step's codes (waits only for this step's loads)
+#pragma unroll
+      for (int sidx = 0; sidx < 4; ++sidx) {
+        const int key = sidx * 8 + (lane >> 3);
+        *reinterpret_cast<uint4*>(s_k + kswz(key, lane & 7)) = kr[t][sidx];
+        *reinterpret_cast<uint4*>(s_v + key * kHeadDim + 16 * (lane & 7)) = vr[t][sidx];
+      }
+      __builtin_amdgcn_wave_barrier();
         // 3. S^T = K * Q^T from LDS. K: lane (n, j) takes chunks j and 4+j of
       //    keys n (block 0) and 16+n (block 1).
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -333,13 +347,13 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
 template <int G>
 hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                            const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                           float qk_scale_log2, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                           int32_t max_seq_len, float qk_scale_log2, const DecodeGeometry& geo, const DecodeWorkspace& ws,
                            hipStream_t stream) {
   dim3 grid((unsigned)geo.n_split, (unsigned)pool.n_kv_heads, (unsigned)batch);
   hipLaunchKernelGGL(decode_stage1_kernel<G>, grid, dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
                      pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride, q, n_q_heads,
-                     row_table, table_stride, seq_lens, geo.n_split, geo.chunk, ws.split_stride, qk_scale_log2,
-                     ws.header, ws.part_o, ws.part_lse);
+                     row_table, table_stride, seq_lens, max_seq_len, geo.n_split, geo.chunk, ws.split_stride,
+                     qk_scale_log2, ws.header, ws.part_o, ws.part_lse);
   return hipGetLastError();
 }
 
@@ -347,15 +361,15 @@ hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batc
 
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                                 const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                                float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                                int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
                                 hipStream_t stream) {
   const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
   switch (n_q_heads / pool.n_kv_heads) {
-    case 1: return launch_stage1_g<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
-    case 2: return launch_stage1_g<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
-    case 4: return launch_stage1_g<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
-    case 8: return launch_stage1_g<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
-    case 16: return launch_stage1_g<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, qk_scale_log2, geo, ws, stream);
+    case 1: return launch_stage1_g<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
+    case 2: return launch_stage1_g<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
+    case 4: return launch_stage1_g<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
+    case 8: return launch_stage1_g<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
+    case 16: return launch_stage1_g<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -170,7 +170,7 @@ fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer* pool, const uint16_t* q
   if (st != FP8KV_OK) return st;
   const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
   return from_hip(fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride,
-                                              seq_lens, sm_scale, geo,
+                                              seq_lens, max_seq_len, sm_scale, geo,
                                               workspace_view(workspace, batch, n_q_heads, max_splits),
                                               static_cast<hipStream_t>(stream)));
 }
@@ -205,7 +205,7 @@ fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, 
   const fp8kv::DecodeWorkspace ws = workspace_view(workspace, batch, n_q_heads, max_splits);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
-                                             sm_scale, geo, ws, s);
+                                             max_seq_len, sm_scale, geo, ws, s);
   if (e != hipSuccess) return FP8KV_ERR_HIP;
   return from_hip(fp8kv::launch_decode_merge(batch, n_q_heads, ws, out, s));
 }

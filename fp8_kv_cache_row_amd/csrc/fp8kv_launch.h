@@ -57,7 +57,7 @@ constexpr size_t kDecodeHeaderBytes = 256;
 
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                                 const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                                float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                                int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
                                 hipStream_t stream);
 
 hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, uint16_t* out,
