@@ -3,26 +3,32 @@
 // FreeToken PR #897 "perf(attention): add packed fp8 kv reads on gfx1201",
 // description and "Fresh R9700 stage-1 A/B": a first stage computes one
 // partial per (head group, split) over FP8 rows fetched through the row table
-// (page size 1, randomized physical slots), a merge kernel combines the
-// partials; packed 4-byte-granular code reads and native converts.  FreeToken
-// PR #853 "What changes": per-row FP32 scales stored next to the codes.
+// (page size 1, randomized physical slots) and a merge kernel combines the
+// partials.  FreeToken PR #853 "What changes": per-row FP32 scales.
 //
 // gfx950 design (not the pages' RDNA4 kernel):
-//  * One wave owns 32 keys of one KV head per step.  QK^T runs on the bf16
-//    MFMA 16x16x32 with the E4M3 codes widened exactly to bf16 (every finite
-//    E4M3FN value is a bf16 value); the per-row K scale and the softmax scale
-//    multiply the 16x16 score tile afterwards.  S^T = K * Q^T puts keys on the
-//    MFMA rows and the G query heads of the group on the columns, so each
-//    lane ends up with 8 keys of one head: the per-head tile max needs only
-//    two cross-lane steps.
-//  * Those 8 keys are exactly the k-slots the lane feeds to the P*V MFMA, so
-//    the probabilities (times the per-row V scale, folded into P) never move
-//    between lanes.  V is fetched as 8-byte row segments (16 lanes cover a
-//    128-byte head row) and byte-transposed in registers.
-//  * Every code byte of a row is loaded exactly once, with 16-byte (K) and
-//    8-byte (V) vector loads that cover whole 128-byte head rows per 16 lanes.
-//  * Stage 2 merges the per-split (o, log2-sum-exp) partials.
+//  * A workgroup (8 waves) covers one split of one (request, KV head); a wave
+//    stages two 32-key steps at a time.  Row indices come from the table,
+//    read speculatively up to the host-side length bound so the read does not
+//    wait for seq_lens.  Codes are fetched as whole 128-byte head rows (8 lanes
+//    x 16 B per row, 8 rows per load), every load of the group in flight before
+//    the first wait, and staged in LDS (K with an XOR chunk swizzle, V rows
+//    padded to 160 B) so the MFMA operands are conflict-light LDS reads.
+//  * QK^T runs on the bf16 MFMA 16x16x32 with E4M3 codes widened exactly to
+//    bf16.  S^T = K * Q^T puts keys on the MFMA rows and the G query heads of
+//    the group on the columns, so each lane holds 8 keys of one head: the
+//    per-head maximum needs two cross-lane steps, and those 8 keys are exactly
+//    the k-slots this lane feeds to the P*V MFMA, so P never moves between
+//    lanes.  The per-row K scale and the softmax scale multiply the score tile
+//    after the MFMA; the per-row V scale is folded into P.
+//  * Online softmax in log2 units with a lazy maximum: the running maximum
+//    moves (and O is rescaled) only when a step's maximum exceeds it by more
+//    than 8, so p stays below 2^8 and most steps skip the rescale.
+//  * Waves merge through LDS; one (o, log2-sum-exp) partial per split.
+
 #include <math.h>
+
+#include <type_traits>
 
 #include "fp8kv_device.h"
 
@@ -31,9 +37,13 @@ namespace fp8kv {
 namespace {
 
 constexpr int kBlock = kDecodeWaves * kWave;
-constexpr int kTileBytes = kDecodeTileKeys * kHeadDim;  // one 32-key step of K (or V) codes
+constexpr int kTileBytes = kDecodeTileKeys * kHeadDim;              // one 32-key step of K codes
+constexpr int kVRowBytes = kHeadDim + 32;                           // V rows padded to 160 B in LDS
+constexpr int kVTileBytes = kDecodeTileKeys * kVRowBytes;
 constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave stages at once
 static_assert(kGroupKeys % kWave == 0, "a group covers whole waves of row indices");
+static_assert(kDecodeTilesPerWave >= 1 && kDecodeTilesPerWave <= 4, "up to four staged steps per wave");
+constexpr float kLazyMaxSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 // Key order inside a 32-key step: k-group j of the P*V contraction holds keys
 // 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
@@ -44,16 +54,18 @@ __device__ __forceinline__ int step_key(int j, int r) { return (r < 4) ? 4 * j +
 // MFMA operand then touch 16 different 16-byte bank groups.
 __device__ __forceinline__ int kswz(int key, int chunk) { return key * kHeadDim + ((chunk ^ (key & 7)) << 4); }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int G>
 __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
-    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
-    int64_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, uint32_t code_row_stride,
+    uint32_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
     int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
     int32_t* __restrict__ header, float* __restrict__ part_o, float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
-  static_assert(G * kHeadDim * 4 <= kDecodeTilesPerWave * 2 * kTileBytes, "merge buffer reuses the tiles");
+  static_assert(G * kHeadDim * 4 <= kDecodeTilesPerWave * (kTileBytes + kVTileBytes), "merge buffer reuses the tiles");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n = lane & 15;
@@ -61,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = seq_lens[b];  // its load overlaps the first (speculative) table loads
+  const int L = seq_lens[b];  // its load overlaps the first (speculative) table reads
   const int key_begin = split * chunk;
   const int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
   const int key_end = min(key_begin + chunk, L);
@@ -70,9 +82,15 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 
   // LDS: per wave kDecodeTilesPerWave steps of K and V codes, their row
   // indices and (k, v) scales.
-  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kDecodeWaves][kDecodeTilesPerWave][2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_kt[kDecodeWaves][kDecodeTilesPerWave][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kDecodeWaves][kDecodeTilesPerWave][kVTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kGroupKeys];
   __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kGroupKeys];
+
+  // Code addresses: row * stride (32 x 32 -> 64-bit) + this lane's 16-byte chunk.
+  const uint64_t kbase = reinterpret_cast<uint64_t>(k_codes) + (uint64_t)g * kHeadDim + 16 * (lane & 7);
+  const uint64_t vbase = reinterpret_cast<uint64_t>(v_codes) + (uint64_t)g * kHeadDim + 16 * (lane & 7);
+  const int32_t* trow = table + (int64_t)b * table_stride;
 
   // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
   // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
@@ -87,19 +105,15 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     qb[kk] = u4_as_bf16x8(u);
   }
 
-  float m_run = -INFINITY;  // running max (log2 units) of head n
-  float l_part = 0.0f;      // running sum of p for head n over this lane's keys
+  float m_run = -INFINITY;  // running (lazy) max, log2 units, of head n
+  float l_part = 0.0f;      // sum of p for head n over this lane's keys
   f32x4 o[8];               // O[head 4j+i][d = 8n + nb]
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* kbase = k_codes + (int64_t)g * kHeadDim;
-  const uint8_t* vbase = v_codes + (int64_t)g * kHeadDim;
-  const int32_t* trow = table + (int64_t)b * table_stride;
-
   for (int k0 = key_begin + wave * kGroupKeys; k0 < key_bound; k0 += kDecodeWaves * kGroupKeys) {
     // 1. Row indices of the group's keys.  The table is read speculatively up
-    //    to the host-side bound (always inside the table), so the load does not
+    //    to the host-side bound (always inside the table), so the read does not
     //    wait for seq_lens; keys at or past the request's length then take the
     //    row of its last key (in bounds, finite codes) and are masked out of
     //    the softmax.
@@ -123,43 +137,46 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     float ksc[kGroupKeys / kWave], vsc[kGroupKeys / kWave];
 #pragma unroll
     for (int c = 0; c < kGroupKeys / kWave; ++c) {
-      const int64_t row = s_rows[wave][c * kWave + lane];
-      ksc[c] = k_scales[row * scale_row_stride + g];
-      vsc[c] = v_scales[row * scale_row_stride + g];
+      const uint32_t row = (uint32_t)s_rows[wave][c * kWave + lane];
+      const uint64_t off = (uint64_t)row * scale_row_stride + g;
+      ksc[c] = k_scales[off];
+      vsc[c] = v_scales[off];
     }
 
     // 2. Whole 128-byte head rows: 8 lanes x 16 B per row, 8 rows per load;
     //    every load of the group is issued before the first wait.
-    uint4 kr[kDecodeTilesPerWave][4], vr[kDecodeTilesPerWave][4];
+    u32x4 kr[kDecodeTilesPerWave][4], vr[kDecodeTilesPerWave][4];  // native vectors: stay in registers
 #pragma unroll
     for (int t = 0; t < kDecodeTilesPerWave; ++t) {
 #pragma unroll
       for (int sidx = 0; sidx < 4; ++sidx) {
-        const int64_t row = s_rows[wave][t * kDecodeTileKeys + sidx * 8 + (lane >> 3)];
-        kr[t][sidx] = *reinterpret_cast<const uint4*>(kbase + row * code_row_stride + 16 * (lane & 7));
-        vr[t][sidx] = *reinterpret_cast<const uint4*>(vbase + row * code_row_stride + 16 * (lane & 7));
+        const uint64_t roff = (uint64_t)(uint32_t)s_rows[wave][t * kDecodeTileKeys + sidx * 8 + (lane >> 3)] * code_row_stride;
+        kr[t][sidx] = *reinterpret_cast<const u32x4*>(kbase + roff);
+        vr[t][sidx] = *reinterpret_cast<const u32x4*>(vbase + roff);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < kGroupKeys / kWave; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
 
-#pragma unroll
-    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+    // One 32-key step; t is a compile-time constant so kr/vr stay in registers.
+    auto step = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
       const int t0 = k0 + t * kDecodeTileKeys;
-      if (t0 >= key_end) break;  // wave-uniform
-      uint8_t* s_k = s_tiles[wave][t][0];
-      uint8_t* s_v = s_tiles[wave][t][1];
-      // stage this step's codes (waits only for this step's loads)
+      if (t0 >= key_end) return;  // wave-uniform
+      uint8_t* s_k = s_kt[wave][t];
+      uint8_t* s_v = s_vt[wave][t];
+      // Stage this step's codes (waits only for this step's loads).
 #pragma unroll
       for (int sidx = 0; sidx < 4; ++sidx) {
         const int key = sidx * 8 + (lane >> 3);
-        *reinterpret_cast<uint4*>(s_k + kswz(key, lane & 7)) = kr[t][sidx];
-        *reinterpret_cast<uint4*>(s_v + key * kHeadDim + 16 * (lane & 7)) = vr[t][sidx];
+        *reinterpret_cast<u32x4*>(s_k + kswz(key, lane & 7)) = kr[t][sidx];
+        *reinterpret_cast<u32x4*>(s_v + key * kVRowBytes + 16 * (lane & 7)) = vr[t][sidx];
       }
       __builtin_amdgcn_wave_barrier();
-        // 3. S^T = K * Q^T from LDS. K: lane (n, j) takes chunks j and 4+j of
-      //    keys n (block 0) and 16+n (block 1).
+
+      // 3. S^T = K * Q^T: lane (n, j) takes chunks j and 4+j of keys n (block 0)
+      //    and 16+n (block 1).
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       {
         const uint4 ka = *reinterpret_cast<const uint4*>(s_k + kswz(n, j));
@@ -178,61 +195,69 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
         s1 = mfma16x16x32(fp8x8_to_bf16x8(kb.z, kb.w), qb[3], s1);
       }
       const float2* scp = &s_sc[wave][t * kDecodeTileKeys];
+      const float4 c01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
+      const float4 c23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
+      const float4 c45 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j]);
+      const float4 c67 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j + 2]);
 
       // Scores in log2 units for head n, keys step_key(j, r).
-      float sv[8];
-  #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float raw = (r < 4) ? s0[r] : s1[r - 4];
-        const bool valid = (t0 + step_key(j, r)) < key_end;
-        sv[r] = valid ? raw * scp[step_key(j, r)].x * qk_scale_log2 : -INFINITY;
+      float sv[8] = {s0[0] * c01.x, s0[1] * c01.z, s0[2] * c23.x, s0[3] * c23.z,
+                     s1[0] * c45.x, s1[1] * c45.z, s1[2] * c67.x, s1[3] * c67.z};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) sv[r] *= qk_scale_log2;
+      if (t0 + kDecodeTileKeys > key_end) {  // wave-uniform: only the request's last step is partial
+#pragma unroll
+        for (int r = 0; r < 8; ++r) sv[r] = (t0 + step_key(j, r) < key_end) ? sv[r] : -INFINITY;
       }
-      float tmax = sv[0];
-  #pragma unroll
-      for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, sv[r]);
+      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
 
-      float psum = 0.0f;
-      uint32_t pw[4];
-  #pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        const float p0 = exp2f(sv[r] - m_new), p1 = exp2f(sv[r + 1] - m_new);
-        psum += p0 + p1;
-        // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
-        pw[r / 2] = f32x2_to_bf16x2(p0 * scp[step_key(j, r)].y, p1 * scp[step_key(j, r + 1)].y);
-      }
-      l_part = l_part * alpha + psum;
-      const bf16x8 pa = u4_as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-
-      // Rescale O rows (heads 4j+i) by their head's alpha.
-      float ai[4];
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
-  #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
+      // Lazy maximum: move it (and rescale O and l) only when this step's
+      // maximum exceeds it by more than the slack; otherwise p <= 2^slack.
+      if (__any(tmax > m_run + kLazyMaxSlack)) {
+        const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_part *= alpha;
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
+        }
       }
 
-      // V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
-      // V[key][d = 8n + nb] for the lane's 8 keys (byte-transposed in registers).
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p[r] = fast_exp2(sv[r] - m_run);
+      l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
+      const uint4 pu = make_uint4(f32x2_to_bf16x2(p[0] * c01.y, p[1] * c01.w), f32x2_to_bf16x2(p[2] * c23.y, p[3] * c23.w),
+                                  f32x2_to_bf16x2(p[4] * c45.y, p[5] * c45.w), f32x2_to_bf16x2(p[6] * c67.y, p[7] * c67.w));
+      const bf16x8 pa = u4_as_bf16x8(pu);
+
+      // 4. V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
+      //    V[key][d = 8n + nb] for the lane's 8 keys (byte-transposed in registers).
       uint32_t lo[8], hi[8];
       {
         uint2 vv[8];
-  #pragma unroll
-        for (int r = 0; r < 8; ++r) vv[r] = *reinterpret_cast<const uint2*>(s_v + step_key(j, r) * kHeadDim + 8 * n);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) vv[r] = *reinterpret_cast<const uint2*>(s_v + step_key(j, r) * kVRowBytes + 8 * n);
         transpose4x4_bytes(vv[0].x, vv[1].x, vv[2].x, vv[3].x, lo[0], lo[1], lo[2], lo[3]);
         transpose4x4_bytes(vv[4].x, vv[5].x, vv[6].x, vv[7].x, hi[0], hi[1], hi[2], hi[3]);
         transpose4x4_bytes(vv[0].y, vv[1].y, vv[2].y, vv[3].y, lo[4], lo[5], lo[6], lo[7]);
         transpose4x4_bytes(vv[4].y, vv[5].y, vv[6].y, vv[7].y, hi[4], hi[5], hi[6], hi[7]);
       }
-  #pragma unroll
+#pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
-    }
+    };
+    step(std::integral_constant<int, 0>{});
+    if constexpr (kDecodeTilesPerWave > 1) step(std::integral_constant<int, 1>{});
+    if constexpr (kDecodeTilesPerWave > 2) step(std::integral_constant<int, 2>{});
+    if constexpr (kDecodeTilesPerWave > 3) step(std::integral_constant<int, 3>{});
     __builtin_amdgcn_wave_barrier();  // this group's LDS is consumed before the next overwrites it
   }
 
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __syncthreads();  // every wave is done with its tiles; reuse them for the merge
-  float* sm_o = reinterpret_cast<float*>(&s_tiles[0][0][0][0]);  // [wave][G][128]
+  float* sm_o = reinterpret_cast<float*>(&s_kt[0][0][0]);  // [wave][G][128]
   if (j == 0) {
     sm_m[wave][n] = m_run;
     sm_l[wave][n] = l_tot;
@@ -252,34 +277,39 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   for (int i = 0; i < 4; ++i) {
     const int head = 4 * j + i;
     if (head < G) {
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) sm_o[(wave * G + head) * kHeadDim + 8 * n + nb] = o[nb][i];
+      float* dst = sm_o + (wave * G + head) * kHeadDim + 8 * n;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
     }
   }
   __syncthreads();
 
-  // Merge the waves of this workgroup into one partial per query head.
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kBlock) {
-    const int h = idx / kHeadDim;
-    const int d = idx % kHeadDim;
+  // Merge the waves of this workgroup into one partial per query head; a
+  // thread produces 4 consecutive d of one head.
+  for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kBlock) {
+    const int h = idx / (kHeadDim / 4);
+    const int d = 4 * (idx % (kHeadDim / 4));
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float oval = 0.0f, lse = -INFINITY;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
     if (M != -INFINITY) {
-      float num = 0.0f, den = 0.0f;
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
-        const float wt = exp2f(sm_m[w][h] - M);
-        num += wt * sm_o[(w * G + h) * kHeadDim + d];
+        const float wt = fast_exp2(sm_m[w][h] - M);
+        const float4 v = *reinterpret_cast<const float4*>(sm_o + (w * G + h) * kHeadDim + d);
+        num.x += wt * v.x;
+        num.y += wt * v.y;
+        num.z += wt * v.z;
+        num.w += wt * v.w;
         den += wt * sm_l[w][h];
       }
-      oval = num / den;
-      lse = M + log2f(den);
     }
+    const float inv = (den > 0.f) ? 1.0f / den : 0.0f;
     const int64_t ph = ((int64_t)b * n_q_heads + h0 + h) * split_stride + split;
-    part_o[ph * kHeadDim + d] = oval;
-    if (d == 0) part_lse[ph] = lse;
+    *reinterpret_cast<float4*>(part_o + ph * kHeadDim + d) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    if (d == 0) part_lse[ph] = (den > 0.f) ? M + log2f(den) : -INFINITY;
   }
 }
 
@@ -351,7 +381,8 @@ hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batc
                            hipStream_t stream) {
   dim3 grid((unsigned)geo.n_split, (unsigned)pool.n_kv_heads, (unsigned)batch);
   hipLaunchKernelGGL(decode_stage1_kernel<G>, grid, dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
-                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride, q, n_q_heads,
+                     pool.k_scales, pool.v_scales, (uint32_t)pool.code_row_stride, (uint32_t)pool.scale_row_stride,
+                     q, n_q_heads,
                      row_table, table_stride, seq_lens, max_seq_len, geo.n_split, geo.chunk, ws.split_stride,
                      qk_scale_log2, ws.header, ws.part_o, ws.part_lse);
   return hipGetLastError();
