@@ -112,26 +112,15 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = key_begin + wave * kGroupKeys; k0 < key_bound; k0 += kDecodeWaves * kGroupKeys) {
-    // 1. Row indices of the group's keys.  The table is read speculatively up
-    //    to the host-side bound (always inside the table), so the read does not
-    //    wait for seq_lens; keys at or past the request's length then take the
-    //    row of its last key (in bounds, finite codes) and are masked out of
+    // 1. Row indices of the group's keys, read up to the host-side bound.
+    //    Every table entry below max_seq_len is a valid physical row (padding
+    //    included), so neither the table read nor the code loads wait for
+    //    seq_lens; keys at or past the request's length are only masked out of
     //    the softmax.
-    int32_t row_s[kGroupKeys / kWave];
 #pragma unroll
-    for (int c = 0; c < kGroupKeys / kWave; ++c) row_s[c] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
-    if (k0 >= key_end) break;  // wave-uniform: nothing of this request left here
-#pragma unroll
-    for (int c = 0; c < kGroupKeys / kWave; ++c) s_rows[wave][c * kWave + lane] = row_s[c];
+    for (int c = 0; c < kGroupKeys / kWave; ++c)
+      s_rows[wave][c * kWave + lane] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
     __builtin_amdgcn_wave_barrier();
-    const int last = key_end - 1 - k0;  // index of the request's last key in this group
-    if (last < kGroupKeys - 1) {
-      const int32_t last_row = s_rows[wave][last];
-#pragma unroll
-      for (int c = 0; c < kGroupKeys / kWave; ++c)
-        if (c * kWave + lane > last) s_rows[wave][c * kWave + lane] = last_row;
-      __builtin_amdgcn_wave_barrier();
-    }
     // The scale loads are issued here but written to LDS only after the code
     // loads are in flight, so the two memory round trips overlap.
     float ksc[kGroupKeys / kWave], vsc[kGroupKeys / kWave];
@@ -163,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     auto step = [&](auto tc) {
       constexpr int t = decltype(tc)::value;
       const int t0 = k0 + t * kDecodeTileKeys;
-      if (t0 >= key_end) return;  // wave-uniform
+      if (t0 >= key_end) return;  // wave-uniform (waits for seq_lens only here)
       uint8_t* s_k = s_kt[wave][t];
       uint8_t* s_v = s_vt[wave][t];
       // Stage this step's codes (waits only for this step's loads).
@@ -323,7 +312,8 @@ static_assert(FP8KV_MAX_SPLITS_INTERNAL <= kMergeBlock, "one merge thread per sp
 __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t* __restrict__ header,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_lse,
-                                                                  int32_t split_stride, uint16_t* __restrict__ out) {
+                                                                  int32_t split_stride, int32_t n_split_arg,
+                                                                  uint16_t* __restrict__ out) {
   __shared__ float s_w[kMergeBlock];
   __shared__ float s_red[kMergeBlock / kWave];
   __shared__ float2 s_acc[kMergeBlock / kWave][kWave];
@@ -331,8 +321,18 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int n_split = header[0];
+  const int n_split = n_split_arg >= 0 ? n_split_arg : header[0];
 
+  // Issue every partial load of this workgroup before any reduction: the
+  // split vectors do not depend on the weights.
+  constexpr int kPerWave = FP8KV_MAX_SPLITS_INTERNAL / (kMergeBlock / kWave);
+  const float* po = part_o + bh * split_stride * kHeadDim + 2 * lane;
+  float2 v[kPerWave];
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int s = wave + i * (kMergeBlock / kWave);
+    v[i] = (s < n_split) ? *reinterpret_cast<const float2*>(po + (int64_t)s * kHeadDim) : make_float2(0.f, 0.f);
+  }
   const float lse = (tid < n_split) ? part_lse[bh * split_stride + tid] : -INFINITY;
   float m = lse;
 #pragma unroll
@@ -342,19 +342,18 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   float M = s_red[0];
 #pragma unroll
   for (int w = 1; w < kMergeBlock / kWave; ++w) M = fmaxf(M, s_red[w]);
-  const float wt = (tid < n_split && M != -INFINITY) ? exp2f(lse - M) : 0.0f;
+  const float wt = (tid < n_split && M != -INFINITY) ? __builtin_amdgcn_exp2f(lse - M) : 0.0f;
   s_w[tid] = wt;
   __syncthreads();
 
-  const float* po = part_o + bh * split_stride * kHeadDim + 2 * lane;
   float2 acc = make_float2(0.f, 0.f);
   float den = 0.f;
-#pragma unroll 4
-  for (int s = wave; s < n_split; s += kMergeBlock / kWave) {
-    const float2 v = *reinterpret_cast<const float2*>(po + (int64_t)s * kHeadDim);
-    const float w = s_w[s];
-    acc.x += w * v.x;
-    acc.y += w * v.y;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int s = wave + i * (kMergeBlock / kWave);
+    const float w = (s < n_split) ? s_w[s] : 0.f;
+    acc.x += w * v[i].x;
+    acc.y += w * v[i].y;
   }
   for (int s = lane; s < n_split; s += kWave) den += s_w[s];
 #pragma unroll
@@ -405,10 +404,10 @@ hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t
   }
 }
 
-hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, uint16_t* out,
-                               hipStream_t stream) {
+hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, int32_t n_split,
+                               uint16_t* out, hipStream_t stream) {
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0, stream,
-                     ws.header, ws.part_o, ws.part_lse, ws.split_stride, out);
+                     ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, out);
   return hipGetLastError();
 }
 

@@ -184,7 +184,7 @@ fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_sp
   fp8kv_status st = current_device(nullptr);
   if (st != FP8KV_OK) return st;
   return from_hip(fp8kv::launch_decode_merge(
-      batch, n_q_heads, workspace_view(const_cast<void*>(workspace), batch, n_q_heads, max_splits), out,
+      batch, n_q_heads, workspace_view(const_cast<void*>(workspace), batch, n_q_heads, max_splits), -1, out,
       static_cast<hipStream_t>(stream)));
 }
 
@@ -207,7 +207,7 @@ fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, 
   hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
                                              max_seq_len, sm_scale, geo, ws, s);
   if (e != hipSuccess) return FP8KV_ERR_HIP;
-  return from_hip(fp8kv::launch_decode_merge(batch, n_q_heads, ws, out, s));
+  return from_hip(fp8kv::launch_decode_merge(batch, n_q_heads, ws, geo.n_split, out, s));
 }
 
 fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q, const uint16_t* k_cur,

@@ -60,8 +60,9 @@ hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t
                                 int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
                                 hipStream_t stream);
 
-hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, uint16_t* out,
-                               hipStream_t stream);
+// n_split < 0: take the split count the preceding stage 1 wrote into the header.
+hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, int32_t n_split,
+                               uint16_t* out, hipStream_t stream);
 
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* ws_k, const uint16_t* ws_v,
                                     const uint16_t* k_cur, const uint16_t* v_cur, int32_t n_prefix,

@@ -141,8 +141,12 @@ size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t ma
  * split count.
  *
  * q:            device bf16 [batch][n_q_heads][128], contiguous, 16-byte aligned.
- * row_table:    device int32, row b at row_table + b * table_stride; entries
- *               [0, seq_lens[b]) are physical rows of `pool`.
+ * row_table:    device int32, row b at row_table + b * table_stride.  Every
+ *               entry in [0, max_seq_len) must be a physical row of `pool`
+ *               holding finite codes and scales (written by
+ *               fp8kv_quantize_rows, or zero-filled): entries at or past
+ *               seq_lens[b] (padding) are read and then masked out (weight 0),
+ *               so they may name any such row, e.g. row 0.
  * seq_lens:     device int32 [batch], each in [0, max_seq_len].
  * max_seq_len:  host-side upper bound on seq_lens (sizes the launch), >= 0,
  *               <= table_stride.
