@@ -302,74 +302,86 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   }
 }
 
-// Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), over the
-// n_split partials that stage 1 recorded in the workspace header.  One
-// workgroup per (request, query head): the split weights are formed once in
-// LDS, then four waves each sum a quarter of the splits (two d per lane).
+// Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) over the
+// splits of (b, h).  One workgroup per (request, query head); wave w takes
+// splits w, w+4, ...: it loads their lse and o vectors together (clamped
+// indices, no branches), keeps its own maximum, and the four waves combine
+// through LDS -- a single memory round trip.
 constexpr int kMergeBlock = 256;
-static_assert(FP8KV_MAX_SPLITS_INTERNAL <= kMergeBlock, "one merge thread per split");
+constexpr int kMergeWaves = kMergeBlock / kWave;
+constexpr int kMergeBatch = 16;  // splits per wave loaded at once
+static_assert(FP8KV_MAX_SPLITS_INTERNAL <= kMergeWaves * kMergeBatch * 4, "merge passes stay few");
 
 __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t* __restrict__ header,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_lse,
                                                                   int32_t split_stride, int32_t n_split_arg,
                                                                   uint16_t* __restrict__ out) {
-  __shared__ float s_w[kMergeBlock];
-  __shared__ float s_red[kMergeBlock / kWave];
-  __shared__ float2 s_acc[kMergeBlock / kWave][kWave];
+  __shared__ float s_m[kMergeWaves];
+  __shared__ float s_den[kMergeWaves];
+  __shared__ float2 s_acc[kMergeWaves][kWave];
   const int64_t bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
   const int n_split = n_split_arg >= 0 ? n_split_arg : header[0];
-
-  // Issue every partial load of this workgroup before any reduction: the
-  // split vectors do not depend on the weights.
-  constexpr int kPerWave = FP8KV_MAX_SPLITS_INTERNAL / (kMergeBlock / kWave);
+  const float* lse_p = part_lse + bh * split_stride;
   const float* po = part_o + bh * split_stride * kHeadDim + 2 * lane;
-  float2 v[kPerWave];
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int s = wave + i * (kMergeBlock / kWave);
-    v[i] = (s < n_split) ? *reinterpret_cast<const float2*>(po + (int64_t)s * kHeadDim) : make_float2(0.f, 0.f);
-  }
-  const float lse = (tid < n_split) ? part_lse[bh * split_stride + tid] : -INFINITY;
-  float m = lse;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  float M = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeBlock / kWave; ++w) M = fmaxf(M, s_red[w]);
-  const float wt = (tid < n_split && M != -INFINITY) ? __builtin_amdgcn_exp2f(lse - M) : 0.0f;
-  s_w[tid] = wt;
-  __syncthreads();
 
+  float m_w = -INFINITY, den = 0.f;
   float2 acc = make_float2(0.f, 0.f);
-  float den = 0.f;
+  for (int base = 0; base < n_split; base += kMergeWaves * kMergeBatch) {
+    float lr[kMergeBatch];
+    float2 v[kMergeBatch];
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int s = wave + i * (kMergeBlock / kWave);
-    const float w = (s < n_split) ? s_w[s] : 0.f;
-    acc.x += w * v[i].x;
-    acc.y += w * v[i].y;
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int sidx = min(base + wave + kMergeWaves * i, n_split - 1);
+      lr[i] = lse_p[sidx];
+      v[i] = *reinterpret_cast<const float2*>(po + (int64_t)sidx * kHeadDim);
+    }
+    float mx = m_w;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      lr[i] = (base + wave + kMergeWaves * i < n_split) ? lr[i] : -INFINITY;
+      mx = fmaxf(mx, lr[i]);
+    }
+    if (mx != -INFINITY) {
+      const float a = __builtin_amdgcn_exp2f(m_w - mx);  // 0 when m_w is -inf
+      acc.x *= a;
+      acc.y *= a;
+      den *= a;
+      m_w = mx;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const float w = __builtin_amdgcn_exp2f(lr[i] - m_w);
+        acc.x += w * v[i].x;
+        acc.y += w * v[i].y;
+        den += w;
+      }
+    }
   }
-  for (int s = lane; s < n_split; s += kWave) den += s_w[s];
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  if (lane == 0) {
+    s_m[wave] = m_w;
+    s_den[wave] = den;
+  }
   s_acc[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
-    float2 t = s_acc[0][lane];
+    float M = s_m[0];
 #pragma unroll
-    for (int w = 1; w < kMergeBlock / kWave; ++w) {
-      t.x += s_acc[w][lane].x;
-      t.y += s_acc[w][lane].y;
+    for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_m[w]);
+    float2 t = make_float2(0.f, 0.f);
+    float d = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kMergeWaves; ++w) {
+        const float a = __builtin_amdgcn_exp2f(s_m[w] - M);
+        t.x += a * s_acc[w][lane].x;
+        t.y += a * s_acc[w][lane].y;
+        d += a * s_den[w];
+      }
     }
-    const float inv = (den > 0.f) ? 1.0f / den : 0.0f;
-    const uint32_t packed = f32x2_to_bf16x2(t.x * inv, t.y * inv);
-    *reinterpret_cast<uint32_t*>(out + bh * kHeadDim + 2 * lane) = packed;
+    const float inv = (d > 0.f) ? 1.0f / d : 0.0f;
+    *reinterpret_cast<uint32_t*>(out + bh * kHeadDim + 2 * lane) = f32x2_to_bf16x2(t.x * inv, t.y * inv);
   }
 }
 
