@@ -8,12 +8,15 @@
 //
 // gfx950 design (not the pages' RDNA4 kernel):
 //  * A workgroup (8 waves) covers one split of one (request, KV head); a wave
-//    stages two 32-key steps at a time.  Row indices come from the table,
-//    read speculatively up to the host-side length bound so the read does not
-//    wait for seq_lens.  Codes are fetched as whole 128-byte head rows (8 lanes
-//    x 16 B per row, 8 rows per load), every load of the group in flight before
-//    the first wait, and staged in LDS (K with an XOR chunk swizzle, V rows
-//    padded to 160 B) so the MFMA operands are conflict-light LDS reads.
+//    takes two 32-key steps at a time.  The request length is read with a
+//    vector load next to the first (speculative, host-bounded) table read, so
+//    it costs no extra round trip, and no code byte past the length's 64-key
+//    group is fetched.
+//  * Every lane loads exactly the code bytes its MFMA operands need, straight
+//    into registers: for keys on the MFMA rows, 16-byte K chunks; for the P*V
+//    contraction, 8 bytes of V per key, 16 lanes covering one whole 128-byte V
+//    row.  All loads of both steps are in flight before the first wait; only
+//    row indices and scales pass through LDS.
 //  * QK^T runs on the bf16 MFMA 16x16x32 with E4M3 codes widened exactly to
 //    bf16.  S^T = K * Q^T puts keys on the MFMA rows and the G query heads of
 //    the group on the columns, so each lane holds 8 keys of one head: the
@@ -37,22 +40,14 @@ namespace fp8kv {
 namespace {
 
 constexpr int kBlock = kDecodeWaves * kWave;
-constexpr int kTileBytes = kDecodeTileKeys * kHeadDim;              // one 32-key step of K codes
-constexpr int kVRowBytes = kHeadDim + 32;                           // V rows padded to 160 B in LDS
-constexpr int kVTileBytes = kDecodeTileKeys * kVRowBytes;
-constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave stages at once
+constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave loads at once
 static_assert(kGroupKeys % kWave == 0, "a group covers whole waves of row indices");
-static_assert(kDecodeTilesPerWave >= 1 && kDecodeTilesPerWave <= 4, "up to four staged steps per wave");
+static_assert(kDecodeTilesPerWave >= 1 && kDecodeTilesPerWave <= 4, "up to four steps in flight per wave");
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 // Key order inside a 32-key step: k-group j of the P*V contraction holds keys
 // 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
 __device__ __forceinline__ int step_key(int j, int r) { return (r < 4) ? 4 * j + r : 12 + 4 * j + r; }
-
-// K rows sit in LDS as [32 keys][8 chunks of 16 B] with chunk c of key m at
-// position c ^ (m & 7): the 16 lanes that read one chunk of 16 keys for the
-// MFMA operand then touch 16 different 16-byte bank groups.
-__device__ __forceinline__ int kswz(int key, int chunk) { return key * kHeadDim + ((chunk ^ (key & 7)) << 4); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -65,7 +60,6 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
     int32_t* __restrict__ header, float* __restrict__ part_o, float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
-  static_assert(G * kHeadDim * 4 <= kDecodeTilesPerWave * (kTileBytes + kVTileBytes), "merge buffer reuses the tiles");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n = lane & 15;
@@ -73,37 +67,54 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = seq_lens[b];  // its load overlaps the first (speculative) table reads
   const int key_begin = split * chunk;
   const int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
-  const int key_end = min(key_begin + chunk, L);
   const int h0 = g * G;
   if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 
-  // LDS: per wave kDecodeTilesPerWave steps of K and V codes, their row
-  // indices and (k, v) scales.
-  __shared__ __attribute__((aligned(16))) uint8_t s_kt[kDecodeWaves][kDecodeTilesPerWave][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kDecodeWaves][kDecodeTilesPerWave][kVTileBytes];
+  // The request length as a vector load, issued first: a scalar load would
+  // share its wait with the kernel-argument loads and delay the table read.
+  int b_lane = b;
+  asm volatile("" : "+v"(b_lane));
+  const int len_lane = seq_lens[b_lane];
+
   __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kGroupKeys];
   __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kGroupKeys];
+  __shared__ __attribute__((aligned(16))) float sm_o[kDecodeWaves][G][kHeadDim];
+  __shared__ float sm_m[kDecodeWaves][16];
+  __shared__ float sm_l[kDecodeWaves][16];
 
-  // Code addresses: row * stride (32 x 32 -> 64-bit) + this lane's 16-byte chunk.
-  const uint64_t kbase = reinterpret_cast<uint64_t>(k_codes) + (uint64_t)g * kHeadDim + 16 * (lane & 7);
-  const uint64_t vbase = reinterpret_cast<uint64_t>(v_codes) + (uint64_t)g * kHeadDim + 16 * (lane & 7);
   const int32_t* trow = table + (int64_t)b * table_stride;
+  // Row indices of the first group, read up to the host-side bound before the
+  // length is known.  Every table entry below max_seq_len names a valid row
+  // (padding included), so reading past the request's length is harmless.
+  // They go to LDS before the length is used, which keeps the compiler from
+  // sinking the read below the length's wait.
+  int k0 = key_begin + wave * kGroupKeys;
+  int rows_in[kGroupKeys / kWave];
+#pragma unroll
+  for (int c = 0; c < kGroupKeys / kWave; ++c) rows_in[c] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
+#pragma unroll
+  for (int c = 0; c < kGroupKeys / kWave; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
 
   // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
   // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
+  // Columns n >= G repeat head G-1: MFMA outputs never mix columns, so they
+  // only produce values that are never stored, and the loads need no branch
+  // (which would make the waits on the loads issued before them inexact).
   bf16x8 qb[4];
+  const uint16_t* qrow = q + ((int64_t)b * n_q_heads + h0 + min(n, G - 1)) * kHeadDim + 16 * j;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (n < G) {
-      const uint16_t* qp = q + ((int64_t)b * n_q_heads + h0 + n) * kHeadDim + 64 * (kk >> 1) + 16 * j + 8 * (kk & 1);
-      u = *reinterpret_cast<const uint4*>(qp);
-    }
-    qb[kk] = u4_as_bf16x8(u);
-  }
+  for (int kk = 0; kk < 4; ++kk) qb[kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * (kk >> 1) + 8 * (kk & 1)));
+
+  const int L = __builtin_amdgcn_readfirstlane(len_lane);
+  const int key_end = min(key_begin + chunk, L);
+
+  // Code addresses: row * stride (32 x 32 -> 64-bit) + the lane's bytes.  The
+  // offsets stay on the global pointers so the loads are global, not flat.
+  // K: key n of a 16-key block, 16-byte chunks j and 4+j.  V: 8 bytes at d = 8n.
+  const uint8_t* kbase = k_codes + g * kHeadDim + 16 * j;
+  const uint8_t* vbase = v_codes + g * kHeadDim + 8 * n;
 
   float m_run = -INFINITY;  // running (lazy) max, log2 units, of head n
   float l_part = 0.0f;      // sum of p for head n over this lane's keys
@@ -111,78 +122,71 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = key_begin + wave * kGroupKeys; k0 < key_bound; k0 += kDecodeWaves * kGroupKeys) {
-    // 1. Row indices of the group's keys, read up to the host-side bound.
-    //    Every table entry below max_seq_len is a valid physical row (padding
-    //    included), so neither the table read nor the code loads wait for
-    //    seq_lens; keys at or past the request's length are only masked out of
-    //    the softmax.
+  for (bool first = true; k0 < key_end; k0 += kDecodeWaves * kGroupKeys, first = false) {
+    // 1. Row indices of the group's keys through LDS (per-wave region).
+    if (!first) {
 #pragma unroll
-    for (int c = 0; c < kGroupKeys / kWave; ++c)
-      s_rows[wave][c * kWave + lane] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
+      for (int c = 0; c < kGroupKeys / kWave; ++c) {
+        rows_in[c] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
+        s_rows[wave][c * kWave + lane] = rows_in[c];
+      }
+    }
     __builtin_amdgcn_wave_barrier();
-    // The scale loads are issued here but written to LDS only after the code
-    // loads are in flight, so the two memory round trips overlap.
+
+    // 2. Scale loads, issued before the code loads: loads complete in issue
+    //    order, so writing the scales to LDS waits for them alone.
     float ksc[kGroupKeys / kWave], vsc[kGroupKeys / kWave];
 #pragma unroll
     for (int c = 0; c < kGroupKeys / kWave; ++c) {
-      const uint32_t row = (uint32_t)s_rows[wave][c * kWave + lane];
+      const uint32_t row = (uint32_t)rows_in[c];
       const uint64_t off = (uint64_t)row * scale_row_stride + g;
       ksc[c] = k_scales[off];
       vsc[c] = v_scales[off];
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. Whole 128-byte head rows: 8 lanes x 16 B per row, 8 rows per load;
-    //    every load of the group is issued before the first wait.
-    u32x4 kr[kDecodeTilesPerWave][4], vr[kDecodeTilesPerWave][4];  // native vectors: stay in registers
+    // 3. Every code load of the group, in step order.
+    u32x4 kr[kDecodeTilesPerWave][4];
+    uint2 vr[kDecodeTilesPerWave][8];
 #pragma unroll
     for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+      const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
+      const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
+      const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
+      kr[t][0] = *reinterpret_cast<const u32x4*>(kbase + r0);
+      kr[t][1] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64);
+      kr[t][2] = *reinterpret_cast<const u32x4*>(kbase + r1);
+      kr[t][3] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64);
+      const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
+      const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
+      const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) {
-        const uint64_t roff = (uint64_t)(uint32_t)s_rows[wave][t * kDecodeTileKeys + sidx * 8 + (lane >> 3)] * code_row_stride;
-        kr[t][sidx] = *reinterpret_cast<const u32x4*>(kbase + roff);
-        vr[t][sidx] = *reinterpret_cast<const u32x4*>(vbase + roff);
-      }
+      for (int r = 0; r < 8; ++r)
+        vr[t][r] = *reinterpret_cast<const uint2*>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < kGroupKeys / kWave; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
+    __builtin_amdgcn_wave_barrier();
+    const bool tail = k0 + kGroupKeys > key_end;  // wave-uniform: only a request's last group
 
     // One 32-key step; t is a compile-time constant so kr/vr stay in registers.
+    // Steps are not skipped (no branch the loads could sink into); keys at or
+    // past the length are masked out of the softmax.
     auto step = [&](auto tc) {
       constexpr int t = decltype(tc)::value;
       const int t0 = k0 + t * kDecodeTileKeys;
-      if (t0 >= key_end) return;  // wave-uniform (waits for seq_lens only here)
-      uint8_t* s_k = s_kt[wave][t];
-      uint8_t* s_v = s_vt[wave][t];
-      // Stage this step's codes (waits only for this step's loads).
-#pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) {
-        const int key = sidx * 8 + (lane >> 3);
-        *reinterpret_cast<u32x4*>(s_k + kswz(key, lane & 7)) = kr[t][sidx];
-        *reinterpret_cast<u32x4*>(s_v + key * kVRowBytes + 16 * (lane & 7)) = vr[t][sidx];
-      }
-      __builtin_amdgcn_wave_barrier();
-
-      // 3. S^T = K * Q^T: lane (n, j) takes chunks j and 4+j of keys n (block 0)
-      //    and 16+n (block 1).
+      // S^T = K * Q^T: lane (n, j) holds chunks j and 4+j of keys n (block 0)
+      // and 16+n (block 1).
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      {
-        const uint4 ka = *reinterpret_cast<const uint4*>(s_k + kswz(n, j));
-        const uint4 kb = *reinterpret_cast<const uint4*>(s_k + kswz(n, 4 + j));
-        s0 = mfma16x16x32(fp8x8_to_bf16x8(ka.x, ka.y), qb[0], s0);
-        s0 = mfma16x16x32(fp8x8_to_bf16x8(ka.z, ka.w), qb[1], s0);
-        s0 = mfma16x16x32(fp8x8_to_bf16x8(kb.x, kb.y), qb[2], s0);
-        s0 = mfma16x16x32(fp8x8_to_bf16x8(kb.z, kb.w), qb[3], s0);
-      }
-      {
-        const uint4 ka = *reinterpret_cast<const uint4*>(s_k + kswz(16 + n, j));
-        const uint4 kb = *reinterpret_cast<const uint4*>(s_k + kswz(16 + n, 4 + j));
-        s1 = mfma16x16x32(fp8x8_to_bf16x8(ka.x, ka.y), qb[0], s1);
-        s1 = mfma16x16x32(fp8x8_to_bf16x8(ka.z, ka.w), qb[1], s1);
-        s1 = mfma16x16x32(fp8x8_to_bf16x8(kb.x, kb.y), qb[2], s1);
-        s1 = mfma16x16x32(fp8x8_to_bf16x8(kb.z, kb.w), qb[3], s1);
-      }
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][0].x, kr[t][0].y), qb[0], s0);
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][0].z, kr[t][0].w), qb[1], s0);
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][1].x, kr[t][1].y), qb[2], s0);
+      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][1].z, kr[t][1].w), qb[3], s0);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][2].x, kr[t][2].y), qb[0], s1);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][2].z, kr[t][2].w), qb[1], s1);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][3].x, kr[t][3].y), qb[2], s1);
+      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][3].z, kr[t][3].w), qb[3], s1);
       const float2* scp = &s_sc[wave][t * kDecodeTileKeys];
       const float4 c01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
       const float4 c23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
                      s1[0] * c45.x, s1[1] * c45.z, s1[2] * c67.x, s1[3] * c67.z};
 #pragma unroll
       for (int r = 0; r < 8; ++r) sv[r] *= qk_scale_log2;
-      if (t0 + kDecodeTileKeys > key_end) {  // wave-uniform: only the request's last step is partial
+      if (tail) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) sv[r] = (t0 + step_key(j, r) < key_end) ? sv[r] : -INFINITY;
       }
@@ -203,9 +207,12 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
 
       // Lazy maximum: move it (and rescale O and l) only when this step's
-      // maximum exceeds it by more than the slack; otherwise p <= 2^slack.
+      // maximum exceeds it by more than the slack; otherwise p <= 2^slack.  A
+      // fully masked step has tmax = -inf and leaves the state untouched; the
+      // group's first step always holds key k0 < key_end, so m_run is finite
+      // before any fully masked step.
       if (__any(tmax > m_run + kLazyMaxSlack)) {
-        const float m_new = fmaxf(m_run, tmax);  // finite: every step has a valid key
+        const float m_new = fmaxf(m_run, tmax);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_part *= alpha;
@@ -228,18 +235,13 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
                                   f32x2_to_bf16x2(p[4] * c45.y, p[5] * c45.w), f32x2_to_bf16x2(p[6] * c67.y, p[7] * c67.w));
       const bf16x8 pa = u4_as_bf16x8(pu);
 
-      // 4. V operand for N-block nb: byte nb of each key's 8-byte segment, i.e.
+      // 4. V operand for N-block nb: byte nb of each key's 8 bytes, i.e.
       //    V[key][d = 8n + nb] for the lane's 8 keys (byte-transposed in registers).
       uint32_t lo[8], hi[8];
-      {
-        uint2 vv[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) vv[r] = *reinterpret_cast<const uint2*>(s_v + step_key(j, r) * kVRowBytes + 8 * n);
-        transpose4x4_bytes(vv[0].x, vv[1].x, vv[2].x, vv[3].x, lo[0], lo[1], lo[2], lo[3]);
-        transpose4x4_bytes(vv[4].x, vv[5].x, vv[6].x, vv[7].x, hi[0], hi[1], hi[2], hi[3]);
-        transpose4x4_bytes(vv[0].y, vv[1].y, vv[2].y, vv[3].y, lo[4], lo[5], lo[6], lo[7]);
-        transpose4x4_bytes(vv[4].y, vv[5].y, vv[6].y, vv[7].y, hi[4], hi[5], hi[6], hi[7]);
-      }
+      transpose4x4_bytes(vr[t][0].x, vr[t][1].x, vr[t][2].x, vr[t][3].x, lo[0], lo[1], lo[2], lo[3]);
+      transpose4x4_bytes(vr[t][4].x, vr[t][5].x, vr[t][6].x, vr[t][7].x, hi[0], hi[1], hi[2], hi[3]);
+      transpose4x4_bytes(vr[t][0].y, vr[t][1].y, vr[t][2].y, vr[t][3].y, lo[4], lo[5], lo[6], lo[7]);
+      transpose4x4_bytes(vr[t][4].y, vr[t][5].y, vr[t][6].y, vr[t][7].y, hi[4], hi[5], hi[6], hi[7]);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
     };
@@ -254,10 +256,6 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   float l_tot = l_part + __shfl_xor(l_part, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
-  __shared__ float sm_m[kDecodeWaves][16];
-  __shared__ float sm_l[kDecodeWaves][16];
-  __syncthreads();  // every wave is done with its tiles; reuse them for the merge
-  float* sm_o = reinterpret_cast<float*>(&s_kt[0][0][0]);  // [wave][G][128]
   if (j == 0) {
     sm_m[wave][n] = m_run;
     sm_l[wave][n] = l_tot;
@@ -266,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   for (int i = 0; i < 4; ++i) {
     const int head = 4 * j + i;
     if (head < G) {
-      float* dst = sm_o + (wave * G + head) * kHeadDim + 8 * n;
+      float* dst = &sm_o[wave][head][8 * n];
       *reinterpret_cast<float4*>(dst) = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
       *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
     }
@@ -287,7 +285,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
         const float wt = fast_exp2(sm_m[w][h] - M);
-        const float4 v = *reinterpret_cast<const float4*>(sm_o + (w * G + h) * kHeadDim + d);
+        const float4 v = *reinterpret_cast<const float4*>(&sm_o[w][h][d]);
         num.x += wt * v.x;
         num.y += wt * v.y;
         num.z += wt * v.z;
