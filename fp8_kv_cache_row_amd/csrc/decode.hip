@@ -44,6 +44,7 @@ constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wav
 static_assert(kGroupKeys % kWave == 0, "a group covers whole waves of row indices");
 static_assert(kDecodeTilesPerWave >= 1 && kDecodeTilesPerWave <= 4, "up to four steps in flight per wave");
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Key order inside a 32-key step: k-group j of the P*V contraction holds keys
 // 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     uint32_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
     int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
-    int32_t* __restrict__ header, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int32_t key_trim, int32_t* __restrict__ header, float* __restrict__ part_o, float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qb[kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * (kk >> 1) + 8 * (kk & 1)));
 
-  const int L = __builtin_amdgcn_readfirstlane(len_lane);
+  const int L = __builtin_amdgcn_readfirstlane(len_lane) - key_trim;  // keys this stage covers
   const int key_end = min(key_begin + chunk, L);
 
   // Code addresses: row * stride (32 x 32 -> 64-bit) + the lane's bytes.  The
@@ -305,15 +306,42 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 // splits w, w+4, ...: it loads their lse and o vectors together (clamped
 // indices, no branches), keeps its own maximum, and the four waves combine
 // through LDS -- a single memory round trip.
+//
+// With APPEND, wave 0 also takes the request's new token (position
+// seq_lens[b] - 1, left out of stage 1): it quantizes the bf16 K and V rows of
+// the head group exactly as the quantize-on-write kernel does (same codec
+// functions), scores q against the decoded codes, and folds the token in as a
+// single-key partial (o = s_v * decode(v), lse = the score).  The workgroup of
+// the group's first query head writes the codes and scales to the token's row.
 constexpr int kMergeBlock = 256;
 constexpr int kMergeWaves = kMergeBlock / kWave;
 constexpr int kMergeBatch = 16;  // splits per wave loaded at once
 static_assert(FP8KV_MAX_SPLITS_INTERNAL <= kMergeWaves * kMergeBatch * 4, "merge passes stay few");
 
+struct AppendKernelArgs {
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_token_stride;
+  const int32_t* table;
+  int64_t table_stride;
+  const int32_t* seq_lens;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_scales;
+  float* v_scales;
+  int64_t code_row_stride;
+  int64_t scale_row_stride;
+  int32_t n_kv_heads;
+  float qk_scale_log2;
+};
+
+template <bool APPEND>
 __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t* __restrict__ header,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_lse,
                                                                   int32_t split_stride, int32_t n_split_arg,
+                                                                  int32_t n_q_heads, AppendKernelArgs app,
                                                                   uint16_t* __restrict__ out) {
   __shared__ float s_m[kMergeWaves];
   __shared__ float s_den[kMergeWaves];
@@ -324,6 +352,22 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   const int n_split = n_split_arg >= 0 ? n_split_arg : header[0];
   const float* lse_p = part_lse + bh * split_stride;
   const float* po = part_o + bh * split_stride * kHeadDim + 2 * lane;
+
+  // The new token's inputs: its bf16 K/V pair at d = 2*lane, 2*lane + 1, and q.
+  uint32_t k2 = 0u, v2 = 0u, q2 = 0u;
+  int len = 0;
+  int64_t b = 0, g = 0;
+  if constexpr (APPEND) {
+    b = bh / n_q_heads;
+    const int h = (int)(bh % n_q_heads);
+    g = h / (n_q_heads / app.n_kv_heads);
+    if (wave == 0) {
+      len = app.seq_lens[b];
+      k2 = *reinterpret_cast<const uint32_t*>(app.k_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
+      v2 = *reinterpret_cast<const uint32_t*>(app.v_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
+      q2 = *reinterpret_cast<const uint32_t*>(app.q + bh * kHeadDim + 2 * lane);
+    }
+  }
 
   float m_w = -INFINITY, den = 0.f;
   float2 acc = make_float2(0.f, 0.f);
@@ -357,6 +401,53 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
       }
     }
   }
+
+  if constexpr (APPEND) {
+    if (wave == 0) {
+      // Quantize the K and V rows (128 values over the wave, two per lane).
+      const float kx0 = bf16lo_to_f32(k2), kx1 = bf16hi_to_f32(k2);
+      const float vx0 = bf16lo_to_f32(v2), vx1 = bf16hi_to_f32(v2);
+      float ka = fmaxf(fabsf(kx0), fabsf(kx1)), va = fmaxf(fabsf(vx0), fabsf(vx1));
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        ka = fmaxf(ka, __shfl_xor(ka, off));
+        va = fmaxf(va, __shfl_xor(va, off));
+      }
+      const float sk = e4m3_row_scale(ka), sv = e4m3_row_scale(va);
+      const uint32_t kc = f32x2_to_fp8x2<false>(e4m3_prescaled(kx0, ka, sk), e4m3_prescaled(kx1, ka, sk), 0u);
+      const uint32_t vc = f32x2_to_fp8x2<false>(e4m3_prescaled(vx0, va, sv), e4m3_prescaled(vx1, va, sv), 0u);
+      // Score and value from the decoded codes, as stage 1 sees every other row.
+      float kd[4], vd[4];
+      fp8x4_to_f32x4(kc, kd);
+      fp8x4_to_f32x4(vc, vd);
+      float dot = bf16lo_to_f32(q2) * kd[0] + bf16hi_to_f32(q2) * kd[1];
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+      const float lse_new = dot * sk * app.qk_scale_log2;
+      const float2 o_new = make_float2(vd[0] * sv, vd[1] * sv);
+      const float mx = fmaxf(m_w, lse_new);
+      const float a = __builtin_amdgcn_exp2f(m_w - mx);
+      const float w = __builtin_amdgcn_exp2f(lse_new - mx);
+      acc.x = acc.x * a + w * o_new.x;
+      acc.y = acc.y * a + w * o_new.y;
+      den = den * a + w;
+      m_w = mx;
+      // One workgroup per (request, KV head) stores the row.
+      if ((bh % n_q_heads) % (n_q_heads / app.n_kv_heads) == 0) {
+        // The position is clamped into the table row so that a length outside
+        // [1, table_stride] cannot address memory outside it.
+        const int64_t pos = min(max((int64_t)len - 1, (int64_t)0), app.table_stride - 1);
+        const int64_t slot = app.table[b * app.table_stride + pos];
+        *reinterpret_cast<uint16_t*>(app.k_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)kc;
+        *reinterpret_cast<uint16_t*>(app.v_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)vc;
+        if (lane == 0) {
+          app.k_scales[slot * app.scale_row_stride + g] = sk;
+          app.v_scales[slot * app.scale_row_stride + g] = sv;
+        }
+      }
+    }
+  }
+
   if (lane == 0) {
     s_m[wave] = m_w;
     s_den[wave] = den;
@@ -387,13 +478,13 @@ template <int G>
 hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                            const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
                            int32_t max_seq_len, float qk_scale_log2, const DecodeGeometry& geo, const DecodeWorkspace& ws,
-                           hipStream_t stream) {
+                           int32_t key_trim, hipStream_t stream) {
   dim3 grid((unsigned)geo.n_split, (unsigned)pool.n_kv_heads, (unsigned)batch);
   hipLaunchKernelGGL(decode_stage1_kernel<G>, grid, dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
                      pool.k_scales, pool.v_scales, (uint32_t)pool.code_row_stride, (uint32_t)pool.scale_row_stride,
                      q, n_q_heads,
                      row_table, table_stride, seq_lens, max_seq_len, geo.n_split, geo.chunk, ws.split_stride,
-                     qk_scale_log2, ws.header, ws.part_o, ws.part_lse);
+                     qk_scale_log2, key_trim, ws.header, ws.part_o, ws.part_lse);
   return hipGetLastError();
 }
 
@@ -402,22 +493,33 @@ hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batc
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                                 const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
                                 int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
-                                hipStream_t stream) {
-  const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
+                                int32_t key_trim, hipStream_t stream) {
+  const float qk_scale_log2 = sm_scale * kLog2e;
   switch (n_q_heads / pool.n_kv_heads) {
-    case 1: return launch_stage1_g<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
-    case 2: return launch_stage1_g<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
-    case 4: return launch_stage1_g<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
-    case 8: return launch_stage1_g<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
-    case 16: return launch_stage1_g<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, stream);
+    case 1: return launch_stage1_g<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
+    case 2: return launch_stage1_g<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
+    case 4: return launch_stage1_g<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
+    case 8: return launch_stage1_g<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
+    case 16: return launch_stage1_g<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, int32_t n_split,
                                uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0, stream,
-                     ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, out);
+  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0,
+                     stream, ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, AppendKernelArgs{},
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,
+                                      int32_t n_split, const AppendArgs& app, uint16_t* out, hipStream_t stream) {
+  const AppendKernelArgs a{app.q, app.k_new, app.v_new, app.new_token_stride, app.row_table, app.table_stride,
+                           app.seq_lens, pool.k_codes, pool.v_codes, pool.k_scales, pool.v_scales,
+                           pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads, app.sm_scale * kLog2e};
+  hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0,
+                     stream, ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
   return hipGetLastError();
 }
 

@@ -60,6 +60,18 @@ __device__ __forceinline__ uint32_t f32x2_to_fp8x2(float a, float b, uint32_t ol
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
+// Quantize-on-write of one element of a row whose absolute maximum is amax:
+// s = fl32(amax / 448) (an IEEE division: the library is built with correctly
+// rounded fp32 division), then fl32(x / s) clamped to the E4M3FN range; the
+// hardware convert (f32x2_to_fp8x2) rounds that to nearest even.  An all-zero
+// row keeps s = 0 and passes x through, so its codes are signed zeros.  Every
+// writer of codes goes through these two functions.
+__device__ __forceinline__ float e4m3_row_scale(float amax) { return amax / 448.0f; }
+__device__ __forceinline__ float e4m3_prescaled(float x, float amax, float s) {
+  const float q = (amax == 0.0f) ? x : x / s;
+  return fminf(fmaxf(q, -448.0f), 448.0f);
+}
+
 // Four E4M3FN codes in one dword -> four f32.
 __device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float* o) {
   f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);

@@ -55,14 +55,32 @@ struct DecodeWorkspace {
 };
 constexpr size_t kDecodeHeaderBytes = 256;
 
+// key_trim = 1 leaves each request's last key (position seq_lens[b] - 1) to
+// the appending merge below.
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                                 const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
                                 int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
-                                hipStream_t stream);
+                                int32_t key_trim, hipStream_t stream);
 
 // n_split < 0: take the split count the preceding stage 1 wrote into the header.
 hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, int32_t n_split,
                                uint16_t* out, hipStream_t stream);
+
+// The new token of each request: bf16 K/V rows [B][token_stride] (head g at
+// g * 128), quantized into pool row row_table[b][seq_lens[b] - 1] and folded
+// into the merge as one more single-key partial.
+struct AppendArgs {
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_token_stride;  // elements
+  const int32_t* row_table;
+  int64_t table_stride;
+  const int32_t* seq_lens;
+  float sm_scale;
+};
+hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,
+                                      int32_t n_split, const AppendArgs& app, uint16_t* out, hipStream_t stream);
 
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* ws_k, const uint16_t* ws_v,
                                     const uint16_t* k_cur, const uint16_t* v_cur, int32_t n_prefix,

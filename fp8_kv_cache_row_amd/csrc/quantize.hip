@@ -44,17 +44,10 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kLanesPerRow));
 
-  // s = amax / 448 with an IEEE division (the library is built with correctly
-  // rounded fp32 division); each element is divided by s, again exactly
-  // rounded, clamped to the E4M3FN range and rounded to nearest even by the
-  // hardware convert.  An all-zero row keeps s = 0 and signed-zero codes.
-  const float s = amax / 448.0f;
+  const float s = e4m3_row_scale(amax);
   float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q = (amax == 0.0f) ? x[i] : x[i] / s;
-    y[i] = fminf(fmaxf(q, -448.0f), 448.0f);
-  }
+  for (int i = 0; i < 8; ++i) y[i] = e4m3_prescaled(x[i], amax, s);
   uint32_t lo = f32x2_to_fp8x2<false>(y[0], y[1], 0u);
   lo = f32x2_to_fp8x2<true>(y[2], y[3], lo);
   uint32_t hi = f32x2_to_fp8x2<false>(y[4], y[5], 0u);

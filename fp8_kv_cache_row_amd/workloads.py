@@ -179,8 +179,12 @@ def model_step_layer(layer: int, table: np.ndarray, seed: int = 0, pool_rows: in
 
 
 def batched_decode(seed: int = 0, n_req: int = 16, lo: int = 1024, hi: int = 32768,
-                   n_q_heads: int = 16, n_kv_heads: int = 4) -> DecodeCase:
-    """16 requests with seeded lengths in [1024, 32768], GQA 4, shared scattered pool."""
+                   n_q_heads: int = 16, n_kv_heads: int = 4, with_new_token: bool = False) -> DecodeCase:
+    """16 requests with seeded lengths in [1024, 32768], GQA 4, shared scattered pool.
+
+    With new tokens, request b's token goes to table[b][lens[b]-1]; they are
+    drawn after everything else, so the other arrays do not depend on it.
+    """
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, n_req, endpoint=True).astype(np.int64)
     pool_rows = int(lens.sum())
@@ -194,9 +198,13 @@ def batched_decode(seed: int = 0, n_req: int = 16, lo: int = 1024, hi: int = 327
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
     for b in range(n_req):
         table[b, :lens[b]] = perm[starts[b]:starts[b] + lens[b]]
+    nk = nv = None
+    if with_new_token:
+        nk = bf16_bits(draw_k(rng, n_req, n_kv_heads, out))
+        nv = bf16_bits(draw_normal(rng, (n_req, n_kv_heads, HEAD_DIM), 0.5))
     return DecodeCase("batched_gqa4_16req", n_q_heads, n_kv_heads, pool_rows,
                       bf16_bits(k), bf16_bits(v), bf16_bits(q), table,
-                      lens.astype(np.int32), softmax_scale())
+                      lens.astype(np.int32), softmax_scale(), nk, nv)
 
 
 def chunked_prefill(seed: int = 0, n_prefix: int = 8192, n_chunk: int = 8192,

@@ -186,6 +186,40 @@ fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_sp
                                 void *stream);
 
 /*
+ * fp8kv_decode_attn_append -- one decode step with the new token's
+ * quantize-on-write folded in (FreeToken PR #853 "Follow-up model/workload
+ * search": on the FP8 path every new K/V row is quantized as it is written;
+ * PR #897 description: the decode reader then attends over the pool).
+ *
+ * For each request b the new token sits at position p_b = seq_lens[b] - 1 of
+ * its row table.  The call has the effect of
+ *   fp8kv_quantize_rows(pool, k_new, v_new, new_token_stride,
+ *                       slots = {row_table[b * table_stride + p_b]}, batch)
+ * followed by fp8kv_decode_attn with the same arguments: the token's codes and
+ * scales land in its row bit for bit as fp8kv_quantize_rows would write them,
+ * and `out` is attention over positions [0, seq_lens[b]) including the token.
+ * The token's row is never read back: stage 1 covers [0, p_b) and the merge
+ * quantizes the token itself and adds it as a single-key partial, which saves
+ * a launch per step.
+ *
+ * k_new, v_new:      device bf16, token b at k_new + b * new_token_stride,
+ *                    [n_kv_heads][128] each; 16-byte aligned, stride a
+ *                    multiple of 8 elements and >= n_kv_heads * 128.
+ * seq_lens:          device int32 [batch], each in [1, max_seq_len].
+ * row_table:         as for fp8kv_decode_attn; in addition the new tokens'
+ *                    rows must differ between requests and no position below
+ *                    p_b of any request may name one of them.
+ * Other arguments, the workspace and the errors are those of
+ * fp8kv_decode_attn; max_seq_len must be >= 1.
+ */
+fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                                      int32_t n_q_heads, const uint16_t *k_new, const uint16_t *v_new,
+                                      int64_t new_token_stride, const int32_t *row_table,
+                                      int64_t table_stride, const int32_t *seq_lens, int32_t max_seq_len,
+                                      float sm_scale, int32_t max_splits, void *workspace,
+                                      size_t workspace_bytes, uint16_t *out, void *stream);
+
+/*
  * fp8kv_prefill_attn -- attention of one prefill chunk over historical FP8 rows
  * (FreeToken PR #853, "What changes": the prefill path reconstructs historical
  * FP8 rows once per layer into one shared BF16 workspace; current-chunk K/V

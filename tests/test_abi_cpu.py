@@ -20,7 +20,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = B.declared_symbols()
     assert set(names) >= {"fp8kv_quantize_rows", "fp8kv_decode_attn", "fp8kv_prefill_attn",
-                          "fp8kv_decode_stage1", "fp8kv_decode_merge",
+                          "fp8kv_decode_attn_append", "fp8kv_decode_stage1", "fp8kv_decode_merge",
                           "fp8kv_decode_workspace_bytes", "fp8kv_status_string"}
     for n in names:
         assert hasattr(lib, n), n
@@ -112,6 +112,27 @@ def test_decode_stage_validation(lib):
     assert m(out=A + 2) == ALIGN
 
 
+def _append(lib, p, **kw):
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
+    return lib.fp8kv_decode_attn_append(ctypes.byref(p), kw.get("q", A), 1, kw.get("hq", 32), kw.get("kn", A),
+                                        kw.get("vn", 2 * A), kw.get("nstride", 512), A, 1024, A,
+                                        kw.get("maxlen", 1000), 0.088, 0, A, kw.get("wsb", wsb), kw.get("out", A),
+                                        None)
+
+
+def test_decode_append_validation(lib):
+    p = _pool()
+    assert _append(lib, p, kn=0) == INVALID
+    assert _append(lib, p, vn=0) == INVALID
+    assert _append(lib, p, out=0) == INVALID
+    assert _append(lib, p, maxlen=0) == INVALID                      # the new token needs a position
+    assert _append(lib, p, nstride=256) == INVALID                   # shorter than Hkv * 128
+    assert _append(lib, p, nstride=516) == ALIGN
+    assert _append(lib, p, kn=A + 8) == ALIGN
+    assert _append(lib, p, hq=12) == UNSUPPORTED
+    assert _append(lib, p, wsb=10) == WORKSPACE
+
+
 def test_decode_workspace_bytes(lib):
     f = lib.fp8kv_decode_workspace_bytes
     assert f(1, 32, 64) == 256 + 1 * 32 * 64 * 129 * 4
@@ -146,3 +167,4 @@ def test_valid_arguments_reach_the_device_check(lib):
     wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
     assert lib.fp8kv_decode_stage1(ctypes.byref(_pool()), A, 1, 32, A, 1024, A, 1000, 0.088, 0, A, wsb, None) == HIP
     assert lib.fp8kv_decode_merge(1, 32, 0, A, wsb, A, None) == HIP
+    assert _append(lib, _pool()) == HIP

@@ -1,0 +1,162 @@
+"""GPU parity: the decode step with the new token's quantize-on-write folded in
+(fp8kv_decode_attn_append).
+
+The call must leave the pool exactly as fp8kv_quantize_rows of the new tokens
+would (codes and scales bit for bit, every other row untouched) and return
+attention over all positions including the new token, within the attention
+tolerance of the fp64 oracle run on the oracle-quantized pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_kv_cache_row_amd as fk
+from fp8_kv_cache_row_amd import workloads as wl
+
+from gpu_common import (assert_bits_equal, assert_close, bf16_to_f64, build_pool, oracle_pool, pool_arrays, say,
+                        to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_step(case, seq_lens=None):
+    """Oracle pool with each request's new token quantized into its row, and
+    the fp64 attention over it."""
+    lens = case.seq_lens if seq_lens is None else seq_lens
+    kc, vc, ks, vs = oracle_pool(case)
+    nkc, nks = oracle.quantize_rows(case.new_k)
+    nvc, nvs = oracle.quantize_rows(case.new_v)
+    for b in range(case.batch):
+        row = int(case.table[b, lens[b] - 1])
+        kc[row], vc[row], ks[row], vs[row] = nkc[b], nvc[b], nks[b], nvs[b]
+    out = oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, lens, case.sm_scale, case.n_kv_heads)
+    return (kc, vc, ks, vs), out
+
+
+def _run_append(pool, case, seq_lens=None, max_seq_len=None, max_splits=0):
+    lens = case.seq_lens if seq_lens is None else seq_lens
+    msl = int(lens.max()) if max_seq_len is None else max_seq_len
+    out = fk.fp8kv_decode_attn_append(pool, to_dev_bf16(case.q), to_dev_bf16(case.new_k), to_dev_bf16(case.new_v),
+                                      to_dev(case.table), to_dev(np.asarray(lens, np.int32)), msl, case.sm_scale,
+                                      max_splits=max_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_pool(pool, ref_pools, what):
+    got = pool_arrays(pool)
+    for name, a, b in zip(("K codes", "V codes", "K scales", "V scales"), got, ref_pools):
+        assert_bits_equal(a, b, f"{what}: {name}")
+
+
+@pytest.mark.parametrize("layout", ["separate", "interleaved"])
+def test_append_32k_layer(layout):
+    say(f"decode+append 32K, 32 q / 4 KV heads, layout={layout}")
+    case = wl.layer_decode(0)
+    pool = build_pool(case, layout)
+    ref_pools, ref = _oracle_step(case)
+    out = bf16_to_f64(_run_append(pool, case))
+    _check_pool(pool, ref_pools, "32K")
+    assert_close(out, ref, "32K append")
+
+
+def test_append_agrees_with_quantize_then_decode():
+    say("decode+append == quantize_rows then decode_attn (pool bit-exact, outputs within rounding)")
+    case = wl.layer_decode(3, ctx=6000, pool_rows=7000)
+    pool_a = build_pool(case)
+    pool_b = build_pool(case)
+    out_a = bf16_to_f64(_run_append(pool_a, case))
+    slot = to_dev(case.table[:, -1].copy())
+    fk.fp8kv_quantize_rows(pool_b, to_dev_bf16(case.new_k), to_dev_bf16(case.new_v), slot)
+    out_b = bf16_to_f64(fk.fp8kv_decode_attn(pool_b, to_dev_bf16(case.q), to_dev(case.table), to_dev(case.seq_lens),
+                                             case.max_seq_len, case.sm_scale))
+    torch.cuda.synchronize()
+    for a, b, name in zip(pool_arrays(pool_a), pool_arrays(pool_b), ("kc", "vc", "ks", "vs")):
+        assert_bits_equal(a, b, name)
+    # Both are within the oracle tolerance; they differ only in fp32 summation
+    # order of the new token's score.
+    assert np.abs(out_a - out_b).max() <= 2e-2
+    _, ref = _oracle_step(case)
+    assert_close(out_a, ref, "append")
+    assert_close(out_b, ref, "two calls")
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 64, 65, 129, 1000])
+def test_append_lengths(L):
+    say(f"decode+append L={L}")
+    case = wl.layer_decode(4, ctx=max(L, 1), pool_rows=2000)
+    pool = build_pool(case)
+    lens = np.array([L], np.int32)
+    ref_pools, ref = _oracle_step(case, lens)
+    out = _run_append(pool, case, seq_lens=lens, max_seq_len=L)
+    _check_pool(pool, ref_pools, f"L={L}")
+    got = bf16_to_f64(out)
+    assert_close(got, ref, f"L={L}")
+    if L == 1:
+        # A single key: every query head of group g returns that key's V row,
+        # dequantized as the prefill reconstruction does it (bf16 of fl32(c*s)).
+        row = int(case.table[0, 0])
+        v_ws = oracle.reconstruct(ref_pools[1], ref_pools[3], np.array([row], np.int32), case.n_kv_heads)[0]
+        G = case.n_q_heads // case.n_kv_heads
+        want = np.repeat(v_ws, G, axis=0)
+        assert_bits_equal(out.view(torch.int16).cpu().numpy()[0].view(np.uint16), want, "L=1 output")
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 4), (4, 2), (8, 1), (16, 2)])
+def test_append_gqa_ratios(G, Hkv):
+    say(f"decode+append GQA {G}, {Hkv} KV heads")
+    case = wl.layer_decode(5, ctx=3000, pool_rows=3500, n_q_heads=G * Hkv, n_kv_heads=Hkv)
+    pool = build_pool(case)
+    ref_pools, ref = _oracle_step(case)
+    out = bf16_to_f64(_run_append(pool, case))
+    _check_pool(pool, ref_pools, f"G={G}")
+    assert_close(out, ref, f"G={G} Hkv={Hkv}")
+
+
+def test_append_batched_16_requests():
+    say("decode+append 16 requests, lengths 1,024..32,768, GQA 4")
+    case = wl.batched_decode(0, with_new_token=True)
+    pool = build_pool(case)
+    ref_pools, ref = _oracle_step(case)
+    for cap in (0, 8):
+        if cap:
+            pool = build_pool(case)
+        out = bf16_to_f64(_run_append(pool, case, max_splits=cap))
+        _check_pool(pool, ref_pools, f"batched cap={cap}")
+        assert_close(out, ref, f"batched cap={cap}")
+        for b in range(case.batch):
+            assert_close(out[b], ref[b], f"  request {b} (L={case.seq_lens[b]})")
+
+
+def test_append_graph_replay():
+    say("decode+append captured in a HIP graph, replayed 4 times")
+    case = wl.layer_decode(6, ctx=8192, pool_rows=9000)
+    pool = build_pool(case)
+    q, nk, nv = to_dev_bf16(case.q), to_dev_bf16(case.new_k), to_dev_bf16(case.new_v)
+    t, sl = to_dev(case.table), to_dev(case.seq_lens)
+    ws = fk.decode_workspace(1, case.n_q_heads)
+    out = torch.empty_like(q)
+
+    def step():
+        fk.fp8kv_decode_attn_append(pool, q, nk, nv, t, sl, case.max_seq_len, case.sm_scale, workspace=ws, out=out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs"
+        _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
+    ref_pools, ref = _oracle_step(case)
+    _check_pool(pool, ref_pools, "graph")
+    assert_close(bf16_to_f64(eager), ref, "graph")
