@@ -71,7 +71,6 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   const int key_begin = split * chunk;
   const int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
   const int h0 = g * G;
-  if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 
   // The request length as a vector load, issued first: a scalar load would
   // share its wait with the kernel-argument loads and delay the table read.
@@ -299,6 +298,10 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     *reinterpret_cast<float4*>(part_o + ph * kHeadDim + d) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
     if (d == 0) part_lse[ph] = (den > 0.f) ? M + log2f(den) : -INFINITY;
   }
+  // The split count for a merge launched without one.  Written last: a branch
+  // at the top would split the entry block and serialize the argument loads
+  // ahead of the first table read.
+  if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 }
 
 // Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) over the
