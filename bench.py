@@ -57,10 +57,15 @@ def parse():
     return ap.parse_args()
 
 
+STAGE1_SOURCES = ("decode.hip", "fp8kv_device.h", "fp8kv_launch.h")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources the stage-1 kernel is built from (its byte counters
+    are only reused while these are unchanged)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_kv_cache_row_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in STAGE1_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
