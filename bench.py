@@ -240,7 +240,8 @@ def main():
 
     def append(p):
         return lib.fp8kv_decode_attn_append(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, new_k.data_ptr(),
-                                            new_v.data_ptr(), Hkv * 128, table.data_ptr(), L, lens.data_ptr(), L,
+                                            new_v.data_ptr(), Hkv * 128, slot.data_ptr(), table.data_ptr(), L,
+                                            lens.data_ptr(), L,
                                             case.sm_scale, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp)
 
     def step(i):

@@ -70,8 +70,8 @@ def load() -> ctypes.CDLL:
     L.fp8kv_decode_workspace_bytes.restype = sz
     L.fp8kv_decode_attn.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp, vp]
     L.fp8kv_decode_attn.restype = ctypes.c_int
-    L.fp8kv_decode_attn_append.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, i64, vp, i32, f32, i32, vp, sz, vp,
-                                           vp]
+    L.fp8kv_decode_attn_append.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, f32, i32, vp, sz,
+                                           vp, vp]
     L.fp8kv_decode_attn_append.restype = ctypes.c_int
     L.fp8kv_decode_stage1.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
     L.fp8kv_decode_stage1.restype = ctypes.c_int
@@ -247,11 +247,12 @@ def fp8kv_decode_attn(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor,
 
 
 def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                             row_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
-                             max_splits: int = 0, workspace: Optional[torch.Tensor] = None,
-                             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                             new_slots: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                             max_seq_len: int, sm_scale: float, max_splits: int = 0,
+                             workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
     """One decode step: quantize each request's new token (k_new/v_new bf16 [B][Hkv][128]) into
-    row_table[b][seq_lens[b] - 1] and attend over positions [0, seq_lens[b])."""
+    pool row new_slots[b] (== row_table[b][seq_lens[b] - 1]) and attend over positions [0, seq_lens[b])."""
     args, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
     B = q.shape[0]
     _dev_check(k_new, "k_new", torch.bfloat16)
@@ -264,10 +265,13 @@ def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tens
     stride = k_new.stride(0) if B > 1 else pool.n_kv_heads * HEAD_DIM
     if B > 1 and v_new.stride(0) != stride:
         raise ValueError("k_new and v_new need the same token stride")
+    _dev_check(new_slots, "new_slots", torch.int32)
+    if new_slots.numel() != B:
+        raise ValueError("new_slots must have B entries")
     if out is None:
         out = torch.empty_like(q)
-    st = load().fp8kv_decode_attn_append(*args[:4], _ptr(_bits(k_new)), _ptr(_bits(v_new)), stride, *args[4:],
-                                         _ptr(_bits(out)), _stream(stream))
+    st = load().fp8kv_decode_attn_append(*args[:4], _ptr(_bits(k_new)), _ptr(_bits(v_new)), stride,
+                                         _ptr(new_slots), *args[4:], _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_decode_attn_append")
     return out
 

@@ -315,7 +315,8 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 // the head group exactly as the quantize-on-write kernel does (same codec
 // functions), scores q against the decoded codes, and folds the token in as a
 // single-key partial (o = s_v * decode(v), lse = the score).  The workgroup of
-// the group's first query head writes the codes and scales to the token's row.
+// the group's first query head writes the codes and scales to the token's row
+// new_slots[b]; every load of the kernel is independent (one round trip).
 constexpr int kMergeBlock = 256;
 constexpr int kMergeWaves = kMergeBlock / kWave;
 constexpr int kMergeBatch = 16;  // splits per wave loaded at once
@@ -326,9 +327,7 @@ struct AppendKernelArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t new_token_stride;
-  const int32_t* table;
-  int64_t table_stride;
-  const int32_t* seq_lens;
+  const int32_t* new_slots;
   uint8_t* k_codes;
   uint8_t* v_codes;
   float* k_scales;
@@ -358,14 +357,14 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
 
   // The new token's inputs: its bf16 K/V pair at d = 2*lane, 2*lane + 1, and q.
   uint32_t k2 = 0u, v2 = 0u, q2 = 0u;
-  int len = 0;
+  int64_t slot = 0;
   int64_t b = 0, g = 0;
   if constexpr (APPEND) {
     b = bh / n_q_heads;
     const int h = (int)(bh % n_q_heads);
     g = h / (n_q_heads / app.n_kv_heads);
     if (wave == 0) {
-      len = app.seq_lens[b];
+      slot = app.new_slots[b];
       k2 = *reinterpret_cast<const uint32_t*>(app.k_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
       v2 = *reinterpret_cast<const uint32_t*>(app.v_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
       q2 = *reinterpret_cast<const uint32_t*>(app.q + bh * kHeadDim + 2 * lane);
@@ -437,10 +436,6 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
       m_w = mx;
       // One workgroup per (request, KV head) stores the row.
       if ((bh % n_q_heads) % (n_q_heads / app.n_kv_heads) == 0) {
-        // The position is clamped into the table row so that a length outside
-        // [1, table_stride] cannot address memory outside it.
-        const int64_t pos = min(max((int64_t)len - 1, (int64_t)0), app.table_stride - 1);
-        const int64_t slot = app.table[b * app.table_stride + pos];
         *reinterpret_cast<uint16_t*>(app.k_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)kc;
         *reinterpret_cast<uint16_t*>(app.v_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)vc;
         if (lane == 0) {
@@ -518,8 +513,8 @@ hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWor
 
 hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,
                                       int32_t n_split, const AppendArgs& app, uint16_t* out, hipStream_t stream) {
-  const AppendKernelArgs a{app.q, app.k_new, app.v_new, app.new_token_stride, app.row_table, app.table_stride,
-                           app.seq_lens, pool.k_codes, pool.v_codes, pool.k_scales, pool.v_scales,
+  const AppendKernelArgs a{app.q, app.k_new, app.v_new, app.new_token_stride, app.new_slots,
+                           pool.k_codes, pool.v_codes, pool.k_scales, pool.v_scales,
                            pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads, app.sm_scale * kLog2e};
   hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0,
                      stream, ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);

@@ -212,14 +212,16 @@ fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, 
 
 fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
                                       int32_t n_q_heads, const uint16_t* k_new, const uint16_t* v_new,
-                                      int64_t new_token_stride, const int32_t* row_table, int64_t table_stride,
+                                      int64_t new_token_stride, const int32_t* new_slots,
+                                      const int32_t* row_table, int64_t table_stride,
                                       const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                                       int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
                                       void* stream) {
   fp8kv_status st = check_decode_args(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
                                       sm_scale, max_splits, workspace, workspace_bytes);
   if (st != FP8KV_OK) return st;
-  if (!out || !k_new || !v_new || max_seq_len < 1) return FP8KV_ERR_INVALID_ARG;
+  if (!out || !k_new || !v_new || !new_slots || max_seq_len < 1) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(new_slots, 4)) return FP8KV_ERR_ALIGNMENT;
   if (new_token_stride < (int64_t)pool->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || (new_token_stride % 8) != 0)
     return FP8KV_ERR_ALIGNMENT;
@@ -232,7 +234,7 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16
   hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
                                              max_seq_len, sm_scale, geo, ws, 1, s);
   if (e != hipSuccess) return FP8KV_ERR_HIP;
-  const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, row_table, table_stride, seq_lens, sm_scale};
+  const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale};
   return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), batch, n_q_heads, ws, geo.n_split, app, out, s));
 }
 

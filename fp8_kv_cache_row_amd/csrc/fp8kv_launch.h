@@ -67,16 +67,14 @@ hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWor
                                uint16_t* out, hipStream_t stream);
 
 // The new token of each request: bf16 K/V rows [B][token_stride] (head g at
-// g * 128), quantized into pool row row_table[b][seq_lens[b] - 1] and folded
-// into the merge as one more single-key partial.
+// g * 128), quantized into pool row new_slots[b] and folded into the merge as
+// one more single-key partial.
 struct AppendArgs {
   const uint16_t* q;
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t new_token_stride;  // elements
-  const int32_t* row_table;
-  int64_t table_stride;
-  const int32_t* seq_lens;
+  const int32_t* new_slots;
   float sm_scale;
 };
 hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,

@@ -191,10 +191,10 @@ fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_sp
  * search": on the FP8 path every new K/V row is quantized as it is written;
  * PR #897 description: the decode reader then attends over the pool).
  *
- * For each request b the new token sits at position p_b = seq_lens[b] - 1 of
- * its row table.  The call has the effect of
- *   fp8kv_quantize_rows(pool, k_new, v_new, new_token_stride,
- *                       slots = {row_table[b * table_stride + p_b]}, batch)
+ * For each request b the new token sits at position p_b = seq_lens[b] - 1,
+ * and its pool row is new_slots[b] (== row_table[b * table_stride + p_b]).
+ * The call has the effect of
+ *   fp8kv_quantize_rows(pool, k_new, v_new, new_token_stride, new_slots, batch)
  * followed by fp8kv_decode_attn with the same arguments: the token's codes and
  * scales land in its row bit for bit as fp8kv_quantize_rows would write them,
  * and `out` is attention over positions [0, seq_lens[b]) including the token.
@@ -205,16 +205,18 @@ fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_sp
  * k_new, v_new:      device bf16, token b at k_new + b * new_token_stride,
  *                    [n_kv_heads][128] each; 16-byte aligned, stride a
  *                    multiple of 8 elements and >= n_kv_heads * 128.
+ * new_slots:         device int32 [batch], 4-byte aligned: physical rows of
+ *                    `pool`, distinct between requests, named by no position
+ *                    below p_b of any request.
  * seq_lens:          device int32 [batch], each in [1, max_seq_len].
- * row_table:         as for fp8kv_decode_attn; in addition the new tokens'
- *                    rows must differ between requests and no position below
- *                    p_b of any request may name one of them.
+ * row_table:         as for fp8kv_decode_attn.
  * Other arguments, the workspace and the errors are those of
  * fp8kv_decode_attn; max_seq_len must be >= 1.
  */
 fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
                                       int32_t n_q_heads, const uint16_t *k_new, const uint16_t *v_new,
-                                      int64_t new_token_stride, const int32_t *row_table,
+                                      int64_t new_token_stride, const int32_t *new_slots,
+                                      const int32_t *row_table,
                                       int64_t table_stride, const int32_t *seq_lens, int32_t max_seq_len,
                                       float sm_scale, int32_t max_splits, void *workspace,
                                       size_t workspace_bytes, uint16_t *out, void *stream);

@@ -115,7 +115,7 @@ def test_decode_stage_validation(lib):
 def _append(lib, p, **kw):
     wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
     return lib.fp8kv_decode_attn_append(ctypes.byref(p), kw.get("q", A), 1, kw.get("hq", 32), kw.get("kn", A),
-                                        kw.get("vn", 2 * A), kw.get("nstride", 512), A, 1024, A,
+                                        kw.get("vn", 2 * A), kw.get("nstride", 512), kw.get("slots", A), A, 1024, A,
                                         kw.get("maxlen", 1000), 0.088, 0, A, kw.get("wsb", wsb), kw.get("out", A),
                                         None)
 
@@ -125,6 +125,8 @@ def test_decode_append_validation(lib):
     assert _append(lib, p, kn=0) == INVALID
     assert _append(lib, p, vn=0) == INVALID
     assert _append(lib, p, out=0) == INVALID
+    assert _append(lib, p, slots=0) == INVALID
+    assert _append(lib, p, slots=A + 2) == ALIGN
     assert _append(lib, p, maxlen=0) == INVALID                      # the new token needs a position
     assert _append(lib, p, nstride=256) == INVALID                   # shorter than Hkv * 128
     assert _append(lib, p, nstride=516) == ALIGN

@@ -37,9 +37,10 @@ def _oracle_step(case, seq_lens=None):
 def _run_append(pool, case, seq_lens=None, max_seq_len=None, max_splits=0):
     lens = case.seq_lens if seq_lens is None else seq_lens
     msl = int(lens.max()) if max_seq_len is None else max_seq_len
+    slots = np.array([case.table[b, lens[b] - 1] for b in range(case.batch)], np.int32)
     out = fk.fp8kv_decode_attn_append(pool, to_dev_bf16(case.q), to_dev_bf16(case.new_k), to_dev_bf16(case.new_v),
-                                      to_dev(case.table), to_dev(np.asarray(lens, np.int32)), msl, case.sm_scale,
-                                      max_splits=max_splits)
+                                      to_dev(slots), to_dev(case.table), to_dev(np.asarray(lens, np.int32)), msl,
+                                      case.sm_scale, max_splits=max_splits)
     torch.cuda.synchronize()
     return out
 
@@ -137,9 +138,11 @@ def test_append_graph_replay():
     t, sl = to_dev(case.table), to_dev(case.seq_lens)
     ws = fk.decode_workspace(1, case.n_q_heads)
     out = torch.empty_like(q)
+    slot = to_dev(case.table[:, -1].copy())
 
     def step():
-        fk.fp8kv_decode_attn_append(pool, q, nk, nv, t, sl, case.max_seq_len, case.sm_scale, workspace=ws, out=out)
+        fk.fp8kv_decode_attn_append(pool, q, nk, nv, slot, t, sl, case.max_seq_len, case.sm_scale, workspace=ws,
+                                    out=out)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
