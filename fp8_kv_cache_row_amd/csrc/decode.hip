@@ -203,8 +203,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
         for (int r = 0; r < 8; ++r) sv[r] = (t0 + step_key(j, r) < key_end) ? sv[r] : -INFINITY;
       }
       float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_over_row_groups(tmax);
 
       // Lazy maximum: move it (and rescale O and l) only when this step's
       // maximum exceeds it by more than the slack; otherwise p <= 2^slack.  A

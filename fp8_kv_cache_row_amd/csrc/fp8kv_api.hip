@@ -19,6 +19,13 @@ using fp8kv::PoolView;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// NaN test on the bit pattern, independent of floating-point compile flags.
+bool is_nan(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof(u));
+  return (u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u;
+}
+
 bool supported_group(int32_t n_q_heads, int32_t n_kv_heads) {
   if (n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return false;
   const int32_t g = n_q_heads / n_kv_heads;
@@ -122,7 +129,7 @@ fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, 
     return FP8KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
   if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
-  if (!(sm_scale == sm_scale)) return FP8KV_ERR_INVALID_ARG;  // NaN
+  if (is_nan(sm_scale)) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4)) return FP8KV_ERR_ALIGNMENT;
   if (!workspace || workspace_bytes < partial_bytes(batch, n_q_heads, split_cap(max_splits)))
     return FP8KV_ERR_WORKSPACE;
@@ -248,7 +255,7 @@ fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q,
   if (n_tokens <= 0 || n_prefix < 0) return FP8KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
   if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
-  if (!(sm_scale == sm_scale)) return FP8KV_ERR_INVALID_ARG;
+  if (is_nan(sm_scale)) return FP8KV_ERR_INVALID_ARG;
   if (n_prefix > 0) {
     if (!prefix_rows) return FP8KV_ERR_INVALID_ARG;
     if (!ws_k || !ws_v || ws_capacity_rows < n_prefix) return FP8KV_ERR_WORKSPACE;

@@ -87,6 +87,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Maximum over the four 16-lane rows of the wave (lanes n, n+16, n+32, n+48),
+// returned to all four.  gfx950's row swaps keep this out of LDS:
+// permlane16_swap(x, x) yields rows (0,0,2,2) and (1,1,3,3) of x,
+// permlane32_swap(y, y) yields its low and high halves.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a.x), __uint_as_float(a.y));
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b.x), __uint_as_float(b.y));
+}
+
 // 4x4 byte transpose across four dwords: out[k] byte r = in[r] byte k.
 __device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                                    uint32_t& o0, uint32_t& o1, uint32_t& o2,
