@@ -9,21 +9,28 @@
 // Work decomposition: a workgroup owns 128 "query rows", each one
 // (query token, query head) pair of a single KV head's group (128/G tokens x
 // G heads), so one K/V tile staged in LDS feeds every query head of the
-// group.  Four waves take 32 rows each.  Per 64-key tile a wave computes
+// group.  Four waves take 32 rows each.  Per 32-key sub-step a wave computes
 // S^T = K * Q^T (keys on MFMA rows, query rows on columns) so that a lane holds
-// 16 keys of one query row: the row max/sum need two cross-lane steps, and the
-// same registers are the k-slots of the P*V MFMA.  V is stored transposed in
-// LDS ([d][key]) so the P*V operand is a plain 8-byte LDS read.
+// 8 keys of one query row: the row max needs two cross-lane steps (gfx950 row
+// swaps), and the same registers are the k-slots of the P*V MFMA.
 //
-// Pipelining: K/V tiles are double-buffered in LDS.  The global loads of tile
-// t+1 are issued into registers before tile t is computed and written to the
-// other buffer afterwards, so one barrier per tile suffices and the load
-// latency hides behind the MFMA work.  A tile is computed as two 32-key
-// sub-steps (QK^T, softmax, P*V each) to keep the live registers low.  Online
-// softmax in log2 units with a lazy maximum (O and l are rescaled only when a
-// sub-step's maximum exceeds the running one by more than 8), so the
-// accumulators are normally touched by the MFMA alone.  Workgroups with the most keys (the last query tokens) are
-// launched first.
+// K and V tiles (64 keys) are both stored row-major, [key][16 chunks of
+// 16 B], chunk c of key m at position c ^ (m & 15).  They are fetched by
+// global-to-LDS loads, which write lane l's 16 bytes at LDS offset 16 l of the
+// instruction's 1 KB (4 key rows): lane l fetches chunk (l & 15) ^ (key & 15)
+// of its key, so the swizzle comes from the gather and no data passes through
+// registers.  The P*V operand (V[key][d] for 4 consecutive keys at one d) is
+// read with the gfx950 transposing LDS read: within a 16-lane group, source
+// lane s names row s/4, columns 4(s%4)..+3 of a 4x16 block, and lane i
+// receives column i of its 4 rows.
+//
+// Pipelining: the tiles are double-buffered; the loads of tile t+1 are issued
+// right after the barrier that opens tile t, so one barrier per tile suffices
+// and the load latency hides behind the MFMA work.  Online softmax in log2
+// units with a lazy maximum (O and l are rescaled only when a sub-step's
+// maximum exceeds the running one by more than 8), so the accumulators are
+// normally touched by the MFMA alone.  Workgroups with the most keys (the last
+// query tokens) are launched first.
 #include <math.h>
 
 #include "fp8kv_device.h"
@@ -33,90 +40,27 @@ namespace fp8kv {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
 constexpr int kRowsPerWg = 128;
 constexpr int kTileKeys = 64;
-// K tile: [64 keys][16 chunks of 16 B]; chunk c of key m is stored at chunk
-// position c ^ (m & 15) so that 16 lanes reading one chunk of 16 keys hit all
-// 64 banks.
-constexpr int kKRowBytes = kHeadDim * 2;
-constexpr int kKTileBytes = kTileKeys * kKRowBytes;
-// V^T tile: [128 d][16 chunks of 8 B (4 keys)]; chunk q of row d is stored at
-// position q ^ vswz(d).  vswz takes 16 distinct values both over d = 16b + n
-// (n = 0..15: the rows one P*V operand read touches) and over d = 8c + k
-// (c = 0..15: the rows one transposing store touches), so neither side has
-// bank conflicts.
-constexpr int kVRowBytes = kTileKeys * 2;
-__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 15; }
-constexpr int kVTileBytes = kHeadDim * kVRowBytes;
+constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 key row
+constexpr int kTileBytes = kTileKeys * kRowBytes;       // 16 KB per tile
+constexpr int kLoadsPerWave = kTileKeys / 4 / kWaves;   // 1 KB (4 rows) per load
 constexpr float kLazyMaxSlack = 8.0f;
+static_assert(kLoadsPerWave * 4 * kWaves == kTileKeys, "a tile is whole 4-row loads");
 
-// One thread's share of a K/V tile in registers: 4 K chunks (16 B each) and
-// 4 keys x 8 d of V.
-struct TileRegs {
-  uint4 k[4];
-  uint4 v[4];
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Fast path: the whole tile lies in the workspace or in the chunk (below
-// n_keys), so every element address is one tile base plus a per-thread offset
-// fixed for the whole loop.
-__device__ __forceinline__ void load_tile_run(TileRegs& r, const uint16_t* __restrict__ kbase,
-                                              const uint16_t* __restrict__ vbase, const int (&kofs)[4],
-                                              const int (&vofs)[4]) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) r.k[it] = *reinterpret_cast<const uint4*>(kbase + kofs[it]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r.v[e] = *reinterpret_cast<const uint4*>(vbase + vofs[e]);
+// Byte offset of 16-byte chunk c of key m (tile-local) in a tile.
+__device__ __forceinline__ int chunk_at(int m, int c) { return m * kRowBytes + ((c ^ (m & 15)) << 4); }
+
+__device__ __forceinline__ void g2lds16(const uint16_t* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// General path (a tile that straddles the workspace/chunk boundary or the
-// last visible key).
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* __restrict__ ws_k,
-                                          const uint16_t* __restrict__ ws_v, const uint16_t* __restrict__ k_cur,
-                                          const uint16_t* __restrict__ v_cur, int n_prefix, int n_keys, int u0,
-                                          int64_t kv_row, int g, int tid) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int c = tid + kBlock * it;
-    const int u = u0 + (c >> 4), ch = c & 15;
-    // keys past n_keys re-read the last valid key (never weighted: masked)
-    const int uc = min(u, n_keys - 1);
-    const uint16_t* src = (uc < n_prefix) ? ws_k + (int64_t)uc * kv_row : k_cur + (int64_t)(uc - n_prefix) * kv_row;
-    r.k[it] = *reinterpret_cast<const uint4*>(src + (int64_t)g * kHeadDim + ch * 8);
-  }
-  const int kg = tid >> 4, c = tid & 15;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int uc = min(u0 + 4 * kg + e, n_keys - 1);
-    const uint16_t* src = (uc < n_prefix) ? ws_v + (int64_t)uc * kv_row : v_cur + (int64_t)(uc - n_prefix) * kv_row;
-    r.v[e] = *reinterpret_cast<const uint4*>(src + (int64_t)g * kHeadDim + c * 8);
-  }
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint8_t* k_lds, uint8_t* v_lds, int tid) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int c = tid + kBlock * it;
-    const int key = c >> 4, ch = c & 15;
-    *reinterpret_cast<uint4*>(k_lds + key * kKRowBytes + ((ch ^ (key & 15)) << 4)) = r.k[it];
-  }
-  // V^T: this thread's 4 keys (4kg..4kg+3) at d = 8c..8c+7 -> 8 rows of 8 bytes
-  const int kg = tid >> 4, c = tid & 15;
-  const uint32_t w[4][4] = {{r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w},
-                            {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w},
-                            {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w},
-                            {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w}};
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint32_t sel = s ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(w[1][p], w[0][p], sel);  // keys 0,1
-      const uint32_t hi = __builtin_amdgcn_perm(w[3][p], w[2][p], sel);  // keys 2,3
-      const int d = 8 * c + 2 * p + s;
-      *reinterpret_cast<uint2*>(v_lds + d * kVRowBytes + ((kg ^ vswz(d)) << 3)) = make_uint2(lo, hi);
-    }
-  }
+__device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(uint2, v);
 }
 
 template <int G>
@@ -125,12 +69,12 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
     const uint16_t* __restrict__ k_cur, const uint16_t* __restrict__ v_cur, int32_t n_prefix, int32_t n_tokens,
     int32_t n_q_heads, int32_t n_kv_heads, float qk_scale_log2, uint16_t* __restrict__ out) {
   constexpr int BQ = kRowsPerWg / G;  // query tokens per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kKTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][kVTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15;
   const int j = lane >> 4;
   const int g = blockIdx.y;
@@ -167,38 +111,53 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
   // first key index at which any row of this workgroup needs the causal mask
   const int diag = n_prefix + i0;
 
-  // Per-thread element offsets of its tile share, relative to the tile's first key.
-  int kofs[4], vofs[4];
+  // This lane's share of a tile fetch: load i covers tile-local keys
+  // 4(kLoadsPerWave * wave + i) + [0, 4); the lane takes key +(lane >> 4) and
+  // the chunk that lands at position (lane & 15) of that key's row.
+  int fkey[kLoadsPerWave], fofs[kLoadsPerWave];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) kofs[it] = ((tid >> 4) + 16 * it) * (int)kv_row + g * kHeadDim + (tid & 15) * 8;
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    fkey[i] = 4 * (kLoadsPerWave * wave + i) + (lane >> 4);
+    fofs[i] = fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ (fkey[i] & 15)) << 3);
+  }
+  auto fetch = [&](int buf, int u0) {
+    uint8_t* kd = k_lds[buf] + kLoadsPerWave * wave * 1024;
+    uint8_t* vd = v_lds[buf] + kLoadsPerWave * wave * 1024;
+    if (u0 + kTileKeys <= n_prefix || (u0 >= n_prefix && u0 + kTileKeys <= n_keys)) {
+      // the whole tile comes from one source: one base plus fixed offsets
+      const int64_t base = (u0 < n_prefix) ? (int64_t)u0 * kv_row : (int64_t)(u0 - n_prefix) * kv_row;
+      const uint16_t* kb = ((u0 < n_prefix) ? ws_k : k_cur) + base;
+      const uint16_t* vb = ((u0 < n_prefix) ? ws_v : v_cur) + base;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) vofs[e] = (4 * (tid >> 4) + e) * (int)kv_row + g * kHeadDim + (tid & 15) * 8;
-  auto fetch = [&](TileRegs& r, int u0) {
-    if (u0 + kTileKeys <= n_prefix) {
-      load_tile_run(r, ws_k + (int64_t)u0 * kv_row, ws_v + (int64_t)u0 * kv_row, kofs, vofs);
-    } else if (u0 >= n_prefix && u0 + kTileKeys <= n_keys) {
-      load_tile_run(r, k_cur + (int64_t)(u0 - n_prefix) * kv_row, v_cur + (int64_t)(u0 - n_prefix) * kv_row, kofs,
-                    vofs);
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        g2lds16(kb + fofs[i], kd + i * 1024);
+        g2lds16(vb + fofs[i], vd + i * 1024);
+      }
     } else {
-      load_tile(r, ws_k, ws_v, k_cur, v_cur, n_prefix, n_keys, u0, kv_row, g, tid);
+      // straddles the workspace/chunk boundary or the last visible key; keys
+      // past n_keys re-read the last one (masked, never weighted)
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int u = min(u0 + fkey[i], n_keys - 1);
+        const int64_t off = (u < n_prefix) ? (int64_t)u * kv_row : (int64_t)(u - n_prefix) * kv_row;
+        const int64_t lo = fofs[i] - fkey[i] * (int)kv_row;  // head + chunk part
+        g2lds16(((u < n_prefix) ? ws_k : k_cur) + off + lo, kd + i * 1024);
+        g2lds16(((u < n_prefix) ? ws_v : v_cur) + off + lo, vd + i * 1024);
+      }
     }
   };
 
-  TileRegs regs;
-  fetch(regs, 0);
-  store_tile(regs, k_lds[0], v_lds[0], tid);
+  fetch(0, 0);
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int u0 = tile * kTileKeys;
     const int buf = tile & 1;
-    __syncthreads();  // tile `tile` is in buf; everyone is done with the other buffer
-    const bool more = tile + 1 < n_tiles;
-    if (more) fetch(regs, u0 + kTileKeys);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `tile` have landed (vmcnt 0)
+    __syncthreads();                // every wave's have; the other buffer is free
+    if (tile + 1 < n_tiles) fetch(buf ^ 1, u0 + kTileKeys);
     const uint8_t* kt = k_lds[buf];
     const uint8_t* vt = v_lds[buf];
 
-    // Two 32-key sub-steps per tile: S^T for key blocks 2st, 2st+1, softmax,
-    // then P*V; live score/operand registers stay at one sub-step's worth.
     const bool tile_mask = (u0 + kTileKeys - 1 > diag) || (u0 + kTileKeys > n_keys);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -211,8 +170,7 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
         const int key = (2 * st + kb2) * 16 + n;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const int ch = 4 * kk + j;  // d = 32kk + 8j + [0, 8)
-          const bf16x8 a = u4_as_bf16x8(*reinterpret_cast<const uint4*>(kt + key * kKRowBytes + ((ch ^ (key & 15)) << 4)));
+          const bf16x8 a = u4_as_bf16x8(*reinterpret_cast<const uint4*>(kt + chunk_at(key, 4 * kk + j)));  // d = 32kk + 8j + [0, 8)
           s[kb2][0] = mfma16x16x32(a, qb[0][kk], s[kb2][0]);
           s[kb2][1] = mfma16x16x32(a, qb[1][kk], s[kb2][1]);
         }
@@ -261,24 +219,22 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
                                          f32x2_to_bf16x2(p[4], p[5]), f32x2_to_bf16x2(p[6], p[7])));
       }
 
-      // ---- O += P * V: B operand = V^T rows d = 16nb + n, the lane's 8 keys
+      // ---- O += P * V.  B operand of lane (n, j): V[key][16nb + n] for keys
+      //      32st + 4j + [0,4) (slots 0..3) and 32st + 16 + 4j + [0,4) (slots
+      //      4..7), by two transposing reads: source lane s = n of group j
+      //      names key +(s >> 2), columns 16nb + 4(s & 3) .. +3.
+      const int ka = 32 * st + 4 * j + (n >> 2);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const int d = 16 * nb + n;
-        const int q0 = 8 * st + j;      // keys 32st + 4j .. +3
-        const int q1 = 8 * st + 4 + j;  // keys 32st + 16 + 4j .. +3
-        const uint8_t* rowp = vt + d * kVRowBytes;
-        const uint2 b0 = *reinterpret_cast<const uint2*>(rowp + ((q0 ^ vswz(d)) << 3));
-        const uint2 b1 = *reinterpret_cast<const uint2*>(rowp + ((q1 ^ vswz(d)) << 3));
+        const int c = 2 * nb + ((n & 3) >> 1);
+        const int half = (n & 1) << 3;
+        const uint2 b0 = ds_read_tr16(vt + chunk_at(ka, c) + half);
+        const uint2 b1 = ds_read_tr16(vt + chunk_at(ka + 16, c) + half);
         const bf16x8 bv = u4_as_bf16x8(make_uint4(b0.x, b0.y, b1.x, b1.y));
         o[0][nb] = mfma16x16x32(pa[0], bv, o[0][nb]);
         o[1][nb] = mfma16x16x32(pa[1], bv, o[1][nb]);
       }
     }
-
-    // ---- the next tile into the other buffer (its last readers finished
-    //      before this iteration's barrier)
-    if (more) store_tile(regs, k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
   }
 
   // ---- normalize and store: lane (n, j) holds rows 4j+i of block cb, d = 16nb + n
