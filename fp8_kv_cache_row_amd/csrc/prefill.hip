@@ -9,7 +9,8 @@
 // Work decomposition: a workgroup owns 128 "query rows", each one
 // (query token, query head) pair of a single KV head's group (128/G tokens x
 // G heads), so one K/V tile staged in LDS feeds every query head of the
-// group.  Four waves take 32 rows each.  Per 32-key sub-step a wave computes
+// group.  Eight waves take 16 rows each (fewer live registers per wave, two
+// waves per SIMD).  Per 32-key sub-step a wave computes
 // S^T = K * Q^T (keys on MFMA rows, query rows on columns) so that a lane holds
 // 8 keys of one query row: the row max needs two cross-lane steps (gfx950 row
 // swaps), and the same registers are the k-slots of the P*V MFMA.
@@ -39,9 +40,13 @@ namespace fp8kv {
 
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kWaves = kBlock / kWave;
+#ifndef FP8KV_PREFILL_ROW_BLOCKS
+#define FP8KV_PREFILL_ROW_BLOCKS 1
+#endif
+constexpr int kRowBlocks = FP8KV_PREFILL_ROW_BLOCKS;    // 16-row query blocks per wave
 constexpr int kRowsPerWg = 128;
+constexpr int kWaves = kRowsPerWg / (16 * kRowBlocks);
+constexpr int kBlock = kWaves * kWave;
 constexpr int kTileKeys = 64;
 constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 key row
 constexpr int kTileBytes = kTileKeys * kRowBytes;       // 16 KB per tile
@@ -83,13 +88,13 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
   const int i_last = min(i0 + BQ, n_tokens) - 1;
   const int n_keys = n_prefix + i_last + 1;  // keys any row of this workgroup may see
 
-  // Q^T operand for the wave's two 16-row column blocks; rows past the chunk
+  // Q^T operand for the wave's 16-row column blocks; rows past the chunk
   // reuse the last token (never stored).
-  bf16x8 qb[2][4];
-  int row_tok[2];
+  bf16x8 qb[kRowBlocks][4];
+  int row_tok[kRowBlocks];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int rho = wave * 32 + cb * 16 + n;
+  for (int cb = 0; cb < kRowBlocks; ++cb) {
+    const int rho = (wave * kRowBlocks + cb) * 16 + n;
     const int tok = min(i0 + rho / G, n_tokens - 1);
     const int head = h0 + rho % G;
     row_tok[cb] = tok;
@@ -98,11 +103,15 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
     for (int kk = 0; kk < 4; ++kk) qb[cb][kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32 * kk));
   }
 
-  float m_run[2] = {-INFINITY, -INFINITY};  // lazy running max of row n (log2 units)
-  float l_part[2] = {0.f, 0.f};             // this lane's share of the row sum
-  f32x4 o[2][8];
+  float m_run[kRowBlocks], l_part[kRowBlocks];  // lazy running max of row n (log2 units); lane's row-sum share
+  f32x4 o[kRowBlocks][8];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kRowBlocks; ++mb) {
+    m_run[mb] = -INFINITY;
+    l_part[mb] = 0.f;
+  }
+#pragma unroll
+  for (int mb = 0; mb < kRowBlocks; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -162,17 +171,17 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       // ---- S^T = K * Q^T for keys u0 + 32st + [0, 32), both query-row blocks
-      f32x4 s[2][2];
+      f32x4 s[2][kRowBlocks];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        s[kb2][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[kb2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < kRowBlocks; ++cb) s[kb2][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int key = (2 * st + kb2) * 16 + n;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 a = u4_as_bf16x8(*reinterpret_cast<const uint4*>(kt + chunk_at(key, 4 * kk + j)));  // d = 32kk + 8j + [0, 8)
-          s[kb2][0] = mfma16x16x32(a, qb[0][kk], s[kb2][0]);
-          s[kb2][1] = mfma16x16x32(a, qb[1][kk], s[kb2][1]);
+#pragma unroll
+          for (int cb = 0; cb < kRowBlocks; ++cb) s[kb2][cb] = mfma16x16x32(a, qb[cb][kk], s[kb2][cb]);
         }
       }
 
@@ -180,9 +189,9 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
       //      scores; the scale enters through one FMA per element.  Lane
       //      (n, j) holds keys 32st + 4j + i (slot i) and 32st + 16 + 4j + i.
       const bool need_mask = tile_mask && (u0 + 32 * st + 31 > diag || u0 + 32 * st + 32 > n_keys);
-      bf16x8 pa[2];
+      bf16x8 pa[kRowBlocks];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < kRowBlocks; ++cb) {
         float sc[8] = {s[0][cb][0], s[0][cb][1], s[0][cb][2], s[0][cb][3],
                        s[1][cb][0], s[1][cb][1], s[1][cb][2], s[1][cb][3]};
         if (need_mask) {
@@ -231,21 +240,21 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
         const uint2 b0 = ds_read_tr16(vt + chunk_at(ka, c) + half);
         const uint2 b1 = ds_read_tr16(vt + chunk_at(ka + 16, c) + half);
         const bf16x8 bv = u4_as_bf16x8(make_uint4(b0.x, b0.y, b1.x, b1.y));
-        o[0][nb] = mfma16x16x32(pa[0], bv, o[0][nb]);
-        o[1][nb] = mfma16x16x32(pa[1], bv, o[1][nb]);
+#pragma unroll
+        for (int cb = 0; cb < kRowBlocks; ++cb) o[cb][nb] = mfma16x16x32(pa[cb], bv, o[cb][nb]);
       }
     }
   }
 
   // ---- normalize and store: lane (n, j) holds rows 4j+i of block cb, d = 16nb + n
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kRowBlocks; ++cb) {
     float l_tot = l_part[cb] + __shfl_xor(l_part[cb], 16);
     l_tot += __shfl_xor(l_tot, 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float li = __shfl(l_tot, 4 * j + i);
-      const int rho = wave * 32 + cb * 16 + 4 * j + i;
+      const int rho = (wave * kRowBlocks + cb) * 16 + 4 * j + i;
       const int tok = i0 + rho / G;
       const int head = h0 + rho % G;
       if (tok < n_tokens) {
