@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--pools", type=int, default=12, help="pool copies rotated per step (cold HBM)")
     ap.add_argument("--max-splits", type=int, default=0)
-    ap.add_argument("--layout", default="separate", choices=["separate", "interleaved"])
+    ap.add_argument("--layout", default="interleaved", choices=["separate", "interleaved"],
+                    help="pool layout: interleaved 1,056-byte row records (K codes, V codes, K scales, V scales "
+                         "of all KV heads) or four separate arrays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) instead")
@@ -72,15 +74,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes_hint: int):
+def measured_traffic(layout: str):
     """HBM bytes per stage-1 launch from the committed rocprofv3 counter runs,
-    or None when they were taken on a different kernel source."""
+    or None when they were taken on a different kernel source or pool layout."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("pool_layout") != layout:
         return None
     return rec.get("bytes_per_launch")
 
@@ -342,7 +344,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(kv_bytes),
+            "traffic": measured_traffic(args.layout),
         },
     }
     if not args.no_prefill:
