@@ -252,8 +252,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   }
 
   // Per-head totals of this wave.
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_over_row_groups(l_part);
 
   if (j == 0) {
     sm_m[wave][n] = m_run;
@@ -372,15 +371,19 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
 
   float m_w = -INFINITY, den = 0.f;
   float2 acc = make_float2(0.f, 0.f);
-  for (int base = 0; base < n_split; base += kMergeWaves * kMergeBatch) {
-    float lr[kMergeBatch];
-    float2 v[kMergeBatch];
+  // One batch of splits: wave w takes splits base + w + 4i, loaded together
+  // (clamped indices, no branches) and folded into (m_w, den, acc).
+  float lr[kMergeBatch];
+  float2 v[kMergeBatch];
+  auto load_batch = [&](int base) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const int sidx = min(base + wave + kMergeWaves * i, n_split - 1);
       lr[i] = lse_p[sidx];
       v[i] = *reinterpret_cast<const float2*>(po + (int64_t)sidx * kHeadDim);
     }
+  };
+  auto fold_batch = [&](int base) {
     float mx = m_w;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
@@ -401,19 +404,18 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
         den += w;
       }
     }
-  }
+  };
+  load_batch(0);  // in flight while wave 0 quantizes and scores the new token
 
+  float lse_new = -INFINITY;
+  float2 o_new = make_float2(0.f, 0.f);
   if constexpr (APPEND) {
     if (wave == 0) {
       // Quantize the K and V rows (128 values over the wave, two per lane).
       const float kx0 = bf16lo_to_f32(k2), kx1 = bf16hi_to_f32(k2);
       const float vx0 = bf16lo_to_f32(v2), vx1 = bf16hi_to_f32(v2);
-      float ka = fmaxf(fabsf(kx0), fabsf(kx1)), va = fmaxf(fabsf(vx0), fabsf(vx1));
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        ka = fmaxf(ka, __shfl_xor(ka, off));
-        va = fmaxf(va, __shfl_xor(va, off));
-      }
+      const float ka = wave_max(fmaxf(fabsf(kx0), fabsf(kx1)));
+      const float va = wave_max(fmaxf(fabsf(vx0), fabsf(vx1)));
       const float sk = e4m3_row_scale(ka), sv = e4m3_row_scale(va);
       const uint32_t kc = f32x2_to_fp8x2<false>(e4m3_prescaled(kx0, ka, sk), e4m3_prescaled(kx1, ka, sk), 0u);
       const uint32_t vc = f32x2_to_fp8x2<false>(e4m3_prescaled(vx0, va, sv), e4m3_prescaled(vx1, va, sv), 0u);
@@ -421,18 +423,9 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
       float kd[4], vd[4];
       fp8x4_to_f32x4(kc, kd);
       fp8x4_to_f32x4(vc, vd);
-      float dot = bf16lo_to_f32(q2) * kd[0] + bf16hi_to_f32(q2) * kd[1];
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
-      const float lse_new = dot * sk * app.qk_scale_log2;
-      const float2 o_new = make_float2(vd[0] * sv, vd[1] * sv);
-      const float mx = fmaxf(m_w, lse_new);
-      const float a = __builtin_amdgcn_exp2f(m_w - mx);
-      const float w = __builtin_amdgcn_exp2f(lse_new - mx);
-      acc.x = acc.x * a + w * o_new.x;
-      acc.y = acc.y * a + w * o_new.y;
-      den = den * a + w;
-      m_w = mx;
+      const float dot = wave_sum(bf16lo_to_f32(q2) * kd[0] + bf16hi_to_f32(q2) * kd[1]);
+      lse_new = dot * sk * app.qk_scale_log2;
+      o_new = make_float2(vd[0] * sv, vd[1] * sv);
       // One workgroup per (request, KV head) stores the row.
       if ((bh % n_q_heads) % (n_q_heads / app.n_kv_heads) == 0) {
         *reinterpret_cast<uint16_t*>(app.k_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)kc;
@@ -442,6 +435,24 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
           app.v_scales[slot * app.scale_row_stride + g] = sv;
         }
       }
+    }
+  }
+
+  fold_batch(0);
+  for (int base = kMergeWaves * kMergeBatch; base < n_split; base += kMergeWaves * kMergeBatch) {
+    load_batch(base);
+    fold_batch(base);
+  }
+
+  if constexpr (APPEND) {
+    if (wave == 0) {  // the new token as one more single-key partial
+      const float mx = fmaxf(m_w, lse_new);
+      const float a = __builtin_amdgcn_exp2f(m_w - mx);
+      const float w = __builtin_amdgcn_exp2f(lse_new - mx);
+      acc.x = acc.x * a + w * o_new.x;
+      acc.y = acc.y * a + w * o_new.y;
+      den = den * a + w;
+      m_w = mx;
     }
   }
 

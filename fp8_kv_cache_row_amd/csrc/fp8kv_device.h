@@ -99,6 +99,43 @@ __device__ __forceinline__ float max_over_row_groups(float x) {
   return fmaxf(__uint_as_float(b.x), __uint_as_float(b.y));
 }
 
+// Sum over the four 16-lane rows of the wave, returned to all four (same row
+// swaps as max_over_row_groups).
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a.x) + __uint_as_float(a.y);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b.x) + __uint_as_float(b.y);
+}
+
+// Full-wave reductions without LDS: DPP within each 16-lane row (quad
+// permutes, then the half-row and row mirrors, each pairing two groups that
+// already hold equal values), then the row swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i within 16
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return max_over_row_groups(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  x += dpp_f32<kDppRowHalfMirror>(x);
+  x += dpp_f32<kDppRowMirror>(x);
+  return sum_over_row_groups(x);
+}
+
 // 4x4 byte transpose across four dwords: out[k] byte r = in[r] byte k.
 __device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                                    uint32_t& o0, uint32_t& o1, uint32_t& o2,

@@ -43,8 +43,11 @@ namespace {
 #ifndef FP8KV_PREFILL_ROW_BLOCKS
 #define FP8KV_PREFILL_ROW_BLOCKS 1
 #endif
+#ifndef FP8KV_PREFILL_ROWS
+#define FP8KV_PREFILL_ROWS 128
+#endif
 constexpr int kRowBlocks = FP8KV_PREFILL_ROW_BLOCKS;    // 16-row query blocks per wave
-constexpr int kRowsPerWg = 128;
+constexpr int kRowsPerWg = FP8KV_PREFILL_ROWS;
 constexpr int kWaves = kRowsPerWg / (16 * kRowBlocks);
 constexpr int kBlock = kWaves * kWave;
 constexpr int kTileKeys = 64;
@@ -52,7 +55,7 @@ constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 key row
 constexpr int kTileBytes = kTileKeys * kRowBytes;       // 16 KB per tile
 constexpr int kLoadsPerWave = kTileKeys / 4 / kWaves;   // 1 KB (4 rows) per load
 constexpr float kLazyMaxSlack = 8.0f;
-static_assert(kLoadsPerWave * 4 * kWaves == kTileKeys, "a tile is whole 4-row loads");
+static_assert(kLoadsPerWave >= 1 && kLoadsPerWave * 4 * kWaves == kTileKeys, "a tile is whole 4-row loads");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
