@@ -83,6 +83,17 @@ def test_append_agrees_with_quantize_then_decode():
     assert_close(out_b, ref, "two calls")
 
 
+@pytest.mark.parametrize("cap", [1, 3, 8, 64, 256])
+def test_append_split_caps(cap):
+    say(f"decode+append 20,000 context, max_splits={cap}")
+    case = wl.layer_decode(9, ctx=20000, pool_rows=21000)
+    pool = build_pool(case)
+    ref_pools, ref = _oracle_step(case)
+    out = bf16_to_f64(_run_append(pool, case, max_splits=cap))
+    _check_pool(pool, ref_pools, f"cap={cap}")
+    assert_close(out, ref, f"cap={cap}")
+
+
 @pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 64, 65, 129, 1000])
 def test_append_lengths(L):
     say(f"decode+append L={L}")
