@@ -30,9 +30,12 @@
 // and the load latency hides behind the MFMA work.  Online softmax in log2
 // units with a lazy maximum (O and l are rescaled only when a sub-step's
 // maximum exceeds the running one by more than 8), so the accumulators are
-// normally touched by the MFMA alone.  Workgroups with the most keys (the last
+// normally touched by the MFMA alone; the row sums are an MFMA of P against a
+// block of ones, which also normalizes by exactly the bf16 p that P*V uses.  Workgroups with the most keys (the last
 // query tokens) are launched first.
 #include <math.h>
+
+#include <type_traits>
 
 #include "fp8kv_device.h"
 
@@ -72,7 +75,7 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p) {
 }
 
 template <int G>
-__global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ws_k, const uint16_t* __restrict__ ws_v,
     const uint16_t* __restrict__ k_cur, const uint16_t* __restrict__ v_cur, int32_t n_prefix, int32_t n_tokens,
     int32_t n_q_heads, int32_t n_kv_heads, float qk_scale_log2, uint16_t* __restrict__ out) {
@@ -106,17 +109,17 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
     for (int kk = 0; kk < 4; ++kk) qb[cb][kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32 * kk));
   }
 
-  float m_run[kRowBlocks], l_part[kRowBlocks];  // lazy running max of row n (log2 units); lane's row-sum share
-  f32x4 o[kRowBlocks][8];
+  float m_run[kRowBlocks];  // lazy running max of row n (log2 units)
+  f32x4 o[kRowBlocks][8];   // O[row 4j+i][d = 16nb + n]
+  f32x4 lsum[kRowBlocks];   // row sums of bf16(p) (an MFMA against ones): row 4j+i in slot i
 #pragma unroll
   for (int mb = 0; mb < kRowBlocks; ++mb) {
     m_run[mb] = -INFINITY;
-    l_part[mb] = 0.f;
-  }
-#pragma unroll
-  for (int mb = 0; mb < kRowBlocks; ++mb)
+    lsum[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16x8 ones = u4_as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
   const int64_t kv_row = (int64_t)n_kv_heads * kHeadDim;  // elements between tokens
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
@@ -126,11 +129,14 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
   // This lane's share of a tile fetch: load i covers tile-local keys
   // 4(kLoadsPerWave * wave + i) + [0, 4); the lane takes key +(lane >> 4) and
   // the chunk that lands at position (lane & 15) of that key's row.
-  int fkey[kLoadsPerWave], fofs[kLoadsPerWave];
+  // Offsets are unsigned 32-bit bytes from a wave-uniform tile base, so each
+  // load is a scalar base plus one 32-bit lane offset.
+  int fkey[kLoadsPerWave];
+  uint32_t fofs[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
     fkey[i] = 4 * (kLoadsPerWave * wave + i) + (lane >> 4);
-    fofs[i] = fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ (fkey[i] & 15)) << 3);
+    fofs[i] = (uint32_t)(fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ (fkey[i] & 15)) << 3)) * 2u;
   }
   auto fetch = [&](int buf, int u0) {
     uint8_t* kd = k_lds[buf] + kLoadsPerWave * wave * 1024;
@@ -142,8 +148,8 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
       const uint16_t* vb = ((u0 < n_prefix) ? ws_v : v_cur) + base;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
-        g2lds16(kb + fofs[i], kd + i * 1024);
-        g2lds16(vb + fofs[i], vd + i * 1024);
+        g2lds16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(kb) + fofs[i]), kd + i * 1024);
+        g2lds16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vb) + fofs[i]), vd + i * 1024);
       }
     } else {
       // straddles the workspace/chunk boundary or the last visible key; keys
@@ -152,18 +158,30 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int u = min(u0 + fkey[i], n_keys - 1);
         const int64_t off = (u < n_prefix) ? (int64_t)u * kv_row : (int64_t)(u - n_prefix) * kv_row;
-        const int64_t lo = fofs[i] - fkey[i] * (int)kv_row;  // head + chunk part
+        const int64_t lo = (int64_t)(fofs[i] / 2u) - fkey[i] * kv_row;  // head + chunk part (elements)
         g2lds16(((u < n_prefix) ? ws_k : k_cur) + off + lo, kd + i * 1024);
         g2lds16(((u < n_prefix) ? ws_v : v_cur) + off + lo, vd + i * 1024);
       }
     }
   };
 
-  fetch(0, 0);
+  // Per-lane LDS offsets within a tile, fixed for the whole loop, so that the
+  // buffer, the sub-step and the key block enter the reads as immediates.
+  //  K operand, MFMA kk: key 16 kb + n, chunk 4kk + j (d = 32kk + 8j + [0, 8)).
+  //  V operand, block nb: key 4j + (n >> 2) (+32st, +16 for the second read),
+  //  columns 16nb + 4(n & 3) .. +3 (chunk 2nb + ((n & 3) >> 1), half n & 1).
+  int kofs[4], vofs[8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kofs[kk] = chunk_at(n, 4 * kk + j);
+  {
+    const int ka = 4 * j + (n >> 2);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) vofs[nb] = chunk_at(ka, 2 * nb + ((n & 3) >> 1)) + ((n & 1) << 3);
+  }
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  auto tile_body = [&](auto bufc, int tile) {
+    constexpr int buf = decltype(bufc)::value;
     const int u0 = tile * kTileKeys;
-    const int buf = tile & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `tile` have landed (vmcnt 0)
     __syncthreads();                // every wave's have; the other buffer is free
     if (tile + 1 < n_tiles) fetch(buf ^ 1, u0 + kTileKeys);
@@ -173,16 +191,16 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
     const bool tile_mask = (u0 + kTileKeys - 1 > diag) || (u0 + kTileKeys > n_keys);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      // ---- S^T = K * Q^T for keys u0 + 32st + [0, 32), both query-row blocks
+      // ---- S^T = K * Q^T for keys u0 + 32st + [0, 32), every query-row block
       f32x4 s[2][kRowBlocks];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int cb = 0; cb < kRowBlocks; ++cb) s[kb2][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int key = (2 * st + kb2) * 16 + n;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = u4_as_bf16x8(*reinterpret_cast<const uint4*>(kt + chunk_at(key, 4 * kk + j)));  // d = 32kk + 8j + [0, 8)
+          // key (2st + kb2) * 16 + n: (key & 15) == n, so the swizzle is in kofs
+          const bf16x8 a = u4_as_bf16x8(*reinterpret_cast<const uint4*>(kt + kofs[kk] + (2 * st + kb2) * 16 * kRowBytes));
 #pragma unroll
           for (int cb = 0; cb < kRowBlocks; ++cb) s[kb2][cb] = mfma16x16x32(a, qb[cb][kk], s[kb2][cb]);
         }
@@ -213,10 +231,11 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
           const float m_new = fmaxf(m_run[cb], tmax);
           const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 on the first sub-step
           m_run[cb] = m_new;
-          l_part[cb] *= alpha;
           float ai[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lsum[cb][i] *= ai[i];
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
@@ -226,42 +245,44 @@ __global__ __launch_bounds__(kBlock) void prefill_attn_kernel(
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], qk_scale_log2, neg_m));
-        l_part[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pa[cb] = u4_as_bf16x8(make_uint4(f32x2_to_bf16x2(p[0], p[1]), f32x2_to_bf16x2(p[2], p[3]),
                                          f32x2_to_bf16x2(p[4], p[5]), f32x2_to_bf16x2(p[6], p[7])));
+        lsum[cb] = mfma16x16x32(pa[cb], ones, lsum[cb]);
       }
 
       // ---- O += P * V.  B operand of lane (n, j): V[key][16nb + n] for keys
       //      32st + 4j + [0,4) (slots 0..3) and 32st + 16 + 4j + [0,4) (slots
       //      4..7), by two transposing reads: source lane s = n of group j
       //      names key +(s >> 2), columns 16nb + 4(s & 3) .. +3.
-      const int ka = 32 * st + 4 * j + (n >> 2);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const int c = 2 * nb + ((n & 3) >> 1);
-        const int half = (n & 1) << 3;
-        const uint2 b0 = ds_read_tr16(vt + chunk_at(ka, c) + half);
-        const uint2 b1 = ds_read_tr16(vt + chunk_at(ka + 16, c) + half);
+        const uint2 b0 = ds_read_tr16(vt + vofs[nb] + 32 * st * kRowBytes);
+        const uint2 b1 = ds_read_tr16(vt + vofs[nb] + (32 * st + 16) * kRowBytes);
         const bf16x8 bv = u4_as_bf16x8(make_uint4(b0.x, b0.y, b1.x, b1.y));
 #pragma unroll
         for (int cb = 0; cb < kRowBlocks; ++cb) o[cb][nb] = mfma16x16x32(pa[cb], bv, o[cb][nb]);
       }
     }
+  };
+
+  fetch(0, 0);
+  // The tile loop is unrolled by the buffer parity so that LDS offsets are
+  // compile-time constants.
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    tile_body(std::integral_constant<int, 0>{}, tile);
+    if (tile + 1 < n_tiles) tile_body(std::integral_constant<int, 1>{}, tile + 1);
   }
 
   // ---- normalize and store: lane (n, j) holds rows 4j+i of block cb, d = 16nb + n
 #pragma unroll
   for (int cb = 0; cb < kRowBlocks; ++cb) {
-    float l_tot = l_part[cb] + __shfl_xor(l_part[cb], 16);
-    l_tot += __shfl_xor(l_tot, 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(l_tot, 4 * j + i);
       const int rho = (wave * kRowBlocks + cb) * 16 + 4 * j + i;
       const int tok = i0 + rho / G;
       const int head = h0 + rho % G;
       if (tok < n_tokens) {
-        const float inv = 1.0f / li;
+        const float inv = 1.0f / lsum[cb][i];
         uint16_t* dst = out + ((int64_t)tok * n_q_heads + head) * kHeadDim + n;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
