@@ -41,7 +41,10 @@ namespace {
 
 constexpr int kBlock = kDecodeWaves * kWave;
 constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave loads at once
-static_assert(kGroupKeys % kWave == 0, "a group covers whole waves of row indices");
+// Row indices and scales are loaded one key per lane; a 32-key group leaves
+// the upper half-wave reading duplicates into padding.
+constexpr int kRowSlots = (kGroupKeys + kWave - 1) / kWave;
+static_assert(kGroupKeys % kWave == 0 || kGroupKeys == kWave / 2, "a group covers whole or half waves of row indices");
 static_assert(kDecodeTilesPerWave >= 1 && kDecodeTilesPerWave <= 4, "up to four steps in flight per wave");
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 constexpr float kLog2e = 1.4426950408889634f;
@@ -59,7 +62,8 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     uint32_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
     int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
-    int32_t key_trim, int32_t* __restrict__ header, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int32_t key_trim, uint32_t max_row, int32_t* __restrict__ header, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -78,8 +82,8 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   asm volatile("" : "+v"(b_lane));
   const int len_lane = seq_lens[b_lane];
 
-  __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kGroupKeys];
-  __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kGroupKeys];
+  __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kRowSlots * kWave];
+  __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kRowSlots * kWave];
   __shared__ __attribute__((aligned(16))) float sm_o[kDecodeWaves][G][kHeadDim];
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
@@ -91,11 +95,11 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   // They go to LDS before the length is used, which keeps the compiler from
   // sinking the read below the length's wait.
   int k0 = key_begin + wave * kGroupKeys;
-  int rows_in[kGroupKeys / kWave];
+  int rows_in[kRowSlots];
 #pragma unroll
-  for (int c = 0; c < kGroupKeys / kWave; ++c) rows_in[c] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
+  for (int c = 0; c < kRowSlots; ++c) rows_in[c] = (int)min((uint32_t)trow[min(k0 + c * kWave + lane, key_bound - 1)], max_row);
 #pragma unroll
-  for (int c = 0; c < kGroupKeys / kWave; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
+  for (int c = 0; c < kRowSlots; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
 
   // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
   // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
@@ -126,8 +130,8 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     // 1. Row indices of the group's keys through LDS (per-wave region).
     if (!first) {
 #pragma unroll
-      for (int c = 0; c < kGroupKeys / kWave; ++c) {
-        rows_in[c] = trow[min(k0 + c * kWave + lane, key_bound - 1)];
+      for (int c = 0; c < kRowSlots; ++c) {
+        rows_in[c] = (int)min((uint32_t)trow[min(k0 + c * kWave + lane, key_bound - 1)], max_row);
         s_rows[wave][c * kWave + lane] = rows_in[c];
       }
     }
@@ -135,9 +139,9 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
 
     // 2. Scale loads, issued before the code loads: loads complete in issue
     //    order, so writing the scales to LDS waits for them alone.
-    float ksc[kGroupKeys / kWave], vsc[kGroupKeys / kWave];
+    float ksc[kRowSlots], vsc[kRowSlots];
 #pragma unroll
-    for (int c = 0; c < kGroupKeys / kWave; ++c) {
+    for (int c = 0; c < kRowSlots; ++c) {
       const uint32_t row = (uint32_t)rows_in[c];
       const uint64_t off = (uint64_t)row * scale_row_stride + g;
       ksc[c] = k_scales[off];
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < kGroupKeys / kWave; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
+    for (int c = 0; c < kRowSlots; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
     __builtin_amdgcn_wave_barrier();
     const bool tail = k0 + kGroupKeys > key_end;  // wave-uniform: only a request's last group
 
@@ -333,6 +337,7 @@ struct AppendKernelArgs {
   int64_t code_row_stride;
   int64_t scale_row_stride;
   int32_t n_kv_heads;
+  uint32_t max_row;
   float qk_scale_log2;
 };
 
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
     const int h = (int)(bh % n_q_heads);
     g = h / (n_q_heads / app.n_kv_heads);
     if (wave == 0) {
-      slot = app.new_slots[b];
+      slot = min((uint32_t)app.new_slots[b], app.max_row);  // out-of-range slots are clamped, never followed
       k2 = *reinterpret_cast<const uint32_t*>(app.k_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
       v2 = *reinterpret_cast<const uint32_t*>(app.v_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
       q2 = *reinterpret_cast<const uint32_t*>(app.q + bh * kHeadDim + 2 * lane);
@@ -492,7 +497,7 @@ hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batc
                      pool.k_scales, pool.v_scales, (uint32_t)pool.code_row_stride, (uint32_t)pool.scale_row_stride,
                      q, n_q_heads,
                      row_table, table_stride, seq_lens, max_seq_len, geo.n_split, geo.chunk, ws.split_stride,
-                     qk_scale_log2, key_trim, ws.header, ws.part_o, ws.part_lse);
+                     qk_scale_log2, key_trim, (uint32_t)(pool.num_rows - 1), ws.header, ws.part_o, ws.part_lse);
   return hipGetLastError();
 }
 
@@ -525,7 +530,8 @@ hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32
                                       int32_t n_split, const AppendArgs& app, uint16_t* out, hipStream_t stream) {
   const AppendKernelArgs a{app.q, app.k_new, app.v_new, app.new_token_stride, app.new_slots,
                            pool.k_codes, pool.v_codes, pool.k_scales, pool.v_scales,
-                           pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads, app.sm_scale * kLog2e};
+                           pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads,
+                           (uint32_t)(pool.num_rows - 1), app.sm_scale * kLog2e};
   hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0,
                      stream, ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
   return hipGetLastError();

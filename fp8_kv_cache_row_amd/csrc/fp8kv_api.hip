@@ -34,7 +34,7 @@ bool supported_group(int32_t n_q_heads, int32_t n_kv_heads) {
 
 fp8kv_status check_pool(const fp8kv_pool_layer* p) {
   if (!p || !p->k_codes || !p->v_codes || !p->k_scales || !p->v_scales) return FP8KV_ERR_INVALID_ARG;
-  if (p->num_rows <= 0 || p->n_kv_heads <= 0) return FP8KV_ERR_INVALID_ARG;
+  if (p->num_rows <= 0 || p->num_rows > INT32_MAX || p->n_kv_heads <= 0) return FP8KV_ERR_INVALID_ARG;
   if (p->head_dim != FP8KV_HEAD_DIM) return FP8KV_ERR_UNSUPPORTED;
   if (p->code_row_stride < (int64_t)p->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
   if (p->scale_row_stride < p->n_kv_heads) return FP8KV_ERR_INVALID_ARG;
@@ -46,7 +46,7 @@ fp8kv_status check_pool(const fp8kv_pool_layer* p) {
 
 PoolView view_of(const fp8kv_pool_layer* p) {
   return PoolView{p->k_codes, p->v_codes, p->k_scales, p->v_scales, p->code_row_stride, p->scale_row_stride,
-                  p->n_kv_heads};
+                  p->n_kv_heads, p->num_rows};
 }
 
 // Per-device facts, queried once: gfx950 or not, and the compute-unit count.

@@ -7,6 +7,9 @@
 
 namespace fp8kv {
 
+// Row indices read from device memory (table entries, slots, prefix rows) are
+// clamped to [0, num_rows) by every kernel, so no table content can make a
+// kernel address memory outside the pool.
 struct PoolView {
   uint8_t* k_codes;
   uint8_t* v_codes;
@@ -15,6 +18,7 @@ struct PoolView {
   int64_t code_row_stride;   // bytes
   int64_t scale_row_stride;  // floats
   int32_t n_kv_heads;
+  int64_t num_rows;
 };
 
 // Decode launch geometry: each workgroup covers `chunk` consecutive logical

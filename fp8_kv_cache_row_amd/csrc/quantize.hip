@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_token_stride,
     const int32_t* __restrict__ slots, int64_t n_rows, int32_t n_kv_heads, uint8_t* __restrict__ k_codes,
     uint8_t* __restrict__ v_codes, float* __restrict__ k_scales, float* __restrict__ v_scales,
-    int64_t code_row_stride, int64_t scale_row_stride) {
+    int64_t code_row_stride, int64_t scale_row_stride, uint32_t max_row) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
   const int sub = threadIdx.x % kLanesPerRow;
   if (row >= n_rows) return;  // whole 16-lane groups leave together
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
   uint32_t hi = f32x2_to_fp8x2<false>(y[4], y[5], 0u);
   hi = f32x2_to_fp8x2<true>(y[6], y[7], hi);
 
-  const int64_t slot = slots[t];
+  const int64_t slot = min((uint32_t)slots[t], max_row);  // out-of-range slots are clamped, never followed
   uint8_t* dst = (kv ? v_codes : k_codes) + slot * code_row_stride + (int64_t)g * kHeadDim + sub * 8;
   *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
   if (sub == 0) (kv ? v_scales : k_scales)[slot * scale_row_stride + g] = s;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kBlock) void reconstruct_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
     int64_t scale_row_stride, const int32_t* __restrict__ prefix_rows, int64_t n_rows, int32_t n_kv_heads,
-    uint16_t* __restrict__ ws_k, uint16_t* __restrict__ ws_v) {
+    uint32_t max_row, uint16_t* __restrict__ ws_k, uint16_t* __restrict__ ws_v) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
   const int sub = threadIdx.x % kLanesPerRow;
   if (row >= n_rows) return;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void reconstruct_kernel(
   const int64_t jk = row / n_kv_heads;
   const int kv = (int)(jk & 1);
   const int64_t j = jk >> 1;
-  const int64_t prow = prefix_rows[j];
+  const int64_t prow = min((uint32_t)prefix_rows[j], max_row);
 
   const uint8_t* src = (kv ? v_codes : k_codes) + prow * code_row_stride + (int64_t)g * kHeadDim + sub * 8;
   const uint2 c = *reinterpret_cast<const uint2*>(src);
@@ -100,7 +100,8 @@ hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const u
   const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
                      src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
-                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride);
+                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride,
+                     (uint32_t)(pool.num_rows - 1));
   return hipGetLastError();
 }
 
@@ -111,7 +112,8 @@ hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, 
   const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL(reconstruct_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, pool.k_codes,
                      pool.v_codes, pool.k_scales, pool.v_scales, pool.code_row_stride,
-                     pool.scale_row_stride, prefix_rows, n_rows, pool.n_kv_heads, ws_k, ws_v);
+                     pool.scale_row_stride, prefix_rows, n_rows, pool.n_kv_heads, (uint32_t)(pool.num_rows - 1), ws_k,
+                     ws_v);
   return hipGetLastError();
 }
 

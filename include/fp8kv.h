@@ -104,7 +104,8 @@ typedef struct fp8kv_pool_layer {
  *                  src_token_stride elements (>= n_kv_heads*128, a multiple of
  *                  8); bases 16-byte aligned.
  * slots:           device int32 [n_tokens], each in [0, pool->num_rows); slots
- *                  must be distinct within one call.
+ *                  must be distinct within one call.  An out-of-range slot is
+ *                  clamped to num_rows - 1 (never an access outside the pool).
  * n_tokens:        >= 0 (0 is a no-op).
  * Errors: INVALID_ARG (null pointer, bad sizes), UNSUPPORTED, ALIGNMENT, HIP.
  */
@@ -141,12 +142,16 @@ size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t ma
  * split count.
  *
  * q:            device bf16 [batch][n_q_heads][128], contiguous, 16-byte aligned.
- * row_table:    device int32, row b at row_table + b * table_stride.  Every
- *               entry in [0, max_seq_len) must be a physical row of `pool`
- *               holding finite codes and scales (written by
- *               fp8kv_quantize_rows, or zero-filled): entries at or past
- *               seq_lens[b] (padding) are read and then masked out (weight 0),
- *               so they may name any such row, e.g. row 0.
+ * row_table:    device int32, row b at row_table + b * table_stride.
+ *               Entries below seq_lens[b] name the request's rows.  Entries
+ *               in [seq_lens[b], max_seq_len) (padding) are read and masked
+ *               out (weight 0).  Every kernel clamps a row index to
+ *               [0, num_rows) before using it (an out-of-range entry reads
+ *               row num_rows - 1, never memory outside the pool), and the
+ *               row an entry resolves to must hold finite codes and scales
+ *               (written by fp8kv_quantize_rows, or zero-filled): a masked
+ *               key has weight exactly 0, which a NaN value would still
+ *               turn into NaN.
  * seq_lens:     device int32 [batch], each in [0, max_seq_len].
  * max_seq_len:  host-side upper bound on seq_lens (sizes the launch), >= 0,
  *               <= table_stride.
@@ -207,7 +212,7 @@ fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_sp
  *                    multiple of 8 elements and >= n_kv_heads * 128.
  * new_slots:         device int32 [batch], 4-byte aligned: physical rows of
  *                    `pool`, distinct between requests, named by no position
- *                    below p_b of any request.
+ *                    below p_b of any request (clamped like table entries).
  * seq_lens:          device int32 [batch], each in [1, max_seq_len].
  * row_table:         as for fp8kv_decode_attn.
  * Other arguments, the workspace and the errors are those of
@@ -240,7 +245,8 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer *pool, const uint16
  *
  * q:            device bf16 [n_tokens][n_q_heads][128], contiguous.
  * k_cur, v_cur: device bf16 [n_tokens][n_kv_heads][128], contiguous.
- * prefix_rows:  device int32 [n_prefix], physical rows of `pool`.
+ * prefix_rows:  device int32 [n_prefix], physical rows of `pool` (an
+ *               out-of-range entry is clamped to num_rows - 1).
  * ws_k, ws_v:   device bf16, each >= n_prefix * n_kv_heads * 128 elements
  *               (ws_capacity_rows >= n_prefix rows); written by step 1, laid
  *               out [n_prefix][n_kv_heads][128]; may be shared by all layers.

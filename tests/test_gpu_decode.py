@@ -250,3 +250,23 @@ def test_stage1_then_merge_equals_full_call():
         two = fk.fp8kv_decode_merge(ws, 1, case.n_q_heads, max_splits=cap)
         torch.cuda.synchronize()
         assert torch.equal(full.view(torch.int16), two.view(torch.int16)), cap
+
+
+def test_out_of_range_padding_entries_are_clamped():
+    """Padding entries (positions >= seq_lens[b]) holding -1, INT32_MAX or rows
+    past the pool are clamped by the kernels to a real row and masked: the
+    output is bit-identical to the same call with row-0 padding."""
+    say("decode 16 requests with garbage padding entries")
+    case = wl.batched_decode(1, n_req=6, lo=100, hi=3000)
+    pool = build_pool(case)
+    want = run_decode(pool, case)
+    bad = case.table.copy()
+    for b in range(case.batch):
+        L = int(case.seq_lens[b])
+        pad = bad[b, L:]
+        pad[0::3] = -1
+        pad[1::3] = np.iinfo(np.int32).max
+        pad[2::3] = case.pool_rows + 7
+    got = run_decode(pool, case, table=bad)
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    assert_close(bf16_to_f64(got), _oracle_decode(case), "garbage padding")
