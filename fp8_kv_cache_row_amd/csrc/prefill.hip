@@ -16,7 +16,8 @@
 // swaps), and the same registers are the k-slots of the P*V MFMA.
 //
 // K and V tiles (64 keys) are both stored row-major, [key][16 chunks of
-// 16 B], chunk c of key m at position c ^ (m & 15).  They are fetched by
+// 16 B], chunk c of key m at position c ^ (m & 15) for K and c ^ (2m & 15)
+// for V (each conflict-free for the reads it serves).  They are fetched by
 // global-to-LDS loads, which write lane l's 16 bytes at LDS offset 16 l of the
 // instruction's 1 KB (4 key rows): lane l fetches chunk (l & 15) ^ (key & 15)
 // of its key, so the swizzle comes from the gather and no data passes through
@@ -62,8 +63,15 @@ static_assert(kLoadsPerWave >= 1 && kLoadsPerWave * 4 * kWaves == kTileKeys, "a 
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Byte offset of 16-byte chunk c of key m (tile-local) in a tile.
+// Byte offset of 16-byte chunk c of key m (tile-local) in a K tile: position
+// c ^ (m & 15), so the 16 keys of one QK^T operand read (same chunk) hit 16
+// different positions.
 __device__ __forceinline__ int chunk_at(int m, int c) { return m * kRowBytes + ((c ^ (m & 15)) << 4); }
+// The same for a V tile, position c ^ (2m & 15): one transposing read takes
+// chunks 2nb and 2nb+1 of 8 consecutive keys, and doubling the key keeps the
+// 8 position pairs {x, x ^ 1} apart.
+__device__ __forceinline__ int vswz(int m) { return (2 * m) & 15; }
+__device__ __forceinline__ int vchunk_at(int m, int c) { return m * kRowBytes + ((c ^ vswz(m)) << 4); }
 
 __device__ __forceinline__ void g2lds16(const uint16_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
@@ -132,11 +140,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   // Offsets are unsigned 32-bit bytes from a wave-uniform tile base, so each
   // load is a scalar base plus one 32-bit lane offset.
   int fkey[kLoadsPerWave];
-  uint32_t fofs[kLoadsPerWave];
+  uint32_t fofs[kLoadsPerWave], vfofs[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
     fkey[i] = 4 * (kLoadsPerWave * wave + i) + (lane >> 4);
     fofs[i] = (uint32_t)(fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ (fkey[i] & 15)) << 3)) * 2u;
+    vfofs[i] = (uint32_t)(fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ vswz(fkey[i])) << 3)) * 2u;
   }
   auto fetch = [&](int buf, int u0) {
     uint8_t* kd = k_lds[buf] + kLoadsPerWave * wave * 1024;
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         g2lds16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(kb) + fofs[i]), kd + i * 1024);
-        g2lds16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vb) + fofs[i]), vd + i * 1024);
+        g2lds16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vb) + vfofs[i]), vd + i * 1024);
       }
     } else {
       // straddles the workspace/chunk boundary or the last visible key; keys
@@ -158,9 +167,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int u = min(u0 + fkey[i], n_keys - 1);
         const int64_t off = (u < n_prefix) ? (int64_t)u * kv_row : (int64_t)(u - n_prefix) * kv_row;
-        const int64_t lo = (int64_t)(fofs[i] / 2u) - fkey[i] * kv_row;  // head + chunk part (elements)
-        g2lds16(((u < n_prefix) ? ws_k : k_cur) + off + lo, kd + i * 1024);
-        g2lds16(((u < n_prefix) ? ws_v : v_cur) + off + lo, vd + i * 1024);
+        const int64_t klo = (int64_t)(fofs[i] / 2u) - fkey[i] * kv_row;  // head + chunk part (elements)
+        const int64_t vlo = (int64_t)(vfofs[i] / 2u) - fkey[i] * kv_row;
+        g2lds16(((u < n_prefix) ? ws_k : k_cur) + off + klo, kd + i * 1024);
+        g2lds16(((u < n_prefix) ? ws_v : v_cur) + off + vlo, vd + i * 1024);
       }
     }
   };
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   {
     const int ka = 4 * j + (n >> 2);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) vofs[nb] = chunk_at(ka, 2 * nb + ((n & 3) >> 1)) + ((n & 1) << 3);
+    for (int nb = 0; nb < 8; ++nb) vofs[nb] = vchunk_at(ka, 2 * nb + ((n & 3) >> 1)) + ((n & 1) << 3);
   }
 
   auto tile_body = [&](auto bufc, int tile) {
