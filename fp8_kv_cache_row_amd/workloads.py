@@ -12,6 +12,8 @@ Shapes follow the workloads described on the pages:
     GQA 4/8, batch 1, 8K/32K keys, randomized physical slots.
   * FreeToken PR #853, "Paired end-to-end A/B": the 8K historical prefix +
     8K new-token prefill operator.
+  * FreeToken PR #897, "Regression and CUDA isolation": head dims 128 and
+    256, 1/3/8 query rows per request, 17/8,192/32,768 keys.
 
 Values are drawn as float32 from numpy's PCG64 generator and rounded to bf16
 (round to nearest even) by torch's CPU cast; arrays of bf16 are returned as
@@ -46,15 +48,15 @@ def softmax_scale(head_dim: int = HEAD_DIM) -> float:
     return float(np.float32(1.0 / np.sqrt(np.float64(head_dim))))
 
 
-def outlier_channels(rng: np.random.Generator, n_kv_heads: int) -> np.ndarray:
+def outlier_channels(rng: np.random.Generator, n_kv_heads: int, head_dim: int = HEAD_DIM) -> np.ndarray:
     """Per KV head, 4 distinct channels that carry x8 outliers in K."""
-    return np.stack([rng.choice(HEAD_DIM, N_OUTLIER_CHANNELS, replace=False)
+    return np.stack([rng.choice(head_dim, N_OUTLIER_CHANNELS, replace=False)
                      for _ in range(n_kv_heads)]).astype(np.int64)
 
 
 def draw_k(rng: np.random.Generator, n: int, n_kv_heads: int,
-           outliers: Optional[np.ndarray]) -> np.ndarray:
-    x = rng.standard_normal((n, n_kv_heads, HEAD_DIM), dtype=np.float32)
+           outliers: Optional[np.ndarray], head_dim: int = HEAD_DIM) -> np.ndarray:
+    x = rng.standard_normal((n, n_kv_heads, head_dim), dtype=np.float32)
     if outliers is not None:
         for h in range(n_kv_heads):
             x[:, h, outliers[h]] *= np.float32(OUTLIER_GAIN)
@@ -72,10 +74,11 @@ def draw_normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray
 class DecodeCase:
     """One decode-attention call over a page-size-1 FP8 pool.
 
-    k_rows / v_rows: bf16 bits [pool_rows][n_kv_heads][128]; pool row r holds
-    k_rows[r] once quantized.  q: bf16 bits [batch][n_q_heads][128].
+    k_rows / v_rows: bf16 bits [pool_rows][n_kv_heads][D]; pool row r holds
+    k_rows[r] once quantized.  q: bf16 bits [batch][n_q_heads][D], or
+    [batch][n_qrows][n_q_heads][D] for a request's last n_qrows positions.
     table: int32 [batch][table_stride] logical -> physical row map.
-    new_k / new_v (optional): bf16 bits [batch][n_kv_heads][128] of the token
+    new_k / new_v (optional): bf16 bits [batch][n_kv_heads][D] of the token
     written during the step into slot table[b][seq_lens[b]-1].
     """
     name: str
@@ -94,6 +97,14 @@ class DecodeCase:
     @property
     def batch(self) -> int:
         return int(self.q.shape[0])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.q.shape[-1])
+
+    @property
+    def n_qrows(self) -> int:
+        return 1 if self.q.ndim == 3 else int(self.q.shape[1])
 
     @property
     def max_seq_len(self) -> int:
@@ -134,26 +145,36 @@ def tiny_decode(seed: int = 0) -> DecodeCase:
                       softmax_scale())
 
 
+def _draw_q(rng: np.random.Generator, batch: int, n_qrows: int, n_q_heads: int, head_dim: int) -> np.ndarray:
+    """Query rows [batch][n_q_heads][D] (one row) or [batch][n_qrows][n_q_heads][D];
+    one row draws the same numbers as the multi-row shape would."""
+    q = draw_normal(rng, (batch, n_qrows, n_q_heads, head_dim))
+    return q[:, 0] if n_qrows == 1 else q
+
+
 def layer_decode(seed: int = 0, ctx: int = 32768, pool_rows: int = 33059,
-                 n_q_heads: int = 32, n_kv_heads: int = 4, with_new_token: bool = True) -> DecodeCase:
+                 n_q_heads: int = 32, n_kv_heads: int = 4, with_new_token: bool = True,
+                 head_dim: int = HEAD_DIM, n_qrows: int = 1) -> DecodeCase:
     """One layer of batch-1 decode: 32 q / 4 KV heads, 32,768 of 33,059 pool rows.
 
     K ~ N(0,1) with 4 fixed x8 outlier channels per head; V ~ 0.5*N(0,1);
     q ~ N(0,1); table = a seeded permutation of the pool, first `ctx` entries.
     """
     rng = np.random.default_rng(seed)
-    out = outlier_channels(rng, n_kv_heads)
-    k = draw_k(rng, pool_rows, n_kv_heads, out)
-    v = draw_normal(rng, (pool_rows, n_kv_heads, HEAD_DIM), 0.5)
-    q = draw_normal(rng, (1, n_q_heads, HEAD_DIM))
+    out = outlier_channels(rng, n_kv_heads, head_dim)
+    k = draw_k(rng, pool_rows, n_kv_heads, out, head_dim)
+    v = draw_normal(rng, (pool_rows, n_kv_heads, head_dim), 0.5)
+    q = _draw_q(rng, 1, n_qrows, n_q_heads, head_dim)
     table = rng.permutation(pool_rows)[:ctx].astype(np.int32).reshape(1, ctx)
     nk = nv = None
     if with_new_token:
-        nk = bf16_bits(draw_k(rng, 1, n_kv_heads, out))
-        nv = bf16_bits(draw_normal(rng, (1, n_kv_heads, HEAD_DIM), 0.5))
-    return DecodeCase(f"layer_decode_{ctx}", n_q_heads, n_kv_heads, pool_rows,
+        nk = bf16_bits(draw_k(rng, 1, n_kv_heads, out, head_dim))
+        nv = bf16_bits(draw_normal(rng, (1, n_kv_heads, head_dim), 0.5))
+    name = f"layer_decode_{ctx}" + ("" if head_dim == HEAD_DIM else f"_d{head_dim}") + \
+        ("" if n_qrows == 1 else f"_{n_qrows}rows")
+    return DecodeCase(name, n_q_heads, n_kv_heads, pool_rows,
                       bf16_bits(k), bf16_bits(v), bf16_bits(q), table,
-                      np.array([ctx], np.int32), softmax_scale(), nk, nv)
+                      np.array([ctx], np.int32), softmax_scale(head_dim), nk, nv)
 
 
 def model_step_table(seed: int = 0, ctx: int = 40000, pool_rows: int = 40290) -> np.ndarray:
@@ -179,7 +200,8 @@ def model_step_layer(layer: int, table: np.ndarray, seed: int = 0, pool_rows: in
 
 
 def batched_decode(seed: int = 0, n_req: int = 16, lo: int = 1024, hi: int = 32768,
-                   n_q_heads: int = 16, n_kv_heads: int = 4, with_new_token: bool = False) -> DecodeCase:
+                   n_q_heads: int = 16, n_kv_heads: int = 4, with_new_token: bool = False,
+                   head_dim: int = HEAD_DIM, n_qrows: int = 1) -> DecodeCase:
     """16 requests with seeded lengths in [1024, 32768], GQA 4, shared scattered pool.
 
     With new tokens, request b's token goes to table[b][lens[b]-1]; they are
@@ -189,10 +211,10 @@ def batched_decode(seed: int = 0, n_req: int = 16, lo: int = 1024, hi: int = 327
     lens = rng.integers(lo, hi, n_req, endpoint=True).astype(np.int64)
     pool_rows = int(lens.sum())
     perm = rng.permutation(pool_rows).astype(np.int32)
-    out = outlier_channels(rng, n_kv_heads)
-    k = draw_k(rng, pool_rows, n_kv_heads, out)
-    v = draw_normal(rng, (pool_rows, n_kv_heads, HEAD_DIM), 0.5)
-    q = draw_normal(rng, (n_req, n_q_heads, HEAD_DIM))
+    out = outlier_channels(rng, n_kv_heads, head_dim)
+    k = draw_k(rng, pool_rows, n_kv_heads, out, head_dim)
+    v = draw_normal(rng, (pool_rows, n_kv_heads, head_dim), 0.5)
+    q = _draw_q(rng, n_req, n_qrows, n_q_heads, head_dim)
     max_len = int(lens.max())
     table = np.zeros((n_req, max_len), np.int32)
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
@@ -200,11 +222,13 @@ def batched_decode(seed: int = 0, n_req: int = 16, lo: int = 1024, hi: int = 327
         table[b, :lens[b]] = perm[starts[b]:starts[b] + lens[b]]
     nk = nv = None
     if with_new_token:
-        nk = bf16_bits(draw_k(rng, n_req, n_kv_heads, out))
-        nv = bf16_bits(draw_normal(rng, (n_req, n_kv_heads, HEAD_DIM), 0.5))
-    return DecodeCase("batched_gqa4_16req", n_q_heads, n_kv_heads, pool_rows,
+        nk = bf16_bits(draw_k(rng, n_req, n_kv_heads, out, head_dim))
+        nv = bf16_bits(draw_normal(rng, (n_req, n_kv_heads, head_dim), 0.5))
+    name = "batched_gqa4_16req" + ("" if head_dim == HEAD_DIM else f"_d{head_dim}") + \
+        ("" if n_qrows == 1 else f"_{n_qrows}rows")
+    return DecodeCase(name, n_q_heads, n_kv_heads, pool_rows,
                       bf16_bits(k), bf16_bits(v), bf16_bits(q), table,
-                      lens.astype(np.int32), softmax_scale(), nk, nv)
+                      lens.astype(np.int32), softmax_scale(head_dim), nk, nv)
 
 
 def chunked_prefill(seed: int = 0, n_prefix: int = 8192, n_chunk: int = 8192,

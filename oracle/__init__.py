@@ -7,7 +7,9 @@ It shares no code with the HIP path.
 The oracle computes, in plain loops:
   * the OCP E4M3FN codec (decode, round-to-nearest-even saturating encode);
   * per-row quantization: s = fl32(amax/448), codes = encode(fl32(x/s));
-  * decode attention in fp64 over the dequantized page-size-1 pool;
+  * decode attention in fp64 over the dequantized page-size-1 pool, for head
+    dim 128 or 256, one or more causal query rows per request and an
+    optional sliding window;
   * prefill reconstruction bf16_rne(fl32(decode(c)*s)) and fp64 causal
     prefill attention over [workspace prefix ; bf16 chunk];
   * KV byte accounting per token and for the shared bf16 workspace.
@@ -24,7 +26,8 @@ import numpy as np
 from . import build as _build
 
 _lib: Optional[ctypes.CDLL] = None
-HEAD_DIM = 128
+HEAD_DIM = 128        # prefill and the default everywhere
+HEAD_DIMS = (128, 256)  # head dims of the pool, quantize and decode
 
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
@@ -49,13 +52,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
-        L.oracle_quantize_rows.argtypes = [_u16p, _i64, _u8p, _f32p]
-        L.oracle_quantize_rows.restype = None
+        L.oracle_quantize_rows.argtypes = [_u16p, _i64, _i32, _u8p, _f32p]
+        L.oracle_quantize_rows.restype = _i32
         L.oracle_decode_attention.argtypes = [
-            _u16p, _i32, _i32, _i32, _u8p, _u8p, _f32p, _f32p, _i64, _i64,
-            _i32p, _i64, _i32p, ctypes.c_float, _f64p]
-        L.oracle_decode_attention.restype = None
-        L.oracle_reconstruct.argtypes = [_u8p, _f32p, _i64, _i64, _i32, _i32p, _i64, _u16p]
+            _u16p, _i32, _i32, _i32, _i32, _i32, _u8p, _u8p, _f32p, _f32p, _i64, _i64,
+            _i32p, _i64, _i32p, _i32, ctypes.c_float, _f64p]
+        L.oracle_decode_attention.restype = _i32
+        L.oracle_reconstruct.argtypes = [_u8p, _f32p, _i64, _i64, _i32, _i32, _i32p, _i64, _u16p]
         L.oracle_reconstruct.restype = None
         L.oracle_prefill_attention.argtypes = [
             _u16p, _u16p, _u16p, _u16p, _u16p, _i32, _i32, _i32, _i32, ctypes.c_float,
@@ -103,20 +106,21 @@ def f32_to_bf16(x: float) -> int:
 # --------------------------------------------------------------- quantize --
 
 def quantize_rows(rows_bf16: np.ndarray):
-    """rows_bf16: [..., 128] uint16 -> (codes uint8 [..., 128], scales float32 [...])."""
+    """rows_bf16: [..., D] uint16 (D = 128 or 256) -> (codes uint8 [..., D], scales float32 [...])."""
     r = np.ascontiguousarray(rows_bf16, dtype=np.uint16)
     shape = r.shape[:-1]
-    assert r.shape[-1] == HEAD_DIM
+    D = r.shape[-1]
+    assert D in HEAD_DIMS
     n = int(np.prod(shape)) if shape else 1
-    flat = r.reshape(n, HEAD_DIM)
-    codes = np.empty((n, HEAD_DIM), np.uint8)
+    flat = r.reshape(n, D)
+    codes = np.empty((n, D), np.uint8)
     scales = np.empty(n, np.float32)
-    lib().oracle_quantize_rows(flat, n, codes, scales)
-    return codes.reshape(*shape, HEAD_DIM), scales.reshape(shape)
+    assert lib().oracle_quantize_rows(flat, n, D, codes, scales) == 0
+    return codes.reshape(*shape, D), scales.reshape(shape)
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """decode(c) * s in fp64, broadcast over the last (128) axis."""
+    """decode(c) * s in fp64, broadcast over the last (head-dim) axis."""
     t = e4m3_decode_table()
     return t[np.asarray(codes, np.uint8)] * np.asarray(scales, np.float64)[..., None]
 
@@ -124,38 +128,46 @@ def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------- attention --
 
 def decode_attention(q, k_codes, v_codes, k_scales, v_scales, table, seq_lens, sm_scale,
-                     n_kv_heads: int) -> np.ndarray:
+                     n_kv_heads: int, window: int = 0) -> np.ndarray:
     """fp64 decode attention.
 
-    q: uint16 [B][Hq][128]; k_codes/v_codes: uint8 [R][Hkv][128];
-    k_scales/v_scales: float32 [R][Hkv]; table: int32 [B][stride]; seq_lens int32 [B].
-    Returns float64 [B][Hq][128].
+    q: uint16 [B][Hq][D] (one query row per request) or [B][n_qrows][Hq][D]
+    (the request's last n_qrows positions, each causal); D = 128 or 256.
+    k_codes/v_codes: uint8 [R][Hkv][D]; k_scales/v_scales: float32 [R][Hkv];
+    table: int32 [B][stride]; seq_lens int32 [B]; window > 0 limits the query
+    at position p to positions p-window+1 .. p.
+    Returns float64 with q's shape.
     """
     q = np.ascontiguousarray(q, np.uint16)
-    B, Hq, D = q.shape
-    assert D == HEAD_DIM
+    single = q.ndim == 3
+    q4 = q[:, None] if single else q
+    B, NQ, Hq, D = q4.shape
+    assert D in HEAD_DIMS
     kc = np.ascontiguousarray(k_codes, np.uint8)
     vc = np.ascontiguousarray(v_codes, np.uint8)
+    assert kc.shape[-1] == D and vc.shape[-1] == D
     ks = np.ascontiguousarray(k_scales, np.float32)
     vs = np.ascontiguousarray(v_scales, np.float32)
     tb = np.ascontiguousarray(table, np.int32)
     sl = np.ascontiguousarray(seq_lens, np.int32)
-    out = np.zeros((B, Hq, HEAD_DIM), np.float64)
-    lib().oracle_decode_attention(q, B, Hq, n_kv_heads, kc.reshape(-1), vc.reshape(-1),
-                                  ks.reshape(-1), vs.reshape(-1), n_kv_heads * HEAD_DIM,
-                                  n_kv_heads, tb.reshape(-1), tb.shape[1], sl,
-                                  float(sm_scale), out)
-    return out
+    out = np.zeros((B, NQ, Hq, D), np.float64)
+    rc = lib().oracle_decode_attention(np.ascontiguousarray(q4), B, NQ, Hq, n_kv_heads, D,
+                                       kc.reshape(-1), vc.reshape(-1), ks.reshape(-1), vs.reshape(-1),
+                                       n_kv_heads * D, n_kv_heads, tb.reshape(-1), tb.shape[1], sl,
+                                       int(window), float(sm_scale), out)
+    assert rc == 0
+    return out[:, 0] if single else out
 
 
 def reconstruct(codes, scales, rows, n_kv_heads: int) -> np.ndarray:
-    """bf16 workspace [P][Hkv][128] (uint16 bits) for pool rows `rows`."""
+    """bf16 workspace [P][Hkv][D] (uint16 bits) for pool rows `rows`."""
     c = np.ascontiguousarray(codes, np.uint8)
+    D = c.shape[-1]
     s = np.ascontiguousarray(scales, np.float32)
     r = np.ascontiguousarray(rows, np.int32)
-    ws = np.empty((r.size, n_kv_heads, HEAD_DIM), np.uint16)
-    lib().oracle_reconstruct(c.reshape(-1), s.reshape(-1), n_kv_heads * HEAD_DIM, n_kv_heads,
-                             n_kv_heads, r, r.size, ws)
+    ws = np.empty((r.size, n_kv_heads, D), np.uint16)
+    lib().oracle_reconstruct(c.reshape(-1), s.reshape(-1), n_kv_heads * D, n_kv_heads,
+                             n_kv_heads, D, r, r.size, ws)
     return ws
 
 

@@ -42,6 +42,15 @@
  *     the plain softmax(q . K^T * sm_scale) . V in fp64.
  *   - the prefill workspace holds bf16_rne(fl32(decode(c) * s)).
  *   - chunk query i sees every prefix row and chunk rows 0..i.
+ *   - head dim D is 128 or 256 ([897] "Regression and CUDA isolation": the
+ *     comparison matrix covers D128 and D256).
+ *   - a decode request may carry n_qrows query rows (up to 8: [897]
+ *     description, the multi-row decode of #900; 1/3/8 query rows in
+ *     "Regression and CUDA isolation"): they are its last n_qrows positions,
+ *     each causal over the request's rows.
+ *   - a sliding window of W keys ([897] "Regression and CUDA isolation": the
+ *     integration cases include an odd sliding window) lets the query at
+ *     position p see positions p-W+1 .. p.
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off.
  * No fast-math: fp32 divisions and products must be IEEE round-to-nearest.
@@ -59,7 +68,8 @@
 #error "the oracle needs float expressions evaluated in float (FLT_EVAL_METHOD == 0)"
 #endif
 
-#define ORACLE_HEAD_DIM 128
+/* Largest head dim the oracle handles (stack arrays are sized by it). */
+#define ORACLE_MAX_HEAD_DIM 256
 
 /* ---------------------------------------------------------------- bf16 -- */
 
@@ -145,107 +155,127 @@ uint8_t oracle_e4m3_encode(float y) {
 
 /* ---------------------------------------------------------- quantize -- */
 
-/* Quantize one row of 128 bf16 values ([853] "What changes": one FP32 scale
+/* Quantize one row of D bf16 values ([853] "What changes": one FP32 scale
  * per physical K/V row; [280]: dynamic per-token / per-KV-head scale).
  *   amax = max |x|, s = fl32(amax / 448), c_d = encode(fl32(x_d / s)).
  * amax == 0 gives s = 0 and codes that keep the sign of each zero input. */
-static void quantize_row(const uint16_t *x, uint8_t *codes, float *scale) {
-    float xf[ORACLE_HEAD_DIM];
+static void quantize_row(const uint16_t *x, int32_t D, uint8_t *codes, float *scale) {
+    float xf[ORACLE_MAX_HEAD_DIM];
     float amax = 0.0f, s;
     int d;
-    for (d = 0; d < ORACLE_HEAD_DIM; ++d) {
+    for (d = 0; d < D; ++d) {
         xf[d] = bf16_to_float(x[d]);
         if (fabsf(xf[d]) > amax)
             amax = fabsf(xf[d]);
     }
     s = amax / 448.0f;
-    for (d = 0; d < ORACLE_HEAD_DIM; ++d) {
+    for (d = 0; d < D; ++d) {
         float yd = (amax == 0.0f) ? xf[d] : xf[d] / s;
         codes[d] = oracle_e4m3_encode(yd);
     }
     *scale = s;
 }
 
-/* rows: [n_rows][128] bf16 bits, contiguous.  codes: [n_rows][128]; scales: [n_rows]. */
-void oracle_quantize_rows(const uint16_t *rows, int64_t n_rows, uint8_t *codes, float *scales) {
+/* rows: [n_rows][head_dim] bf16 bits, contiguous.  codes: [n_rows][head_dim];
+ * scales: [n_rows].  head_dim in [1, ORACLE_MAX_HEAD_DIM]; returns 0, or -1 for
+ * an unsupported head_dim. */
+int32_t oracle_quantize_rows(const uint16_t *rows, int64_t n_rows, int32_t head_dim, uint8_t *codes,
+                             float *scales) {
     int64_t r;
+    if (head_dim <= 0 || head_dim > ORACLE_MAX_HEAD_DIM)
+        return -1;
 #pragma omp parallel for schedule(static)
     for (r = 0; r < n_rows; ++r)
-        quantize_row(rows + r * ORACLE_HEAD_DIM, codes + r * ORACLE_HEAD_DIM, scales + r);
+        quantize_row(rows + r * head_dim, head_dim, codes + r * head_dim, scales + r);
+    return 0;
 }
 
 /* --------------------------------------------------------- attention -- */
 
-/* Decode attention for one token per request over a page-size-1 FP8 pool
- * ([853] "What changes"; [897] description: BF16 query, D=128, GQA decode).
+/* Decode attention over a page-size-1 FP8 pool ([853] "What changes"; [897]
+ * description: BF16 query, GQA decode over FP8 rows with per-row scales).
  *
- * Pool layout: codes of physical row r, KV head g start at
- *   k_codes + r * code_row_stride + g * 128   (bytes),
+ * Pool layout (D = head_dim): codes of physical row r, KV head g start at
+ *   k_codes + r * code_row_stride + g * D   (bytes),
  * scales at k_scales[r * scale_row_stride + g]; the same for V.
- * q: [batch][n_q_heads][128] bf16 bits.  table: [batch][table_stride] int32.
- * out: [batch][n_q_heads][128] doubles.
+ * q: [batch][n_qrows][n_q_heads][D] bf16 bits.  table: [batch][table_stride].
+ * out: [batch][n_qrows][n_q_heads][D] doubles.
  *
- * For request b and query head h (KV head g = h / (n_q_heads / n_kv_heads)):
+ * Request b holds positions 0 .. L-1 (L = seq_lens[b]) at rows table[b][t].
+ * Its query row i (0 <= i < n_qrows) sits at position p = L - n_qrows + i and
+ * sees positions t with lo <= t <= p, where lo = max(0, p - window + 1) for
+ * window > 0 and lo = 0 otherwise.  For query head h (KV head
+ * g = h / (n_q_heads / n_kv_heads)):
  *   khat_t = decode(k code) * k_scale,  vhat_t = decode(v code) * v_scale (fp64)
  *   z_t    = sm_scale * sum_d q_d * khat_t[d]
  *   out    = sum_t exp(z_t - max z) vhat_t / sum_t exp(z_t - max z)
- * A request with zero rows gets an all-zero output. */
-void oracle_decode_attention(const uint16_t *q, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
-                             const uint8_t *k_codes, const uint8_t *v_codes,
-                             const float *k_scales, const float *v_scales,
-                             int64_t code_row_stride, int64_t scale_row_stride,
-                             const int32_t *table, int64_t table_stride, const int32_t *seq_lens,
-                             float sm_scale, double *out) {
+ * A query row that sees no position (p < 0) gets an all-zero output.
+ * Returns 0, or -1 for an unsupported head_dim. */
+int32_t oracle_decode_attention(const uint16_t *q, int32_t batch, int32_t n_qrows, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim,
+                                const uint8_t *k_codes, const uint8_t *v_codes,
+                                const float *k_scales, const float *v_scales,
+                                int64_t code_row_stride, int64_t scale_row_stride,
+                                const int32_t *table, int64_t table_stride, const int32_t *seq_lens,
+                                int32_t window, float sm_scale, double *out) {
+    const int32_t D = head_dim;
     int32_t group = n_q_heads / n_kv_heads;
-    int64_t bh;
+    int64_t job;
     double lut[256];
     int i;
+    if (D <= 0 || D > ORACLE_MAX_HEAD_DIM)
+        return -1;
     for (i = 0; i < 256; ++i)
         lut[i] = oracle_e4m3_decode((uint8_t)i);
 
 #pragma omp parallel for schedule(dynamic, 1)
-    for (bh = 0; bh < (int64_t)batch * n_q_heads; ++bh) {
-        int32_t b = (int32_t)(bh / n_q_heads), h = (int32_t)(bh % n_q_heads);
+    for (job = 0; job < (int64_t)batch * n_qrows * n_q_heads; ++job) {
+        int32_t h = (int32_t)(job % n_q_heads);
+        int32_t qi = (int32_t)((job / n_q_heads) % n_qrows);
+        int32_t b = (int32_t)(job / ((int64_t)n_q_heads * n_qrows));
         int32_t g = h / group;
-        int64_t L = seq_lens[b], t;
-        double qd[ORACLE_HEAD_DIM], acc[ORACLE_HEAD_DIM];
+        int64_t p = (int64_t)seq_lens[b] - n_qrows + qi, lo = 0, t;
+        double qd[ORACLE_MAX_HEAD_DIM], acc[ORACLE_MAX_HEAD_DIM];
         double *z, zmax = -INFINITY, denom = 0.0;
-        double *o = out + bh * ORACLE_HEAD_DIM;
+        double *o = out + job * D;
         int d;
-        for (d = 0; d < ORACLE_HEAD_DIM; ++d) {
-            qd[d] = (double)bf16_to_float(q[bh * ORACLE_HEAD_DIM + d]);
+        if (window > 0 && p - window + 1 > 0)
+            lo = p - window + 1;
+        for (d = 0; d < D; ++d) {
+            qd[d] = (double)bf16_to_float(q[job * D + d]);
             acc[d] = 0.0;
         }
-        if (L <= 0) {
-            for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+        if (p < 0) {
+            for (d = 0; d < D; ++d)
                 o[d] = 0.0;
             continue;
         }
-        z = (double *)malloc((size_t)L * sizeof(double));
-        for (t = 0; t < L; ++t) {
+        z = (double *)malloc((size_t)(p - lo + 1) * sizeof(double));
+        for (t = lo; t <= p; ++t) {
             int64_t row = table[(int64_t)b * table_stride + t];
-            const uint8_t *kc = k_codes + row * code_row_stride + (int64_t)g * ORACLE_HEAD_DIM;
+            const uint8_t *kc = k_codes + row * code_row_stride + (int64_t)g * D;
             double ks = (double)k_scales[row * scale_row_stride + g];
             double dot = 0.0;
-            for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+            for (d = 0; d < D; ++d)
                 dot += qd[d] * (lut[kc[d]] * ks);
-            z[t] = dot * (double)sm_scale;
-            if (z[t] > zmax)
-                zmax = z[t];
+            z[t - lo] = dot * (double)sm_scale;
+            if (z[t - lo] > zmax)
+                zmax = z[t - lo];
         }
-        for (t = 0; t < L; ++t) {
+        for (t = lo; t <= p; ++t) {
             int64_t row = table[(int64_t)b * table_stride + t];
-            const uint8_t *vc = v_codes + row * code_row_stride + (int64_t)g * ORACLE_HEAD_DIM;
+            const uint8_t *vc = v_codes + row * code_row_stride + (int64_t)g * D;
             double vs = (double)v_scales[row * scale_row_stride + g];
-            double w = exp(z[t] - zmax);
+            double w = exp(z[t - lo] - zmax);
             denom += w;
-            for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+            for (d = 0; d < D; ++d)
                 acc[d] += w * (lut[vc[d]] * vs);
         }
-        for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+        for (d = 0; d < D; ++d)
             o[d] = acc[d] / denom;
         free(z);
     }
+    return 0;
 }
 
 /* --------------------------------------------------------- prefill -- */
@@ -253,9 +283,9 @@ void oracle_decode_attention(const uint16_t *q, int32_t batch, int32_t n_q_heads
 /* Rebuild historical FP8 rows as bf16 ([853] "What changes": historical FP8
  * rows are reconstructed once per layer into one shared BF16 workspace).
  * ws[j][g][d] = bf16_rne(fl32(decode(code) * scale)) for pool row rows[j].
- * ws: [n_rows][n_kv_heads][128] bf16 bits. */
+ * ws: [n_rows][n_kv_heads][head_dim] bf16 bits. */
 void oracle_reconstruct(const uint8_t *codes, const float *scales, int64_t code_row_stride,
-                        int64_t scale_row_stride, int32_t n_kv_heads, const int32_t *rows,
+                        int64_t scale_row_stride, int32_t n_kv_heads, int32_t head_dim, const int32_t *rows,
                         int64_t n_rows, uint16_t *ws) {
     int64_t j;
 #pragma omp parallel for schedule(static)
@@ -264,16 +294,20 @@ void oracle_reconstruct(const uint8_t *codes, const float *scales, int64_t code_
         int32_t g;
         int d;
         for (g = 0; g < n_kv_heads; ++g) {
-            const uint8_t *c = codes + row * code_row_stride + (int64_t)g * ORACLE_HEAD_DIM;
+            const uint8_t *c = codes + row * code_row_stride + (int64_t)g * head_dim;
             float s = scales[row * scale_row_stride + g];
-            uint16_t *w = ws + (j * n_kv_heads + g) * ORACLE_HEAD_DIM;
-            for (d = 0; d < ORACLE_HEAD_DIM; ++d) {
+            uint16_t *w = ws + (j * n_kv_heads + g) * head_dim;
+            for (d = 0; d < head_dim; ++d) {
                 float v = (float)oracle_e4m3_decode(c[d]) * s; /* exact decode, one fp32 rounding */
                 w[d] = float_to_bf16_rne(v);
             }
         }
     }
 }
+
+/* Prefill attention runs at D = 128, the head dim of the pages' prefill
+ * measurements. */
+#define ORACLE_PREFILL_HEAD_DIM 128
 
 /* Chunked-prefill attention ([853] "What changes": the current chunk's K/V stay
  * BF16; historical rows come from the BF16 workspace).
@@ -293,21 +327,21 @@ void oracle_prefill_attention(const uint16_t *q, const uint16_t *ws_k, const uin
         int32_t qi = (int32_t)(job / n_q_heads), h = (int32_t)(job % n_q_heads);
         int32_t i = q_idx[qi], g = h / group;
         int64_t n_keys = (int64_t)n_prefix + i + 1, u;
-        double qd[ORACLE_HEAD_DIM], acc[ORACLE_HEAD_DIM];
+        double qd[ORACLE_PREFILL_HEAD_DIM], acc[ORACLE_PREFILL_HEAD_DIM];
         double *z = (double *)malloc((size_t)n_keys * sizeof(double));
         double zmax = -INFINITY, denom = 0.0;
-        double *o = out + job * ORACLE_HEAD_DIM;
+        double *o = out + job * ORACLE_PREFILL_HEAD_DIM;
         int d;
-        for (d = 0; d < ORACLE_HEAD_DIM; ++d) {
-            qd[d] = (double)bf16_to_float(q[((int64_t)i * n_q_heads + h) * ORACLE_HEAD_DIM + d]);
+        for (d = 0; d < ORACLE_PREFILL_HEAD_DIM; ++d) {
+            qd[d] = (double)bf16_to_float(q[((int64_t)i * n_q_heads + h) * ORACLE_PREFILL_HEAD_DIM + d]);
             acc[d] = 0.0;
         }
         for (u = 0; u < n_keys; ++u) {
             const uint16_t *k = (u < n_prefix)
-                ? ws_k + (u * n_kv_heads + g) * ORACLE_HEAD_DIM
-                : k_cur + ((u - n_prefix) * n_kv_heads + g) * ORACLE_HEAD_DIM;
+                ? ws_k + (u * n_kv_heads + g) * ORACLE_PREFILL_HEAD_DIM
+                : k_cur + ((u - n_prefix) * n_kv_heads + g) * ORACLE_PREFILL_HEAD_DIM;
             double dot = 0.0;
-            for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+            for (d = 0; d < ORACLE_PREFILL_HEAD_DIM; ++d)
                 dot += qd[d] * (double)bf16_to_float(k[d]);
             z[u] = dot * (double)sm_scale;
             if (z[u] > zmax)
@@ -315,14 +349,14 @@ void oracle_prefill_attention(const uint16_t *q, const uint16_t *ws_k, const uin
         }
         for (u = 0; u < n_keys; ++u) {
             const uint16_t *v = (u < n_prefix)
-                ? ws_v + (u * n_kv_heads + g) * ORACLE_HEAD_DIM
-                : v_cur + ((u - n_prefix) * n_kv_heads + g) * ORACLE_HEAD_DIM;
+                ? ws_v + (u * n_kv_heads + g) * ORACLE_PREFILL_HEAD_DIM
+                : v_cur + ((u - n_prefix) * n_kv_heads + g) * ORACLE_PREFILL_HEAD_DIM;
             double w = exp(z[u] - zmax);
             denom += w;
-            for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+            for (d = 0; d < ORACLE_PREFILL_HEAD_DIM; ++d)
                 acc[d] += w * (double)bf16_to_float(v[d]);
         }
-        for (d = 0; d < ORACLE_HEAD_DIM; ++d)
+        for (d = 0; d < ORACLE_PREFILL_HEAD_DIM; ++d)
             o[d] = acc[d] / denom;
         free(z);
     }
