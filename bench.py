@@ -233,7 +233,7 @@ def main():
                                        lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb, sp)
 
     def merge():
-        return lib.fp8kv_decode_merge(1, Hq, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp)
+        return lib.fp8kv_decode_merge(1, Hq, 128, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp)
 
     def decode(p):
         return lib.fp8kv_decode_attn(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,

@@ -1,7 +1,7 @@
 """Thin ctypes binding of libfp8kv.so.
 
-The three calls keep the C names (fp8kv_quantize_rows, fp8kv_decode_attn,
-fp8kv_prefill_attn).  This module only marshals arguments: it takes torch
+The calls keep the C names (fp8kv_quantize_rows, fp8kv_decode_attn,
+fp8kv_decode_attn_rows, fp8kv_decode_attn_append, fp8kv_prefill_attn, ...).  This module only marshals arguments: it takes torch
 device tensors, checks dtypes/shapes that the C ABI cannot see, passes raw
 pointers and the current stream, and raises on a non-OK status.  Every step of
 the computation runs in the library's HIP kernels; there is no fallback.
@@ -18,7 +18,9 @@ from typing import Optional
 
 import torch
 
-HEAD_DIM = 128
+HEAD_DIM = 128           # prefill, and the default pool head dim
+HEAD_DIMS = (128, 256)   # pool / quantize / decode head dims
+MAX_QUERY_ROWS = 8
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8kv.so")
 _HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp8kv.h")
 
@@ -66,16 +68,18 @@ def load() -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.fp8kv_quantize_rows.argtypes = [P, vp, vp, i64, vp, i32, vp]
     L.fp8kv_quantize_rows.restype = ctypes.c_int
-    L.fp8kv_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    L.fp8kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.fp8kv_decode_workspace_bytes.restype = sz
     L.fp8kv_decode_attn.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp, vp]
     L.fp8kv_decode_attn.restype = ctypes.c_int
+    L.fp8kv_decode_attn_rows.argtypes = [P, vp, i32, i32, i32, vp, i64, vp, i32, i32, f32, i32, vp, sz, vp, vp]
+    L.fp8kv_decode_attn_rows.restype = ctypes.c_int
     L.fp8kv_decode_attn_append.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, f32, i32, vp, sz,
                                            vp, vp]
     L.fp8kv_decode_attn_append.restype = ctypes.c_int
     L.fp8kv_decode_stage1.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
     L.fp8kv_decode_stage1.restype = ctypes.c_int
-    L.fp8kv_decode_merge.argtypes = [i32, i32, i32, vp, sz, vp, vp]
+    L.fp8kv_decode_merge.argtypes = [i32, i32, i32, i32, vp, sz, vp, vp]
     L.fp8kv_decode_merge.restype = ctypes.c_int
     L.fp8kv_prefill_attn.argtypes = [P, vp, vp, vp, i32, i32, vp, i32, vp, vp, i64, f32, vp, vp]
     L.fp8kv_prefill_attn.restype = ctypes.c_int
@@ -128,18 +132,19 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
 class Fp8KvPool:
     """One layer of the page-size-1 FP8 row pool, allocated on the current device.
 
-    layout="separate": k_codes/v_codes uint8 [R][Hkv][128], k_scales/v_scales
-      float32 [R][Hkv] (four allocations).
+    layout="separate": k_codes/v_codes uint8 [R][Hkv][D], k_scales/v_scales
+      float32 [R][Hkv] (four allocations); D = head_dim, 128 or 256.
     layout="interleaved": one record per row holding K codes, V codes, K scales,
       V scales back to back (rounded up to 16 bytes), so every byte of a row is
       in one contiguous span.
     """
 
     def __init__(self, num_rows: int, n_kv_heads: int, layout: str = "separate",
-                 device: Optional[torch.device] = None):
+                 device: Optional[torch.device] = None, head_dim: int = HEAD_DIM):
         dev = device or torch.device("cuda", torch.cuda.current_device())
         self.num_rows, self.n_kv_heads, self.layout = int(num_rows), int(n_kv_heads), layout
-        H, D = self.n_kv_heads, HEAD_DIM
+        self.head_dim = int(head_dim)
+        H, D = self.n_kv_heads, self.head_dim
         if layout == "separate":
             self.k_codes = torch.zeros((num_rows, H, D), dtype=torch.uint8, device=dev)
             self.v_codes = torch.zeros((num_rows, H, D), dtype=torch.uint8, device=dev)
@@ -169,7 +174,7 @@ class Fp8KvPool:
         if self.layout == "separate":
             return self.k_scales, self.v_scales
         H = self.n_kv_heads
-        off = 2 * H * HEAD_DIM
+        off = 2 * H * self.head_dim
         ks = self.record[:, off:off + 4 * H].contiguous().view(torch.float32)
         vs = self.record[:, off + 4 * H:off + 8 * H].contiguous().view(torch.float32)
         return ks, vs
@@ -185,17 +190,18 @@ class Fp8KvPool:
 
 def fp8kv_quantize_rows(pool: Fp8KvPool, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor,
                         stream=None) -> None:
-    """Quantize bf16 K/V rows [N][Hkv][128] into pool rows slots[N] (int32)."""
+    """Quantize bf16 K/V rows [N][Hkv][D] into pool rows slots[N] (int32)."""
     _dev_check(k, "k", torch.bfloat16)
     _dev_check(v, "v", torch.bfloat16)
     _dev_check(slots, "slots", torch.int32)
     n = int(slots.numel())
-    if k.shape != v.shape or k.dim() != 3 or k.shape[0] != n or k.shape[1:] != (pool.n_kv_heads, HEAD_DIM):
-        raise ValueError(f"k/v must be [{n}][{pool.n_kv_heads}][{HEAD_DIM}], got {tuple(k.shape)} / {tuple(v.shape)}")
-    if k.stride(2) != 1 or k.stride(1) != HEAD_DIM or v.stride(2) != 1 or v.stride(1) != HEAD_DIM:
-        raise ValueError("k and v need contiguous [Hkv][128] rows")
+    D = pool.head_dim
+    if k.shape != v.shape or k.dim() != 3 or k.shape[0] != n or k.shape[1:] != (pool.n_kv_heads, D):
+        raise ValueError(f"k/v must be [{n}][{pool.n_kv_heads}][{D}], got {tuple(k.shape)} / {tuple(v.shape)}")
+    if k.stride(2) != 1 or k.stride(1) != D or v.stride(2) != 1 or v.stride(1) != D:
+        raise ValueError(f"k and v need contiguous [Hkv][{D}] rows")
     # a single token may carry any token stride (even 0); only token 0 is read
-    stride = k.stride(0) if n > 1 else pool.n_kv_heads * HEAD_DIM
+    stride = k.stride(0) if n > 1 else pool.n_kv_heads * D
     if n > 1 and v.stride(0) != stride:
         raise ValueError("k and v need the same token stride")
     st = load().fp8kv_quantize_rows(ctypes.byref(pool.layer), _ptr(_bits(k)), _ptr(_bits(v)), stride,
@@ -203,46 +209,73 @@ def fp8kv_quantize_rows(pool: Fp8KvPool, k: torch.Tensor, v: torch.Tensor, slots
     _check(st, "fp8kv_quantize_rows")
 
 
-def fp8kv_decode_workspace_bytes(batch: int, n_q_heads: int, max_splits: int = 0) -> int:
-    return int(load().fp8kv_decode_workspace_bytes(batch, n_q_heads, max_splits))
+def fp8kv_decode_workspace_bytes(n_queries: int, n_q_heads: int, head_dim: int = HEAD_DIM,
+                                 max_splits: int = 0) -> int:
+    return int(load().fp8kv_decode_workspace_bytes(n_queries, n_q_heads, head_dim, max_splits))
 
 
-def decode_workspace(batch: int, n_q_heads: int, max_splits: int = 0, device=None) -> torch.Tensor:
-    nbytes = fp8kv_decode_workspace_bytes(batch, n_q_heads, max_splits)
+def decode_workspace(n_queries: int, n_q_heads: int, max_splits: int = 0, device=None,
+                     head_dim: int = HEAD_DIM) -> torch.Tensor:
+    """Workspace for `n_queries` query rows (batch * n_qrows) of n_q_heads heads."""
+    nbytes = fp8kv_decode_workspace_bytes(n_queries, n_q_heads, head_dim, max_splits)
     return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
 
 
-def _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace):
+def _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace, multi=False):
+    """Common marshalling; q is [B][Hq][D] or, with multi, [B][n_qrows][Hq][D]."""
     _dev_check(q, "q", torch.bfloat16)
     _dev_check(row_table, "row_table", torch.int32)
     _dev_check(seq_lens, "seq_lens", torch.int32)
-    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B][Hq][128] bf16 tensor")
-    B, Hq, _ = q.shape
+    D = pool.head_dim
+    want = 4 if multi else 3
+    if q.dim() != want or q.shape[-1] != D or not q.is_contiguous():
+        shape = "[B][n_qrows][Hq]" if multi else "[B][Hq]"
+        raise ValueError(f"q must be a contiguous {shape}[{D}] bf16 tensor")
+    B, Hq = int(q.shape[0]), int(q.shape[-2])
+    nq = int(q.shape[1]) if multi else 1
     if row_table.dim() != 2 or row_table.shape[0] != B or row_table.stride(1) != 1:
         raise ValueError("row_table must be [B][stride] with unit inner stride")
     if seq_lens.numel() != B:
         raise ValueError("seq_lens must have B entries")
     if workspace is None:
-        workspace = decode_workspace(B, Hq, max_splits, q.device)
+        workspace = decode_workspace(B * nq, Hq, max_splits, q.device, D)
     # a size-1 batch dimension may carry any stride (even 0); only row 0 is read
     table_stride = row_table.stride(0) if B > 1 else max(int(row_table.shape[1]), 1)
-    args = [ctypes.byref(pool.layer), _ptr(_bits(q)), B, Hq, _ptr(row_table), table_stride, _ptr(seq_lens),
-            int(max_seq_len), float(sm_scale), int(max_splits), _ptr(workspace),
-            workspace.numel() * workspace.element_size()]
-    return args, workspace
+    return dict(pool=ctypes.byref(pool.layer), q=_ptr(_bits(q)), B=B, nq=nq, Hq=Hq, table=_ptr(row_table),
+                table_stride=table_stride, seq_lens=_ptr(seq_lens), max_seq_len=int(max_seq_len),
+                sm_scale=float(sm_scale), max_splits=int(max_splits), ws=_ptr(workspace),
+                ws_bytes=workspace.numel() * workspace.element_size()), workspace
 
 
 def fp8kv_decode_attn(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
                       max_seq_len: int, sm_scale: float, max_splits: int = 0,
                       workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
-    """Decode attention: q bf16 [B][Hq][128], row_table int32 [B][stride], seq_lens int32 [B]."""
-    args, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
+    """Decode attention: q bf16 [B][Hq][D], row_table int32 [B][stride], seq_lens int32 [B]."""
+    a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
     if out is None:
         out = torch.empty_like(q)
-    st = load().fp8kv_decode_attn(*args, _ptr(_bits(out)), _stream(stream))
+    st = load().fp8kv_decode_attn(a["pool"], a["q"], a["B"], a["Hq"], a["table"], a["table_stride"], a["seq_lens"],
+                                  a["max_seq_len"], a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],
+                                  _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_decode_attn")
+    return out
+
+
+def fp8kv_decode_attn_rows(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                           max_seq_len: int, sm_scale: float, window: int = 0, max_splits: int = 0,
+                           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Decode attention for n_qrows causal query rows per request (q bf16 [B][n_qrows][Hq][D],
+    the request's last n_qrows positions) with an optional sliding window of `window` keys."""
+    a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace,
+                                multi=True)
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().fp8kv_decode_attn_rows(a["pool"], a["q"], a["B"], a["nq"], a["Hq"], a["table"], a["table_stride"],
+                                       a["seq_lens"], a["max_seq_len"], int(window), a["sm_scale"], a["max_splits"],
+                                       a["ws"], a["ws_bytes"], _ptr(_bits(out)), _stream(stream))
+    _check(st, "fp8kv_decode_attn_rows")
     return out
 
 
@@ -251,18 +284,18 @@ def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tens
                              max_seq_len: int, sm_scale: float, max_splits: int = 0,
                              workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                              stream=None) -> torch.Tensor:
-    """One decode step: quantize each request's new token (k_new/v_new bf16 [B][Hkv][128]) into
+    """One decode step: quantize each request's new token (k_new/v_new bf16 [B][Hkv][D]) into
     pool row new_slots[b] (== row_table[b][seq_lens[b] - 1]) and attend over positions [0, seq_lens[b])."""
-    args, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
-    B = q.shape[0]
+    a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
+    B, D = a["B"], pool.head_dim
     _dev_check(k_new, "k_new", torch.bfloat16)
     _dev_check(v_new, "v_new", torch.bfloat16)
-    shape = (B, pool.n_kv_heads, HEAD_DIM)
+    shape = (B, pool.n_kv_heads, D)
     if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
         raise ValueError(f"k_new/v_new must be {list(shape)}, got {tuple(k_new.shape)} / {tuple(v_new.shape)}")
-    if k_new.stride(2) != 1 or k_new.stride(1) != HEAD_DIM or v_new.stride(2) != 1 or v_new.stride(1) != HEAD_DIM:
-        raise ValueError("k_new and v_new need contiguous [Hkv][128] rows")
-    stride = k_new.stride(0) if B > 1 else pool.n_kv_heads * HEAD_DIM
+    if k_new.stride(2) != 1 or k_new.stride(1) != D or v_new.stride(2) != 1 or v_new.stride(1) != D:
+        raise ValueError(f"k_new and v_new need contiguous [Hkv][{D}] rows")
+    stride = k_new.stride(0) if B > 1 else pool.n_kv_heads * D
     if B > 1 and v_new.stride(0) != stride:
         raise ValueError("k_new and v_new need the same token stride")
     _dev_check(new_slots, "new_slots", torch.int32)
@@ -270,8 +303,10 @@ def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tens
         raise ValueError("new_slots must have B entries")
     if out is None:
         out = torch.empty_like(q)
-    st = load().fp8kv_decode_attn_append(*args[:4], _ptr(_bits(k_new)), _ptr(_bits(v_new)), stride,
-                                         _ptr(new_slots), *args[4:], _ptr(_bits(out)), _stream(stream))
+    st = load().fp8kv_decode_attn_append(a["pool"], a["q"], B, a["Hq"], _ptr(_bits(k_new)), _ptr(_bits(v_new)), stride,
+                                         _ptr(new_slots), a["table"], a["table_stride"], a["seq_lens"],
+                                         a["max_seq_len"], a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],
+                                         _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_decode_attn_append")
     return out
 
@@ -280,18 +315,20 @@ def fp8kv_decode_stage1(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tenso
                         max_seq_len: int, sm_scale: float, max_splits: int = 0,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """First (split-K) stage only; returns the workspace holding the partials."""
-    args, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
-    st = load().fp8kv_decode_stage1(*args, _stream(stream))
+    a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
+    st = load().fp8kv_decode_stage1(a["pool"], a["q"], a["B"], a["Hq"], a["table"], a["table_stride"], a["seq_lens"],
+                                    a["max_seq_len"], a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],
+                                    _stream(stream))
     _check(st, "fp8kv_decode_stage1")
     return workspace
 
 
 def fp8kv_decode_merge(workspace: torch.Tensor, batch: int, n_q_heads: int, max_splits: int = 0,
-                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Merge the partials of a preceding fp8kv_decode_stage1 into bf16 out [B][Hq][128]."""
+                       out: Optional[torch.Tensor] = None, stream=None, head_dim: int = HEAD_DIM) -> torch.Tensor:
+    """Merge the partials of a preceding fp8kv_decode_stage1 into bf16 out [B][Hq][D]."""
     if out is None:
-        out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=workspace.device)
-    st = load().fp8kv_decode_merge(batch, n_q_heads, max_splits, _ptr(workspace),
+        out = torch.empty((batch, n_q_heads, head_dim), dtype=torch.bfloat16, device=workspace.device)
+    st = load().fp8kv_decode_merge(batch, n_q_heads, head_dim, max_splits, _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _ptr(_bits(out)),
                                    _stream(stream))
     _check(st, "fp8kv_decode_merge")

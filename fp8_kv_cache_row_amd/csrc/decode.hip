@@ -39,15 +39,12 @@ namespace fp8kv {
 
 namespace {
 
-constexpr int kBlock = kDecodeWaves * kWave;
-constexpr int kGroupKeys = kDecodeTilesPerWave * kDecodeTileKeys;  // keys a wave loads at once
-// Row indices and scales are loaded one key per lane; a 32-key group leaves
-// the upper half-wave reading duplicates into padding.
-constexpr int kRowSlots = (kGroupKeys + kWave - 1) / kWave;
-static_assert(kGroupKeys % kWave == 0 || kGroupKeys == kWave / 2, "a group covers whole or half waves of row indices");
-static_assert(kDecodeTilesPerWave >= 1 && kDecodeTilesPerWave <= 4, "up to four steps in flight per wave");
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 constexpr float kLog2e = 1.4426950408889634f;
+// Running maximum before any visible key: finite, so a column with no visible
+// key in a step gets p = exp2(-inf - kNoMax) = 0 instead of NaN, and far below
+// every real score.
+constexpr float kNoMax = -1.0e30f;
 
 // Key order inside a 32-key step: k-group j of the P*V contraction holds keys
 // 4j..4j+3 (first 16-key MFMA block) and 16+4j..16+4j+3 (second block).
@@ -55,25 +52,78 @@ __device__ __forceinline__ int step_key(int j, int r) { return (r < 4) ? 4 * j +
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int G>
-__global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
+// Compile-time shape of one stage-1 instantiation.
+//   D       head dim (128 or 256).
+//   NT      16-wide column tiles per workgroup.  A column is one (query row i,
+//           query head hh of the group) pair, c = i * G + hh.
+//   MULTI   several query rows per request (columns c >= G exist); otherwise
+//           the columns are the G heads of one row and G is a template value.
+//   WINDOW  a sliding key window: the key range starts at the first row's
+//           lowest visible position, so the table read waits for the length.
+template <int G_, int D_, int NT_, bool MULTI_, bool WINDOW_>
+struct Stage1 {
+  static constexpr int G = G_, D = D_, NT = NT_;
+  static constexpr bool MULTI = MULTI_, WINDOW = WINDOW_;
+  // Registers: NT * D / 16 accumulators of 4 floats each, NT * D / 32 query
+  // operands and one or two steps of codes in flight.  Wide shapes run 4
+  // waves (one per SIMD, 512 registers each) instead of 8.
+  static constexpr int kWaves = (NT * D >= 512) ? 4 : kDecodeWaves;
+  static constexpr int kBlock = kWaves * kWave;
+  static constexpr int kSteps = (D == 128 && NT == 1) ? kDecodeTilesPerWave : 1;  // 32-key steps loaded at once
+  static constexpr int kGroupKeys = kSteps * kDecodeTileKeys;
+  // Row indices and scales are loaded one key per lane; a 32-key group leaves
+  // the upper half-wave reading duplicates into padding.
+  static constexpr int kRowSlots = (kGroupKeys + kWave - 1) / kWave;
+  static constexpr int kKC = D / 64;  // 16-byte K chunks per key and lane
+  static constexpr int kQK = D / 32;  // QK^T MFMAs per 16-key block
+  static constexpr int kVW = D / 64;  // V dwords per key and lane (D / 16 bytes)
+  static constexpr int kNB = D / 16;  // O column blocks: lane column n holds d = kNB * n + nb
+  static constexpr int kPassCols = MULTI ? 16 : G;  // LDS columns per epilogue pass
+  static_assert(D == 128 || D == 256, "head dim 128 or 256");
+  static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
+  static_assert(kGroupKeys % kWave == 0 || kGroupKeys == kWave / 2, "a group covers whole or half waves of row indices");
+  static_assert(kSteps >= 1 && kSteps <= 4, "up to four steps in flight per wave");
+};
+
+template <int W>
+__device__ __forceinline__ void load_v_words(const uint8_t* p, uint32_t (&w)[W]) {
+  if constexpr (W == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    w[0] = t.x;
+    w[1] = t.y;
+  } else {
+    static_assert(W == 4, "8 or 16 bytes of V per key and lane");
+    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    w[0] = t.x;
+    w[1] = t.y;
+    w[2] = t.z;
+    w[3] = t.w;
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, uint32_t code_row_stride,
-    uint32_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads,
+    uint32_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads, int32_t n_qrows, int32_t g_shift,
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
     int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
-    int32_t key_trim, uint32_t max_row, int32_t* __restrict__ header, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
-  static_assert(G >= 1 && G <= 16, "query heads per KV head must fit one 16-wide MFMA tile");
+    int32_t key_trim, int32_t window, int32_t n_col_groups, uint32_t max_row, int32_t* __restrict__ header,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int D = C::D, NT = C::NT, kWaves = C::kWaves, kBlock = C::kBlock;
+  constexpr int kSteps = C::kSteps, kGroupKeys = C::kGroupKeys, kRowSlots = C::kRowSlots;
+  constexpr int kNB = C::kNB, kPassCols = C::kPassCols;
+  // Query heads per KV head: a template value unless several rows share the tiles.
+  const int G = C::MULTI ? (1 << g_shift) : C::G;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n = lane & 15;
   const int j = lane >> 4;
   const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  const int g = C::MULTI ? (int)blockIdx.y / n_col_groups : (int)blockIdx.y;
+  const int cg = C::MULTI ? (int)blockIdx.y - g * n_col_groups : 0;
   const int b = blockIdx.z;
-  const int key_begin = split * chunk;
-  const int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
+  const int n_cols = G * n_qrows;  // columns of this KV head
   const int h0 = g * G;
 
   // The request length as a vector load, issued first: a scalar load would
@@ -82,56 +132,93 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
   asm volatile("" : "+v"(b_lane));
   const int len_lane = seq_lens[b_lane];
 
-  __shared__ __attribute__((aligned(16))) int32_t s_rows[kDecodeWaves][kRowSlots * kWave];
-  __shared__ __attribute__((aligned(16))) float2 s_sc[kDecodeWaves][kRowSlots * kWave];
-  __shared__ __attribute__((aligned(16))) float sm_o[kDecodeWaves][G][kHeadDim];
-  __shared__ float sm_m[kDecodeWaves][16];
-  __shared__ float sm_l[kDecodeWaves][16];
+  __shared__ __attribute__((aligned(16))) int32_t s_rows[kWaves][kRowSlots * kWave];
+  __shared__ __attribute__((aligned(16))) float2 s_sc[kWaves][kRowSlots * kWave];
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][kPassCols][128];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
 
   const int32_t* trow = table + (int64_t)b * table_stride;
-  // Row indices of the first group, read up to the host-side bound before the
-  // length is known.  Every table entry below max_seq_len names a valid row
-  // (padding included), so reading past the request's length is harmless.
-  // They go to LDS before the length is used, which keeps the compiler from
-  // sinking the read below the length's wait.
+  int key_begin = split * chunk;
+  int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
   int k0 = key_begin + wave * kGroupKeys;
   int rows_in[kRowSlots];
+  if constexpr (!C::WINDOW) {
+    // Row indices of the first group, read up to the host-side bound before
+    // the length is known.  Every table entry below max_seq_len names a row
+    // (clamped to the pool), so reading past the request's length is
+    // harmless.  They go to LDS before the length is used, which keeps the
+    // compiler from sinking the read below the length's wait.
 #pragma unroll
-  for (int c = 0; c < kRowSlots; ++c) rows_in[c] = (int)min((uint32_t)trow[min(k0 + c * kWave + lane, key_bound - 1)], max_row);
+    for (int c = 0; c < kRowSlots; ++c)
+      rows_in[c] = (int)min((uint32_t)trow[max(min(k0 + c * kWave + lane, key_bound - 1), 0)], max_row);
 #pragma unroll
-  for (int c = 0; c < kRowSlots; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
+    for (int c = 0; c < kRowSlots; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
+  }
 
-  // Q^T operand: column n = query head h0 + n; for MFMA kk the lane's eight
-  // k-slots are d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).
-  // Columns n >= G repeat head G-1: MFMA outputs never mix columns, so they
-  // only produce values that are never stored, and the loads need no branch
-  // (which would make the waits on the loads issued before them inexact).
-  bf16x8 qb[4];
-  const uint16_t* qrow = q + ((int64_t)b * n_q_heads + h0 + min(n, G - 1)) * kHeadDim + 16 * j;
+  // Q^T operand of tile t: column n is c = (cg * NT + t) * 16 + n (query row
+  // c / G, head h0 + c % G); for MFMA kk the lane's eight k-slots are
+  // d = 64*(kk/2) + 16*j + 8*(kk%2) + [0, 8).  Columns past the last repeat it:
+  // MFMA outputs never mix columns, so they only produce values that are never
+  // stored, and the loads need no branch (which would make the waits on the
+  // loads issued before them inexact).
+  bf16x8 qb[NT][C::kQK];
+  int col_row[NT];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qb[kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * (kk >> 1) + 8 * (kk & 1)));
+  for (int t = 0; t < NT; ++t) {
+    const int c = min((cg * NT + t) * 16 + n, n_cols - 1);
+    const int i = C::MULTI ? (c >> g_shift) : 0;
+    col_row[t] = i;
+    const uint16_t* qrow = q + (((int64_t)b * n_qrows + i) * n_q_heads + h0 + (c - i * G)) * D + 16 * j;
+#pragma unroll
+    for (int kk = 0; kk < C::kQK; ++kk)
+      qb[t][kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * (kk >> 1) + 8 * (kk & 1)));
+  }
 
-  const int L = __builtin_amdgcn_readfirstlane(len_lane) - key_trim;  // keys this stage covers
-  const int key_end = min(key_begin + chunk, L);
+  // Positions: request length len; query row i sits at p_i = len - n_qrows + i
+  // and sees positions [lo_i, p_i] (lo_i = p_i + 1 - window with a window).
+  // With key_trim = 1 (one row) the last position is left to the merge.
+  const int len = min(__builtin_amdgcn_readfirstlane(len_lane), max_seq_len);
+  const int first_end = len - n_qrows + 1 - key_trim;  // end of the first row's keys
+  int last_lo = 0;                                     // largest lowest visible position
+  if constexpr (C::WINDOW) {
+    const int first_lo = max(0, len - n_qrows + 1 - window);
+    last_lo = max(0, len - window);
+    key_begin = first_lo + split * chunk;
+    key_bound = min(key_begin + chunk, len);
+    k0 = key_begin + wave * kGroupKeys;
+  }
+  const int key_end = min(key_begin + chunk, len - key_trim);  // keys this split covers
+  int cend[NT], clo[NT];  // the lane's columns see keys [clo, cend) of this split
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int p = len - n_qrows + col_row[t];
+    cend[t] = min(p + 1 - key_trim, key_end);
+    clo[t] = C::WINDOW ? max(0, p + 1 - window) : 0;
+  }
 
   // Code addresses: row * stride (32 x 32 -> 64-bit) + the lane's bytes.  The
   // offsets stay on the global pointers so the loads are global, not flat.
-  // K: key n of a 16-key block, 16-byte chunks j and 4+j.  V: 8 bytes at d = 8n.
-  const uint8_t* kbase = k_codes + g * kHeadDim + 16 * j;
-  const uint8_t* vbase = v_codes + g * kHeadDim + 8 * n;
+  // K: key n of a 16-key block, 16-byte chunks j + 4c.  V: D/16 bytes at d = (D/16) n.
+  const uint8_t* kbase = k_codes + g * D + 16 * j;
+  const uint8_t* vbase = v_codes + g * D + (D / 16) * n;
 
-  float m_run = -INFINITY;  // running (lazy) max, log2 units, of head n
-  float l_part = 0.0f;      // sum of p for head n over this lane's keys
-  f32x4 o[8];               // O[head 4j+i][d = 8n + nb]
+  float m_run[NT], l_part[NT];  // running (lazy) max in log2 units, and the sum of p, of column n
+  f32x4 o[NT][kNB];             // O[column 4j+i][d = kNB*n + nb]
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = kNoMax;
+    l_part[t] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  for (bool first = true; k0 < key_end; k0 += kDecodeWaves * kGroupKeys, first = false) {
+  for (bool first = true; k0 < key_end; k0 += kWaves * kGroupKeys, first = false) {
     // 1. Row indices of the group's keys through LDS (per-wave region).
-    if (!first) {
+    if (C::WINDOW || !first) {
 #pragma unroll
       for (int c = 0; c < kRowSlots; ++c) {
-        rows_in[c] = (int)min((uint32_t)trow[min(k0 + c * kWave + lane, key_bound - 1)], max_row);
+        rows_in[c] = (int)min((uint32_t)trow[max(min(k0 + c * kWave + lane, key_bound - 1), 0)], max_row);
         s_rows[wave][c * kWave + lane] = rows_in[c];
       }
     }
@@ -150,175 +237,206 @@ __global__ __launch_bounds__(kBlock) void decode_stage1_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. Every code load of the group, in step order.
-    u32x4 kr[kDecodeTilesPerWave][4];
-    uint2 vr[kDecodeTilesPerWave][8];
+    u32x4 kr[kSteps][2][C::kKC];
+    uint32_t vr[kSteps][8][C::kVW];
 #pragma unroll
-    for (int t = 0; t < kDecodeTilesPerWave; ++t) {
+    for (int t = 0; t < kSteps; ++t) {
       const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
       const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
       const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
-      kr[t][0] = *reinterpret_cast<const u32x4*>(kbase + r0);
-      kr[t][1] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64);
-      kr[t][2] = *reinterpret_cast<const u32x4*>(kbase + r1);
-      kr[t][3] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64);
+#pragma unroll
+      for (int c = 0; c < C::kKC; ++c) {
+        kr[t][0][c] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64 * c);
+        kr[t][1][c] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64 * c);
+      }
       const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
       const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
       const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        vr[t][r] = *reinterpret_cast<const uint2*>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride);
+      for (int r = 0; r < 8; ++r) load_v_words(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < kRowSlots; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
     __builtin_amdgcn_wave_barrier();
-    const bool tail = k0 + kGroupKeys > key_end;  // wave-uniform: only a request's last group
+    // Wave-uniform: only groups that reach past the first row's end, or start
+    // below the last row's window start, need per-column masks.
+    const bool masked = (k0 + kGroupKeys > min(first_end, key_end)) || (C::WINDOW && k0 < last_lo);
 
-    // One 32-key step; t is a compile-time constant so kr/vr stay in registers.
-    // Steps are not skipped (no branch the loads could sink into); keys at or
-    // past the length are masked out of the softmax.
-    auto step = [&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      const int t0 = k0 + t * kDecodeTileKeys;
-      // S^T = K * Q^T: lane (n, j) holds chunks j and 4+j of keys n (block 0)
-      // and 16+n (block 1).
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][0].x, kr[t][0].y), qb[0], s0);
-      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][0].z, kr[t][0].w), qb[1], s0);
-      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][1].x, kr[t][1].y), qb[2], s0);
-      s0 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][1].z, kr[t][1].w), qb[3], s0);
-      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][2].x, kr[t][2].y), qb[0], s1);
-      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][2].z, kr[t][2].w), qb[1], s1);
-      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][3].x, kr[t][3].y), qb[2], s1);
-      s1 = mfma16x16x32(fp8x8_to_bf16x8(kr[t][3].z, kr[t][3].w), qb[3], s1);
-      const float2* scp = &s_sc[wave][t * kDecodeTileKeys];
+    // One 32-key step; st is a compile-time constant so kr/vr stay in
+    // registers.  Steps are not skipped (no branch the loads could sink
+    // into); keys a column does not see are masked out of its softmax.
+    auto step = [&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      const int t0 = k0 + st * kDecodeTileKeys;
+      // S^T = K * Q^T: lane (n, j) holds chunks j + 4c of keys n (block 0)
+      // and 16+n (block 1).  Each K operand is widened once for all tiles.
+      f32x4 s0[NT], s1[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s0[t] = s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C::kQK; ++kk) {
+        const u32x4 w0 = kr[st][0][kk >> 1], w1 = kr[st][1][kk >> 1];
+        const bf16x8 a0 = (kk & 1) ? fp8x8_to_bf16x8(w0.z, w0.w) : fp8x8_to_bf16x8(w0.x, w0.y);
+        const bf16x8 a1 = (kk & 1) ? fp8x8_to_bf16x8(w1.z, w1.w) : fp8x8_to_bf16x8(w1.x, w1.y);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          s0[t] = mfma16x16x32(a0, qb[t][kk], s0[t]);
+          s1[t] = mfma16x16x32(a1, qb[t][kk], s1[t]);
+        }
+      }
+      const float2* scp = &s_sc[wave][st * kDecodeTileKeys];
       const float4 c01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
       const float4 c23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
       const float4 c45 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j]);
       const float4 c67 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j + 2]);
 
-      // Scores in log2 units for head n, keys step_key(j, r).
-      float sv[8] = {s0[0] * c01.x, s0[1] * c01.z, s0[2] * c23.x, s0[3] * c23.z,
-                     s1[0] * c45.x, s1[1] * c45.z, s1[2] * c67.x, s1[3] * c67.z};
+      bf16x8 pa[NT];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) sv[r] *= qk_scale_log2;
-      if (tail) {
+      for (int t = 0; t < NT; ++t) {
+        // Scores in log2 units for column n, keys step_key(j, r).
+        float sv[8] = {s0[t][0] * c01.x, s0[t][1] * c01.z, s0[t][2] * c23.x, s0[t][3] * c23.z,
+                       s1[t][0] * c45.x, s1[t][1] * c45.z, s1[t][2] * c67.x, s1[t][3] * c67.z};
 #pragma unroll
-        for (int r = 0; r < 8; ++r) sv[r] = (t0 + step_key(j, r) < key_end) ? sv[r] : -INFINITY;
-      }
-      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tmax = max_over_row_groups(tmax);
+        for (int r = 0; r < 8; ++r) sv[r] *= qk_scale_log2;
+        if (masked) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const int key = t0 + step_key(j, r);
+            const bool vis = key < cend[t] && (!C::WINDOW || key >= clo[t]);
+            sv[r] = vis ? sv[r] : -INFINITY;
+          }
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        tmax = max_over_row_groups(tmax);
 
-      // Lazy maximum: move it (and rescale O and l) only when this step's
-      // maximum exceeds it by more than the slack; otherwise p <= 2^slack.  A
-      // fully masked step has tmax = -inf and leaves the state untouched; the
-      // group's first step always holds key k0 < key_end, so m_run is finite
-      // before any fully masked step.
-      if (__any(tmax > m_run + kLazyMaxSlack)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_part *= alpha;
-        float ai[4];
+        // Lazy maximum: move it (and rescale O and l) only when this step's
+        // maximum exceeds it by more than the slack; otherwise p <= 2^slack.
+        // A column with no visible key keeps m_run = kNoMax and gets p = 0.
+        if (__any(tmax > m_run[t] + kLazyMaxSlack)) {
+          const float m_new = fmaxf(m_run[t], tmax);
+          const float alpha = fast_exp2(m_run[t] - m_new);
+          m_run[t] = m_new;
+          l_part[t] *= alpha;
+          float ai[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+          for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
+          for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[nb][i] *= ai[i];
+            for (int i = 0; i < 4; ++i) o[t][nb][i] *= ai[i];
+          }
+        }
+
+        float p[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) p[r] = fast_exp2(sv[r] - m_run[t]);
+        l_part[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        // P' = p * v_scale as the bf16 A operand (row = column n, k-slots = keys).
+        const uint4 pu = make_uint4(f32x2_to_bf16x2(p[0] * c01.y, p[1] * c01.w), f32x2_to_bf16x2(p[2] * c23.y, p[3] * c23.w),
+                                    f32x2_to_bf16x2(p[4] * c45.y, p[5] * c45.w), f32x2_to_bf16x2(p[6] * c67.y, p[7] * c67.w));
+        pa[t] = u4_as_bf16x8(pu);
+      }
+
+      // 4. V operand for column block nb: byte nb of each key's D/16 bytes,
+      //    i.e. V[key][d = kNB*n + nb] for the lane's 8 keys (byte-transposed
+      //    in registers), shared by all tiles.
+#pragma unroll
+      for (int w = 0; w < C::kVW; ++w) {
+        uint32_t lo[4], hi[4];
+        transpose4x4_bytes(vr[st][0][w], vr[st][1][w], vr[st][2][w], vr[st][3][w], lo[0], lo[1], lo[2], lo[3]);
+        transpose4x4_bytes(vr[st][4][w], vr[st][5][w], vr[st][6][w], vr[st][7][w], hi[0], hi[1], hi[2], hi[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x8 vb = fp8x8_to_bf16x8(lo[e], hi[e]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o[t][4 * w + e] = mfma16x16x32(pa[t], vb, o[t][4 * w + e]);
         }
       }
-
-      float p[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) p[r] = fast_exp2(sv[r] - m_run);
-      l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      // P' = p * v_scale as the bf16 A operand (row = head n, k-slots = keys).
-      const uint4 pu = make_uint4(f32x2_to_bf16x2(p[0] * c01.y, p[1] * c01.w), f32x2_to_bf16x2(p[2] * c23.y, p[3] * c23.w),
-                                  f32x2_to_bf16x2(p[4] * c45.y, p[5] * c45.w), f32x2_to_bf16x2(p[6] * c67.y, p[7] * c67.w));
-      const bf16x8 pa = u4_as_bf16x8(pu);
-
-      // 4. V operand for N-block nb: byte nb of each key's 8 bytes, i.e.
-      //    V[key][d = 8n + nb] for the lane's 8 keys (byte-transposed in registers).
-      uint32_t lo[8], hi[8];
-      transpose4x4_bytes(vr[t][0].x, vr[t][1].x, vr[t][2].x, vr[t][3].x, lo[0], lo[1], lo[2], lo[3]);
-      transpose4x4_bytes(vr[t][4].x, vr[t][5].x, vr[t][6].x, vr[t][7].x, hi[0], hi[1], hi[2], hi[3]);
-      transpose4x4_bytes(vr[t][0].y, vr[t][1].y, vr[t][2].y, vr[t][3].y, lo[4], lo[5], lo[6], lo[7]);
-      transpose4x4_bytes(vr[t][4].y, vr[t][5].y, vr[t][6].y, vr[t][7].y, hi[4], hi[5], hi[6], hi[7]);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[nb] = mfma16x16x32(pa, fp8x8_to_bf16x8(lo[nb], hi[nb]), o[nb]);
     };
     step(std::integral_constant<int, 0>{});
-    if constexpr (kDecodeTilesPerWave > 1) step(std::integral_constant<int, 1>{});
-    if constexpr (kDecodeTilesPerWave > 2) step(std::integral_constant<int, 2>{});
-    if constexpr (kDecodeTilesPerWave > 3) step(std::integral_constant<int, 3>{});
+    if constexpr (kSteps > 1) step(std::integral_constant<int, 1>{});
+    if constexpr (kSteps > 2) step(std::integral_constant<int, 2>{});
+    if constexpr (kSteps > 3) step(std::integral_constant<int, 3>{});
     __builtin_amdgcn_wave_barrier();  // this group's LDS is consumed before the next overwrites it
   }
 
-  // Per-head totals of this wave.
-  const float l_tot = sum_over_row_groups(l_part);
-
-  if (j == 0) {
-    sm_m[wave][n] = m_run;
-    sm_l[wave][n] = l_tot;
-  }
+  // Merge the waves of this workgroup into one partial per column, one pass
+  // per (tile, 128 of the D columns of O).  In pass half, LDS column
+  // d' = 8 n' + e holds d = kNB n' + 8 half + e.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int head = 4 * j + i;
-    if (head < G) {
-      float* dst = &sm_o[wave][head][8 * n];
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
-    }
-  }
-  __syncthreads();
-
-  // Merge the waves of this workgroup into one partial per query head; a
-  // thread produces 4 consecutive d of one head.
-  for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kBlock) {
-    const int h = idx / (kHeadDim / 4);
-    const int d = 4 * (idx % (kHeadDim / 4));
-    float M = -INFINITY;
+  for (int t = 0; t < NT; ++t) {
+    const float l_tot = sum_over_row_groups(l_part[t]);
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f;
-    if (M != -INFINITY) {
+    for (int half = 0; half < D / 128; ++half) {
+      if (t + half > 0) __syncthreads();  // the previous pass has read LDS
+      if (j == 0 && n < kPassCols) {
+        sm_m[wave][n] = m_run[t];
+        sm_l[wave][n] = l_tot;
+      }
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float wt = fast_exp2(sm_m[w][h] - M);
-        const float4 v = *reinterpret_cast<const float4*>(&sm_o[w][h][d]);
-        num.x += wt * v.x;
-        num.y += wt * v.y;
-        num.z += wt * v.z;
-        num.w += wt * v.w;
-        den += wt * sm_l[w][h];
+      for (int i = 0; i < 4; ++i) {
+        const int col = 4 * j + i;
+        if (col < kPassCols) {
+          float* dst = &sm_o[wave][col][8 * n];
+          const int e0 = 8 * half;
+          *reinterpret_cast<float4*>(dst) = make_float4(o[t][e0][i], o[t][e0 + 1][i], o[t][e0 + 2][i], o[t][e0 + 3][i]);
+          *reinterpret_cast<float4*>(dst + 4) =
+              make_float4(o[t][e0 + 4][i], o[t][e0 + 5][i], o[t][e0 + 6][i], o[t][e0 + 7][i]);
+        }
+      }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < kPassCols * 32; idx += kBlock) {
+        const int col = idx >> 5;
+        const int c = (cg * NT + t) * 16 + col;
+        if (c >= n_cols) continue;
+        const int i = C::MULTI ? (c >> g_shift) : 0;
+        const int dp = 4 * (idx & 31);
+        const int d = kNB * (dp >> 3) + 8 * half + (dp & 7);
+        float M = sm_m[0][col];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][col]);
+        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float wt = fast_exp2(sm_m[w][col] - M);
+          const float4 v = *reinterpret_cast<const float4*>(&sm_o[w][col][dp]);
+          num.x += wt * v.x;
+          num.y += wt * v.y;
+          num.z += wt * v.z;
+          num.w += wt * v.w;
+          den += wt * sm_l[w][col];
+        }
+        const float inv = (den > 0.f) ? 1.0f / den : 0.0f;
+        const int64_t bh = ((int64_t)b * n_qrows + i) * n_q_heads + h0 + (c - i * G);
+        const int64_t ph = bh * split_stride + split;
+        *reinterpret_cast<float4*>(part_o + ph * D + d) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+        if (half == 0 && dp == 0) part_lse[ph] = (den > 0.f) ? M + log2f(den) : -INFINITY;
       }
     }
-    const float inv = (den > 0.f) ? 1.0f / den : 0.0f;
-    const int64_t ph = ((int64_t)b * n_q_heads + h0 + h) * split_stride + split;
-    *reinterpret_cast<float4*>(part_o + ph * kHeadDim + d) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
-    if (d == 0) part_lse[ph] = (den > 0.f) ? M + log2f(den) : -INFINITY;
   }
   // The split count for a merge launched without one.  Written last: a branch
   // at the top would split the entry block and serialize the argument loads
   // ahead of the first table read.
-  if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
+  if (split == 0 && blockIdx.y == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 }
 
 // Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) over the
-// splits of (b, h).  One workgroup per (request, query head); wave w takes
-// splits w, w+4, ...: it loads their lse and o vectors together (clamped
-// indices, no branches), keeps its own maximum, and the four waves combine
-// through LDS -- a single memory round trip.
+// splits of (b, h).  One workgroup per (request, query row, query head); wave w
+// takes splits w, w+4, ...: it loads their lse and o vectors together
+// (clamped indices, no branches), keeps its own maximum, and the four waves
+// combine through LDS -- a single memory round trip.  Lane l owns
+// d = E*l .. E*l + E-1 (E = D / 64).
 //
-// With APPEND, wave 0 also takes the request's new token (position
-// seq_lens[b] - 1, left out of stage 1): it quantizes the bf16 K and V rows of
-// the head group exactly as the quantize-on-write kernel does (same codec
-// functions), scores q against the decoded codes, and folds the token in as a
-// single-key partial (o = s_v * decode(v), lse = the score).  The workgroup of
-// the group's first query head writes the codes and scales to the token's row
-// new_slots[b]; every load of the kernel is independent (one round trip).
+// With APPEND (one query row per request), wave 0 also takes the request's
+// new token (position seq_lens[b] - 1, left out of stage 1): it quantizes the
+// bf16 K and V rows of the head group exactly as the quantize-on-write kernel
+// does (same codec functions), scores q against the decoded codes, and folds
+// the token in as a single-key partial (o = s_v * decode(v), lse = the score).
+// The workgroup of the group's first query head writes the codes and scales
+// to the token's row new_slots[b]; every load of the kernel is independent
+// (one round trip).
 constexpr int kMergeBlock = 256;
 constexpr int kMergeWaves = kMergeBlock / kWave;
 constexpr int kMergeBatch = 16;  // splits per wave loaded at once
@@ -341,25 +459,35 @@ struct AppendKernelArgs {
   float qk_scale_log2;
 };
 
-template <bool APPEND>
+// E consecutive values per lane: bf16 bit patterns in E/2 dwords, fp32 in a vector.
+template <int E>
+struct LaneVec {
+  typedef float F __attribute__((ext_vector_type(E)));
+  typedef uint32_t U __attribute__((ext_vector_type(E / 2)));
+};
+
+template <int D, bool APPEND>
 __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t* __restrict__ header,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_lse,
                                                                   int32_t split_stride, int32_t n_split_arg,
                                                                   int32_t n_q_heads, AppendKernelArgs app,
                                                                   uint16_t* __restrict__ out) {
+  constexpr int E = D / kWave;
+  typedef typename LaneVec<E>::F vecf;
+  typedef typename LaneVec<E>::U vecu;
   __shared__ float s_m[kMergeWaves];
   __shared__ float s_den[kMergeWaves];
-  __shared__ float2 s_acc[kMergeWaves][kWave];
+  __shared__ vecf s_acc[kMergeWaves][kWave];
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n_split = n_split_arg >= 0 ? n_split_arg : header[0];
   const float* lse_p = part_lse + bh * split_stride;
-  const float* po = part_o + bh * split_stride * kHeadDim + 2 * lane;
+  const float* po = part_o + bh * split_stride * D + E * lane;
 
-  // The new token's inputs: its bf16 K/V pair at d = 2*lane, 2*lane + 1, and q.
-  uint32_t k2 = 0u, v2 = 0u, q2 = 0u;
+  // The new token's inputs: its bf16 K/V values at d = E*lane + [0, E), and q.
+  vecu k2 = {}, v2 = {}, q2 = {};
   int64_t slot = 0;
   int64_t b = 0, g = 0;
   if constexpr (APPEND) {
@@ -368,24 +496,24 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
     g = h / (n_q_heads / app.n_kv_heads);
     if (wave == 0) {
       slot = min((uint32_t)app.new_slots[b], app.max_row);  // out-of-range slots are clamped, never followed
-      k2 = *reinterpret_cast<const uint32_t*>(app.k_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
-      v2 = *reinterpret_cast<const uint32_t*>(app.v_new + b * app.new_token_stride + g * kHeadDim + 2 * lane);
-      q2 = *reinterpret_cast<const uint32_t*>(app.q + bh * kHeadDim + 2 * lane);
+      k2 = *reinterpret_cast<const vecu*>(app.k_new + b * app.new_token_stride + g * D + E * lane);
+      v2 = *reinterpret_cast<const vecu*>(app.v_new + b * app.new_token_stride + g * D + E * lane);
+      q2 = *reinterpret_cast<const vecu*>(app.q + bh * D + E * lane);
     }
   }
 
   float m_w = -INFINITY, den = 0.f;
-  float2 acc = make_float2(0.f, 0.f);
+  vecf acc = {};
   // One batch of splits: wave w takes splits base + w + 4i, loaded together
   // (clamped indices, no branches) and folded into (m_w, den, acc).
   float lr[kMergeBatch];
-  float2 v[kMergeBatch];
+  vecf v[kMergeBatch];
   auto load_batch = [&](int base) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const int sidx = min(base + wave + kMergeWaves * i, n_split - 1);
       lr[i] = lse_p[sidx];
-      v[i] = *reinterpret_cast<const float2*>(po + (int64_t)sidx * kHeadDim);
+      v[i] = *reinterpret_cast<const vecf*>(po + (int64_t)sidx * D);
     }
   };
   auto fold_batch = [&](int base) {
@@ -397,15 +525,13 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
     }
     if (mx != -INFINITY) {
       const float a = __builtin_amdgcn_exp2f(m_w - mx);  // 0 when m_w is -inf
-      acc.x *= a;
-      acc.y *= a;
+      acc *= a;
       den *= a;
       m_w = mx;
 #pragma unroll
       for (int i = 0; i < kMergeBatch; ++i) {
         const float w = __builtin_amdgcn_exp2f(lr[i] - m_w);
-        acc.x += w * v[i].x;
-        acc.y += w * v[i].y;
+        acc += w * v[i];
         den += w;
       }
     }
@@ -413,28 +539,58 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   load_batch(0);  // in flight while wave 0 quantizes and scores the new token
 
   float lse_new = -INFINITY;
-  float2 o_new = make_float2(0.f, 0.f);
+  vecf o_new = {};
   if constexpr (APPEND) {
     if (wave == 0) {
-      // Quantize the K and V rows (128 values over the wave, two per lane).
-      const float kx0 = bf16lo_to_f32(k2), kx1 = bf16hi_to_f32(k2);
-      const float vx0 = bf16lo_to_f32(v2), vx1 = bf16hi_to_f32(v2);
-      const float ka = wave_max(fmaxf(fabsf(kx0), fabsf(kx1)));
-      const float va = wave_max(fmaxf(fabsf(vx0), fabsf(vx1)));
+      // Quantize the K and V rows (D values over the wave, E per lane).
+      float kx[E], vx[E], qx[E];
+      float ka = 0.f, va = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        kx[e] = bf16lo_to_f32(k2[e / 2]);
+        kx[e + 1] = bf16hi_to_f32(k2[e / 2]);
+        vx[e] = bf16lo_to_f32(v2[e / 2]);
+        vx[e + 1] = bf16hi_to_f32(v2[e / 2]);
+        qx[e] = bf16lo_to_f32(q2[e / 2]);
+        qx[e + 1] = bf16hi_to_f32(q2[e / 2]);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ka = fmaxf(ka, fabsf(kx[e]));
+        va = fmaxf(va, fabsf(vx[e]));
+      }
+      ka = wave_max(ka);
+      va = wave_max(va);
       const float sk = e4m3_row_scale(ka), sv = e4m3_row_scale(va);
-      const uint32_t kc = f32x2_to_fp8x2<false>(e4m3_prescaled(kx0, ka, sk), e4m3_prescaled(kx1, ka, sk), 0u);
-      const uint32_t vc = f32x2_to_fp8x2<false>(e4m3_prescaled(vx0, va, sv), e4m3_prescaled(vx1, va, sv), 0u);
+      uint32_t kc = 0u, vc = 0u;  // E codes, byte e = element e
+      kc = f32x2_to_fp8x2<false>(e4m3_prescaled(kx[0], ka, sk), e4m3_prescaled(kx[1], ka, sk), kc);
+      vc = f32x2_to_fp8x2<false>(e4m3_prescaled(vx[0], va, sv), e4m3_prescaled(vx[1], va, sv), vc);
+      if constexpr (E == 4) {
+        kc = f32x2_to_fp8x2<true>(e4m3_prescaled(kx[2], ka, sk), e4m3_prescaled(kx[3], ka, sk), kc);
+        vc = f32x2_to_fp8x2<true>(e4m3_prescaled(vx[2], va, sv), e4m3_prescaled(vx[3], va, sv), vc);
+      }
       // Score and value from the decoded codes, as stage 1 sees every other row.
       float kd[4], vd[4];
       fp8x4_to_f32x4(kc, kd);
       fp8x4_to_f32x4(vc, vd);
-      const float dot = wave_sum(bf16lo_to_f32(q2) * kd[0] + bf16hi_to_f32(q2) * kd[1]);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part += qx[e] * kd[e];
+      const float dot = wave_sum(part);
       lse_new = dot * sk * app.qk_scale_log2;
-      o_new = make_float2(vd[0] * sv, vd[1] * sv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o_new[e] = vd[e] * sv;
       // One workgroup per (request, KV head) stores the row.
       if ((bh % n_q_heads) % (n_q_heads / app.n_kv_heads) == 0) {
-        *reinterpret_cast<uint16_t*>(app.k_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)kc;
-        *reinterpret_cast<uint16_t*>(app.v_codes + slot * app.code_row_stride + g * kHeadDim + 2 * lane) = (uint16_t)vc;
+        uint8_t* kdst = app.k_codes + slot * app.code_row_stride + g * D + E * lane;
+        uint8_t* vdst = app.v_codes + slot * app.code_row_stride + g * D + E * lane;
+        if constexpr (E == 2) {
+          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
+          *reinterpret_cast<uint16_t*>(vdst) = (uint16_t)vc;
+        } else {
+          *reinterpret_cast<uint32_t*>(kdst) = kc;
+          *reinterpret_cast<uint32_t*>(vdst) = vc;
+        }
         if (lane == 0) {
           app.k_scales[slot * app.scale_row_stride + g] = sk;
           app.v_scales[slot * app.scale_row_stride + g] = sv;
@@ -454,8 +610,7 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
       const float mx = fmaxf(m_w, lse_new);
       const float a = __builtin_amdgcn_exp2f(m_w - mx);
       const float w = __builtin_amdgcn_exp2f(lse_new - mx);
-      acc.x = acc.x * a + w * o_new.x;
-      acc.y = acc.y * a + w * o_new.y;
+      acc = acc * a + w * o_new;
       den = den * a + w;
       m_w = mx;
     }
@@ -471,59 +626,108 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
     float M = s_m[0];
 #pragma unroll
     for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_m[w]);
-    float2 t = make_float2(0.f, 0.f);
+    vecf t = {};
     float d = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kMergeWaves; ++w) {
         const float a = __builtin_amdgcn_exp2f(s_m[w] - M);
-        t.x += a * s_acc[w][lane].x;
-        t.y += a * s_acc[w][lane].y;
+        t += a * s_acc[w][lane];
         d += a * s_den[w];
       }
     }
     const float inv = (d > 0.f) ? 1.0f / d : 0.0f;
-    *reinterpret_cast<uint32_t*>(out + bh * kHeadDim + 2 * lane) = f32x2_to_bf16x2(t.x * inv, t.y * inv);
+    vecu r;
+#pragma unroll
+    for (int e = 0; e < E; e += 2) r[e / 2] = f32x2_to_bf16x2(t[e] * inv, t[e + 1] * inv);
+    *reinterpret_cast<vecu*>(out + bh * D + E * lane) = r;
   }
 }
 
-template <int G>
-hipError_t launch_stage1_g(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                           const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                           int32_t max_seq_len, float qk_scale_log2, const DecodeGeometry& geo, const DecodeWorkspace& ws,
-                           int32_t key_trim, hipStream_t stream) {
-  dim3 grid((unsigned)geo.n_split, (unsigned)pool.n_kv_heads, (unsigned)batch);
-  hipLaunchKernelGGL(decode_stage1_kernel<G>, grid, dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
+template <class C>
+hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk_scale_log2,
+                             const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim, hipStream_t stream) {
+  dim3 grid((unsigned)geo.n_split, (unsigned)(pool.n_kv_heads * geo.n_col_groups), (unsigned)sh.batch);
+  int g_shift = 0;
+  while ((1 << g_shift) < sh.n_q_heads / pool.n_kv_heads) ++g_shift;
+  hipLaunchKernelGGL(decode_stage1_kernel<C>, grid, dim3(C::kBlock), 0, stream, pool.k_codes, pool.v_codes,
                      pool.k_scales, pool.v_scales, (uint32_t)pool.code_row_stride, (uint32_t)pool.scale_row_stride,
-                     q, n_q_heads,
-                     row_table, table_stride, seq_lens, max_seq_len, geo.n_split, geo.chunk, ws.split_stride,
-                     qk_scale_log2, key_trim, (uint32_t)(pool.num_rows - 1), ws.header, ws.part_o, ws.part_lse);
+                     q, sh.n_q_heads, sh.n_qrows, g_shift, sh.row_table, sh.table_stride, sh.seq_lens, sh.max_seq_len,
+                     geo.n_split, geo.chunk, ws.split_stride, qk_scale_log2, key_trim, sh.window, geo.n_col_groups,
+                     (uint32_t)(pool.num_rows - 1), ws.header, ws.part_o, ws.part_lse);
+  return hipGetLastError();
+}
+
+// One row per request: G is a template value.
+template <int D, bool WINDOW>
+hipError_t launch_stage1_single(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
+                                const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
+                                hipStream_t stream) {
+  switch (sh.n_q_heads / pool.n_kv_heads) {
+    case 1: return launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 2: return launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 4: return launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 8: return launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 16: return launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Several rows per request: NT column tiles per workgroup, G at run time.
+template <int D, bool WINDOW>
+hipError_t launch_stage1_multi(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
+                               const DecodeGeometry& geo, const DecodeWorkspace& ws, hipStream_t stream) {
+  switch (geo.col_tiles) {
+    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW>>(pool, q, sh, qk, geo, ws, 0, stream);
+    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW>>(pool, q, sh, qk, geo, ws, 0, stream);
+    case 4:
+      if constexpr (D == 128) return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW>>(pool, q, sh, qk, geo, ws, 0, stream);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_merge_d(int64_t n_rows_heads, const DecodeWorkspace& ws, int32_t n_split, int32_t n_q_heads,
+                          uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_merge_kernel<D, false>), dim3((unsigned)n_rows_heads), dim3(kMergeBlock), 0, stream,
+                     ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, AppendKernelArgs{}, out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                                const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                                int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
-                                int32_t key_trim, hipStream_t stream) {
-  const float qk_scale_log2 = sm_scale * kLog2e;
-  switch (n_q_heads / pool.n_kv_heads) {
-    case 1: return launch_stage1_g<1>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
-    case 2: return launch_stage1_g<2>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
-    case 4: return launch_stage1_g<4>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
-    case 8: return launch_stage1_g<8>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
-    case 16: return launch_stage1_g<16>(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, qk_scale_log2, geo, ws, key_trim, stream);
-    default: return hipErrorInvalidValue;
+int32_t decode_max_col_tiles(int32_t head_dim) { return head_dim == 128 ? 4 : 2; }
+
+hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float sm_scale,
+                                const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
+                                hipStream_t stream) {
+  const float qk = sm_scale * kLog2e;
+  const bool window = sh.window > 0;
+  if (sh.n_qrows == 1 && geo.n_col_groups == 1 && geo.col_tiles == 1) {
+    if (pool.head_dim == 128)
+      return window ? launch_stage1_single<128, true>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                    : launch_stage1_single<128, false>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    if (pool.head_dim == 256)
+      return window ? launch_stage1_single<256, true>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                    : launch_stage1_single<256, false>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    return hipErrorInvalidValue;
   }
+  if (key_trim != 0) return hipErrorInvalidValue;
+  if (pool.head_dim == 128)
+    return window ? launch_stage1_multi<128, true>(pool, q, sh, qk, geo, ws, stream)
+                  : launch_stage1_multi<128, false>(pool, q, sh, qk, geo, ws, stream);
+  if (pool.head_dim == 256)
+    return window ? launch_stage1_multi<256, true>(pool, q, sh, qk, geo, ws, stream)
+                  : launch_stage1_multi<256, false>(pool, q, sh, qk, geo, ws, stream);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, int32_t n_split,
+hipError_t launch_decode_merge(int64_t n_rows_heads, int32_t head_dim, const DecodeWorkspace& ws, int32_t n_split,
                                uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0,
-                     stream, ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, AppendKernelArgs{},
-                     out);
-  return hipGetLastError();
+  if (head_dim == 128) return launch_merge_d<128>(n_rows_heads, ws, n_split, 1, out, stream);
+  if (head_dim == 256) return launch_merge_d<256>(n_rows_heads, ws, n_split, 1, out, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,
@@ -532,8 +736,15 @@ hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32
                            pool.k_codes, pool.v_codes, pool.k_scales, pool.v_scales,
                            pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads,
                            (uint32_t)(pool.num_rows - 1), app.sm_scale * kLog2e};
-  hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)((int64_t)batch * n_q_heads)), dim3(kMergeBlock), 0,
-                     stream, ws.header, ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  const dim3 grid((unsigned)((int64_t)batch * n_q_heads));
+  if (pool.head_dim == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128, true>), grid, dim3(kMergeBlock), 0, stream, ws.header, ws.part_o,
+                       ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  else if (pool.head_dim == 256)
+    hipLaunchKernelGGL((decode_merge_kernel<256, true>), grid, dim3(kMergeBlock), 0, stream, ws.header, ws.part_o,
+                       ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

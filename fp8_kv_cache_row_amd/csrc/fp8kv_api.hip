@@ -17,6 +17,8 @@ namespace {
 
 using fp8kv::PoolView;
 
+fp8kv_status from_hip(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_ERR_HIP; }
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // NaN test on the bit pattern, independent of floating-point compile flags.
@@ -35,8 +37,8 @@ bool supported_group(int32_t n_q_heads, int32_t n_kv_heads) {
 fp8kv_status check_pool(const fp8kv_pool_layer* p) {
   if (!p || !p->k_codes || !p->v_codes || !p->k_scales || !p->v_scales) return FP8KV_ERR_INVALID_ARG;
   if (p->num_rows <= 0 || p->num_rows > INT32_MAX || p->n_kv_heads <= 0) return FP8KV_ERR_INVALID_ARG;
-  if (p->head_dim != FP8KV_HEAD_DIM) return FP8KV_ERR_UNSUPPORTED;
-  if (p->code_row_stride < (int64_t)p->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
+  if (p->head_dim != FP8KV_HEAD_DIM && p->head_dim != FP8KV_HEAD_DIM_256) return FP8KV_ERR_UNSUPPORTED;
+  if (p->code_row_stride < (int64_t)p->n_kv_heads * p->head_dim) return FP8KV_ERR_INVALID_ARG;
   if (p->scale_row_stride < p->n_kv_heads) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(p->k_codes, 16) || !aligned(p->v_codes, 16) || (p->code_row_stride % 16) != 0)
     return FP8KV_ERR_ALIGNMENT;
@@ -46,7 +48,7 @@ fp8kv_status check_pool(const fp8kv_pool_layer* p) {
 
 PoolView view_of(const fp8kv_pool_layer* p) {
   return PoolView{p->k_codes, p->v_codes, p->k_scales, p->v_scales, p->code_row_stride, p->scale_row_stride,
-                  p->n_kv_heads, p->num_rows};
+                  p->n_kv_heads, p->head_dim, p->num_rows};
 }
 
 // Per-device facts, queried once: gfx950 or not, and the compute-unit count.
@@ -80,18 +82,30 @@ int32_t split_cap(int32_t max_splits) {
   return (max_splits > 0 && max_splits < FP8KV_MAX_SPLITS) ? max_splits : FP8KV_MAX_SPLITS;
 }
 
-// Split choice: about one stage-1 workgroup (kDecodeWaves waves, one LDS-full
-// workgroup per CU) per compute unit across the batch; a split covers a
-// multiple of 32 keys.
-fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
-                                      int32_t max_splits, int n_cu) {
+// Split choice: about one stage-1 workgroup per compute unit across the
+// batch (a workgroup fills its CU's registers: 8 waves of up to 256 or 4 waves
+// of up to 512); a split covers a multiple of 32 keys of the request's key
+// span (the window plus the extra query rows with a window, max_seq_len
+// otherwise).  Several query rows put G * n_qrows columns on the MFMA tiles:
+// as many 16-column tiles per workgroup as the head dim allows, and more
+// column groups beyond that.
+fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t group,
+                                      int32_t n_qrows, int32_t max_seq_len, int32_t window, int32_t max_splits,
+                                      int n_cu) {
+  int32_t col_tiles = 1, n_col_groups = 1;
+  if (n_qrows > 1) {
+    const int32_t tiles = (group * n_qrows + 15) / 16;
+    const int32_t cap = fp8kv::decode_max_col_tiles(head_dim);
+    col_tiles = 1;
+    while (col_tiles < tiles && col_tiles < cap) col_tiles *= 2;
+    n_col_groups = (tiles + col_tiles - 1) / col_tiles;
+  }
   const int64_t unit = fp8kv::kDecodeTileKeys;
-  const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
-  const int64_t per = (int64_t)batch * n_kv_heads;
-  // LDS holds kDecodeTilesPerWave steps per wave; 128 KB of staging fits one workgroup per CU
-  const int64_t staged = (int64_t)fp8kv::kDecodeWaves * fp8kv::kDecodeTilesPerWave;
-  const int64_t per_cu = staged >= 16 ? 1 : 16 / staged;
-  const int64_t target = (int64_t)n_cu * per_cu;
+  int64_t span = max_seq_len;
+  if (window > 0 && (int64_t)window + n_qrows - 1 < span) span = (int64_t)window + n_qrows - 1;
+  const int64_t L = span > 0 ? span : 1;
+  const int64_t per = (int64_t)batch * n_kv_heads * n_col_groups;
+  const int64_t target = n_cu;
   int64_t want = (target + per - 1) / per;
   if (want < 1) want = 1;
   int64_t ns = want;
@@ -101,43 +115,67 @@ fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t
   int64_t chunk = (L + ns - 1) / ns;
   chunk = (chunk + unit - 1) / unit * unit;
   ns = (L + chunk - 1) / chunk;
-  return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk};
+  return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk, col_tiles, n_col_groups};
 }
 
-size_t partial_bytes(int64_t batch, int64_t n_q_heads, int64_t split_stride) {
-  return fp8kv::kDecodeHeaderBytes +
-         (size_t)(batch * n_q_heads * split_stride) * (FP8KV_HEAD_DIM + 1) * sizeof(float);
+size_t partial_bytes(int64_t n_queries, int64_t n_q_heads, int64_t head_dim, int64_t split_stride) {
+  return fp8kv::kDecodeHeaderBytes + (size_t)(n_queries * n_q_heads * split_stride) * (head_dim + 1) * sizeof(float);
 }
 
-fp8kv::DecodeWorkspace workspace_view(void* workspace, int32_t batch, int32_t n_q_heads, int32_t max_splits) {
+fp8kv::DecodeWorkspace workspace_view(void* workspace, int64_t n_queries, int32_t n_q_heads, int32_t head_dim,
+                                      int32_t max_splits) {
   const int32_t stride = split_cap(max_splits);
   char* base = static_cast<char*>(workspace);
   float* part_o = reinterpret_cast<float*>(base + fp8kv::kDecodeHeaderBytes);
-  float* part_lse = part_o + (size_t)batch * n_q_heads * stride * FP8KV_HEAD_DIM;
+  float* part_lse = part_o + (size_t)n_queries * n_q_heads * stride * head_dim;
   return fp8kv::DecodeWorkspace{reinterpret_cast<int32_t*>(base), part_o, part_lse, stride};
 }
 
-// Checks shared by the full decode call and its first stage.
-fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                               const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                               int32_t max_seq_len, float sm_scale, int32_t max_splits, const void* workspace,
-                               size_t workspace_bytes) {
+bool valid_head_dim(int32_t d) { return d == FP8KV_HEAD_DIM || d == FP8KV_HEAD_DIM_256; }
+
+// Checks shared by every decode entry point.
+fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
+                               int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                               const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float sm_scale,
+                               int32_t max_splits, const void* workspace, size_t workspace_bytes) {
   fp8kv_status st = check_pool(pool);
   if (st != FP8KV_OK) return st;
   if (!q || !row_table || !seq_lens) return FP8KV_ERR_INVALID_ARG;
   if (batch <= 0 || max_seq_len < 0 || max_splits < 0 || table_stride < max_seq_len || table_stride <= 0)
     return FP8KV_ERR_INVALID_ARG;
+  if (n_qrows < 1 || n_qrows > FP8KV_MAX_QUERY_ROWS || window < 0) return FP8KV_ERR_INVALID_ARG;
+  if ((int64_t)batch * n_qrows > INT32_MAX / 2) return FP8KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
   if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
   if (is_nan(sm_scale)) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4)) return FP8KV_ERR_ALIGNMENT;
-  if (!workspace || workspace_bytes < partial_bytes(batch, n_q_heads, split_cap(max_splits)))
+  if (!workspace ||
+      workspace_bytes < partial_bytes((int64_t)batch * n_qrows, n_q_heads, pool->head_dim, split_cap(max_splits)))
     return FP8KV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return FP8KV_ERR_ALIGNMENT;
   return FP8KV_OK;
 }
 
-fp8kv_status from_hip(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_ERR_HIP; }
+// Stage 1 (and the merge unless `app` is given) of one decode call.
+fp8kv_status run_decode(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
+                        int32_t n_q_heads, const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
+                        int32_t max_seq_len, int32_t window, float sm_scale, int32_t max_splits, void* workspace,
+                        uint16_t* out, const fp8kv::AppendArgs* app, void* stream) {
+  int n_cu = 0;
+  fp8kv_status st = current_device(&n_cu);
+  if (st != FP8KV_OK) return st;
+  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, pool->head_dim, n_q_heads / pool->n_kv_heads,
+                                                    n_qrows, max_seq_len, window, max_splits, n_cu);
+  const int64_t n_queries = (int64_t)batch * n_qrows;
+  const fp8kv::DecodeWorkspace ws = workspace_view(workspace, n_queries, n_q_heads, pool->head_dim, max_splits);
+  const fp8kv::DecodeShape shape{batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? 1 : 0, s);
+  if (e != hipSuccess) return FP8KV_ERR_HIP;
+  if (app) return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), batch, n_q_heads, ws, geo.n_split, *app, out, s));
+  if (!out) return FP8KV_OK;
+  return from_hip(fp8kv::launch_decode_merge(n_queries * n_q_heads, pool->head_dim, ws, geo.n_split, out, s));
+}
 
 }  // namespace
 
@@ -151,7 +189,7 @@ fp8kv_status fp8kv_quantize_rows(const fp8kv_pool_layer* pool, const uint16_t* k
   if (n_tokens < 0) return FP8KV_ERR_INVALID_ARG;
   if (n_tokens == 0) return FP8KV_OK;
   if (!k || !v || !slots) return FP8KV_ERR_INVALID_ARG;
-  if (src_token_stride < (int64_t)pool->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
+  if (src_token_stride < (int64_t)pool->n_kv_heads * pool->head_dim) return FP8KV_ERR_INVALID_ARG;
   if ((src_token_stride % 8) != 0 || !aligned(k, 16) || !aligned(v, 16)) return FP8KV_ERR_ALIGNMENT;
   if (!aligned(slots, 4)) return FP8KV_ERR_ALIGNMENT;
   st = current_device(nullptr);
@@ -160,39 +198,36 @@ fp8kv_status fp8kv_quantize_rows(const fp8kv_pool_layer* pool, const uint16_t* k
                                               static_cast<hipStream_t>(stream)));
 }
 
-size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_splits) {
-  if (batch <= 0 || n_q_heads <= 0 || max_splits < 0) return 0;
-  return partial_bytes(batch, n_q_heads, split_cap(max_splits));
+size_t fp8kv_decode_workspace_bytes(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits) {
+  if (n_queries <= 0 || n_q_heads <= 0 || max_splits < 0 || !valid_head_dim(head_dim)) return 0;
+  return partial_bytes(n_queries, n_q_heads, head_dim, split_cap(max_splits));
 }
 
 fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
                                  int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
                                  const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, int32_t max_splits,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  fp8kv_status st = check_decode_args(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
+  fp8kv_status st = check_decode_args(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0,
                                       sm_scale, max_splits, workspace, workspace_bytes);
   if (st != FP8KV_OK) return st;
-  int n_cu = 0;
-  st = current_device(&n_cu);
-  if (st != FP8KV_OK) return st;
-  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
-  return from_hip(fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride,
-                                              seq_lens, max_seq_len, sm_scale, geo,
-                                              workspace_view(workspace, batch, n_q_heads, max_splits), 0,
-                                              static_cast<hipStream_t>(stream)));
+  return run_decode(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0, sm_scale,
+                    max_splits, workspace, nullptr, nullptr, stream);
 }
 
-fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_splits, const void* workspace,
-                                size_t workspace_bytes, uint16_t* out, void* stream) {
-  if (batch <= 0 || n_q_heads <= 0 || max_splits < 0 || !out) return FP8KV_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < partial_bytes(batch, n_q_heads, split_cap(max_splits)))
+fp8kv_status fp8kv_decode_merge(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits,
+                                const void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
+  if (n_queries <= 0 || n_q_heads <= 0 || max_splits < 0 || !out) return FP8KV_ERR_INVALID_ARG;
+  if (!valid_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
+  if ((int64_t)n_queries * n_q_heads > INT32_MAX) return FP8KV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < partial_bytes(n_queries, n_q_heads, head_dim, split_cap(max_splits)))
     return FP8KV_ERR_WORKSPACE;
   if (!aligned(workspace, 256) || !aligned(out, 16)) return FP8KV_ERR_ALIGNMENT;
   fp8kv_status st = current_device(nullptr);
   if (st != FP8KV_OK) return st;
-  return from_hip(fp8kv::launch_decode_merge(
-      batch, n_q_heads, workspace_view(const_cast<void*>(workspace), batch, n_q_heads, max_splits), -1, out,
-      static_cast<hipStream_t>(stream)));
+  const fp8kv::DecodeWorkspace ws =
+      workspace_view(const_cast<void*>(workspace), n_queries, n_q_heads, head_dim, max_splits);
+  return from_hip(fp8kv::launch_decode_merge((int64_t)n_queries * n_q_heads, head_dim, ws, -1, out,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
@@ -200,21 +235,22 @@ fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer* pool, const uint16_t* q, 
                                const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                                int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
                                void* stream) {
-  fp8kv_status st = check_decode_args(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
-                                      sm_scale, max_splits, workspace, workspace_bytes);
+  return fp8kv_decode_attn_rows(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0,
+                                sm_scale, max_splits, workspace, workspace_bytes, out, stream);
+}
+
+fp8kv_status fp8kv_decode_attn_rows(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
+                                    int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                                    const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float sm_scale,
+                                    int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
+                                    void* stream) {
+  fp8kv_status st = check_decode_args(pool, q, batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens,
+                                      max_seq_len, window, sm_scale, max_splits, workspace, workspace_bytes);
   if (st != FP8KV_OK) return st;
   if (!out) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(out, 16)) return FP8KV_ERR_ALIGNMENT;
-  int n_cu = 0;
-  st = current_device(&n_cu);
-  if (st != FP8KV_OK) return st;
-  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
-  const fp8kv::DecodeWorkspace ws = workspace_view(workspace, batch, n_q_heads, max_splits);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
-                                             max_seq_len, sm_scale, geo, ws, 0, s);
-  if (e != hipSuccess) return FP8KV_ERR_HIP;
-  return from_hip(fp8kv::launch_decode_merge(batch, n_q_heads, ws, geo.n_split, out, s));
+  return run_decode(pool, q, batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window,
+                    sm_scale, max_splits, workspace, out, nullptr, stream);
 }
 
 fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
@@ -224,25 +260,17 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16
                                       const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                                       int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
                                       void* stream) {
-  fp8kv_status st = check_decode_args(pool, q, batch, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
+  fp8kv_status st = check_decode_args(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0,
                                       sm_scale, max_splits, workspace, workspace_bytes);
   if (st != FP8KV_OK) return st;
   if (!out || !k_new || !v_new || !new_slots || max_seq_len < 1) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(new_slots, 4)) return FP8KV_ERR_ALIGNMENT;
-  if (new_token_stride < (int64_t)pool->n_kv_heads * FP8KV_HEAD_DIM) return FP8KV_ERR_INVALID_ARG;
+  if (new_token_stride < (int64_t)pool->n_kv_heads * pool->head_dim) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || (new_token_stride % 8) != 0)
     return FP8KV_ERR_ALIGNMENT;
-  int n_cu = 0;
-  st = current_device(&n_cu);
-  if (st != FP8KV_OK) return st;
-  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, max_seq_len, max_splits, n_cu);
-  const fp8kv::DecodeWorkspace ws = workspace_view(workspace, batch, n_q_heads, max_splits);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, batch, n_q_heads, row_table, table_stride, seq_lens,
-                                             max_seq_len, sm_scale, geo, ws, 1, s);
-  if (e != hipSuccess) return FP8KV_ERR_HIP;
   const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale};
-  return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), batch, n_q_heads, ws, geo.n_split, app, out, s));
+  return run_decode(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0, sm_scale,
+                    max_splits, workspace, out, &app, stream);
 }
 
 fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q, const uint16_t* k_cur,
@@ -251,6 +279,7 @@ fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q,
                                 int64_t ws_capacity_rows, float sm_scale, uint16_t* out, void* stream) {
   fp8kv_status st = check_pool(pool);
   if (st != FP8KV_OK) return st;
+  if (pool->head_dim != FP8KV_HEAD_DIM) return FP8KV_ERR_UNSUPPORTED;
   if (!q || !k_cur || !v_cur || !out) return FP8KV_ERR_INVALID_ARG;
   if (n_tokens <= 0 || n_prefix < 0) return FP8KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;

@@ -18,14 +18,34 @@ struct PoolView {
   int64_t code_row_stride;   // bytes
   int64_t scale_row_stride;  // floats
   int32_t n_kv_heads;
+  int32_t head_dim;  // 128 or 256
   int64_t num_rows;
 };
 
-// Decode launch geometry: each workgroup covers `chunk` consecutive logical
-// rows of one (request, KV head); `n_split` workgroups per (request, KV head).
+// Decode launch geometry: each workgroup covers `chunk` consecutive keys of
+// one (request, KV head, column group); `n_split` workgroups per (request, KV
+// head, column group).  A column is one (query row, query head) pair of a KV
+// head; a workgroup holds `col_tiles` tiles of 16 columns, and `n_col_groups`
+// workgroups cover all G * n_qrows columns (one row per request: 1 and 1).
 struct DecodeGeometry {
   int32_t n_split;
-  int32_t chunk;  // multiple of kDecodeTileKeys * kDecodeWaves
+  int32_t chunk;  // multiple of kDecodeTileKeys
+  int32_t col_tiles;
+  int32_t n_col_groups;
+};
+
+// The decode problem: q [batch][n_qrows][n_q_heads][head_dim]; query row i of
+// request b sits at position seq_lens[b] - n_qrows + i and sees positions
+// [max(0, p - window + 1), p] (window <= 0: [0, p]).
+struct DecodeShape {
+  int32_t batch;
+  int32_t n_qrows;
+  int32_t n_q_heads;
+  const int32_t* row_table;
+  int64_t table_stride;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t window;
 };
 
 #ifndef FP8KV_DECODE_WAVES
@@ -37,9 +57,9 @@ struct DecodeGeometry {
 // Must equal FP8KV_MAX_SPLITS of the public header (checked in the C ABI).
 #define FP8KV_MAX_SPLITS_INTERNAL 256
 
-constexpr int kDecodeWaves = FP8KV_DECODE_WAVES;                 // waves per stage-1 workgroup
+constexpr int kDecodeWaves = FP8KV_DECODE_WAVES;                 // waves per stage-1 workgroup (narrow shapes)
 constexpr int kDecodeTileKeys = 32;                              // keys per wave per MFMA step
-constexpr int kDecodeTilesPerWave = FP8KV_DECODE_TILES_PER_WAVE;  // steps a wave stages in LDS at once
+constexpr int kDecodeTilesPerWave = FP8KV_DECODE_TILES_PER_WAVE;  // steps in flight per wave (D = 128, one tile)
 
 hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const uint16_t* v,
                                 int64_t src_token_stride, const int32_t* slots, int32_t n_tokens,
@@ -49,8 +69,9 @@ hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, 
                               uint16_t* ws_k, uint16_t* ws_v, hipStream_t stream);
 
 // Split-K partials in the caller's workspace: a 256-byte header whose first
-// int32 is the split count of the last stage-1 launch, then o[B][Hq][split_stride][128]
-// and lse[B][Hq][split_stride] (fp32, log2 units).
+// int32 is the split count of the last stage-1 launch, then
+// o[B * n_qrows][Hq][split_stride][head_dim] and lse[B * n_qrows][Hq][split_stride]
+// (fp32, log2 units).
 struct DecodeWorkspace {
   int32_t* header;
   float* part_o;
@@ -59,20 +80,23 @@ struct DecodeWorkspace {
 };
 constexpr size_t kDecodeHeaderBytes = 256;
 
-// key_trim = 1 leaves each request's last key (position seq_lens[b] - 1) to
-// the appending merge below.
-hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                                const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
-                                int32_t max_seq_len, float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
-                                int32_t key_trim, hipStream_t stream);
+// Column tiles one stage-1 workgroup can hold at this head dim.
+int32_t decode_max_col_tiles(int32_t head_dim);
 
-// n_split < 0: take the split count the preceding stage 1 wrote into the header.
-hipError_t launch_decode_merge(int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws, int32_t n_split,
+// key_trim = 1 (one query row per request) leaves each request's last key
+// (position seq_lens[b] - 1) to the appending merge below.
+hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const DecodeShape& shape, float sm_scale,
+                                const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
+                                hipStream_t stream);
+
+// n_split < 0: take the split count the preceding stage 1 wrote into the
+// header.  n_rows_heads = batch * n_qrows * n_q_heads output vectors.
+hipError_t launch_decode_merge(int64_t n_rows_heads, int32_t head_dim, const DecodeWorkspace& ws, int32_t n_split,
                                uint16_t* out, hipStream_t stream);
 
 // The new token of each request: bf16 K/V rows [B][token_stride] (head g at
-// g * 128), quantized into pool row new_slots[b] and folded into the merge as
-// one more single-key partial.
+// g * head_dim), quantized into pool row new_slots[b] and folded into the
+// merge as one more single-key partial.
 struct AppendArgs {
   const uint16_t* q;
   const uint16_t* k_new;

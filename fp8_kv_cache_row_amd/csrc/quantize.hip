@@ -5,26 +5,28 @@
 // rebuilds historical FP8 rows once per layer into a shared BF16 workspace.
 // "Follow-up model/workload search": the FP8 path quantizes every new K/V row.
 //
-// Both kernels give one 128-element row to 16 lanes (8 elements, 16 bytes of
-// bf16 or 8 bytes of codes per lane), so a wave handles 4 rows with fully
-// coalesced 256-byte / 128-byte row accesses and the row reduction stays
-// inside a 16-lane DPP row.
+// Both kernels give one row of D elements to D/8 lanes (8 elements, 16 bytes
+// of bf16 or 8 bytes of codes per lane), so a wave handles 64*8/D rows with
+// fully coalesced row accesses and the row reduction stays inside 16 or 32
+// lanes.  Quantize covers head dims 128 and 256; the reconstruction serves
+// the D = 128 prefill.
 #include "fp8kv_device.h"
 
 namespace fp8kv {
 
 namespace {
 
-constexpr int kLanesPerRow = 16;
 constexpr int kBlock = 256;
-constexpr int kRowsPerBlock = kBlock / kLanesPerRow;
 
 // Rows are enumerated as ((token * 2 + kv) * n_kv_heads + head), kv 0 = K, 1 = V.
+template <int D>
 __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_token_stride,
     const int32_t* __restrict__ slots, int64_t n_rows, int32_t n_kv_heads, uint8_t* __restrict__ k_codes,
     uint8_t* __restrict__ v_codes, float* __restrict__ k_scales, float* __restrict__ v_scales,
     int64_t code_row_stride, int64_t scale_row_stride, uint32_t max_row) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerBlock = kBlock / kLanesPerRow;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
   const int sub = threadIdx.x % kLanesPerRow;
   if (row >= n_rows) return;  // whole 16-lane groups leave together
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
   const int kv = (int)(tk & 1);
   const int64_t t = tk >> 1;
 
-  const uint16_t* src = (kv ? v : k) + t * src_token_stride + (int64_t)g * kHeadDim + sub * 8;
+  const uint16_t* src = (kv ? v : k) + t * src_token_stride + (int64_t)g * D + sub * 8;
   const uint4 raw = *reinterpret_cast<const uint4*>(src);
   float x[8] = {bf16lo_to_f32(raw.x), bf16hi_to_f32(raw.x), bf16lo_to_f32(raw.y), bf16hi_to_f32(raw.y),
                 bf16lo_to_f32(raw.z), bf16hi_to_f32(raw.z), bf16lo_to_f32(raw.w), bf16hi_to_f32(raw.w)};
@@ -54,13 +56,15 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
   hi = f32x2_to_fp8x2<true>(y[6], y[7], hi);
 
   const int64_t slot = min((uint32_t)slots[t], max_row);  // out-of-range slots are clamped, never followed
-  uint8_t* dst = (kv ? v_codes : k_codes) + slot * code_row_stride + (int64_t)g * kHeadDim + sub * 8;
+  uint8_t* dst = (kv ? v_codes : k_codes) + slot * code_row_stride + (int64_t)g * D + sub * 8;
   *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
   if (sub == 0) (kv ? v_scales : k_scales)[slot * scale_row_stride + g] = s;
 }
 
 // Rows enumerated as ((j * 2 + kv) * n_kv_heads + head) for prefix position j.
 // ws[j][head][d] = bf16_rne(fl32(decode(code) * scale)).
+constexpr int kLanesPerRow = kHeadDim / 8;
+constexpr int kRowsPerBlock = kBlock / kLanesPerRow;
 __global__ __launch_bounds__(kBlock) void reconstruct_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
@@ -97,11 +101,20 @@ hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const u
                                 hipStream_t stream) {
   const int64_t n_rows = (int64_t)n_tokens * 2 * pool.n_kv_heads;
   if (n_rows == 0) return hipSuccess;
-  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
-                     src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
-                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride,
-                     (uint32_t)(pool.num_rows - 1));
+  const int rows_per_block = kBlock / (pool.head_dim / 8);
+  const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+  if (pool.head_dim == 128)
+    hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
+                       src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
+                       pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride,
+                       (uint32_t)(pool.num_rows - 1));
+  else if (pool.head_dim == 256)
+    hipLaunchKernelGGL(quantize_rows_kernel<256>, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
+                       src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
+                       pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride,
+                       (uint32_t)(pool.num_rows - 1));
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -109,6 +122,7 @@ hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, 
                               uint16_t* ws_k, uint16_t* ws_v, hipStream_t stream) {
   const int64_t n_rows = (int64_t)n_prefix * 2 * pool.n_kv_heads;
   if (n_rows == 0) return hipSuccess;
+  if (pool.head_dim != kHeadDim) return hipErrorInvalidValue;
   const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL(reconstruct_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, pool.k_codes,
                      pool.v_codes, pool.k_scales, pool.v_scales, pool.code_row_stride,

@@ -9,7 +9,9 @@
  * current chunk's K/V stay BF16.  FreeToken PR #897 "perf(attention): add packed
  * fp8 kv reads on gfx1201" (description; "Fresh R9700 stage-1 A/B") fixes the
  * decode case: BF16 query, head dim 128, GQA 4/8, page size 1 with randomized
- * physical slots, a split-K first stage and a merge kernel.
+ * physical slots, a split-K first stage and a merge kernel; its section
+ * "Regression and CUDA isolation" widens the decode matrix to head dim 256,
+ * 1/3/8 query rows per request and an odd sliding window.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -40,17 +42,21 @@
 extern "C" {
 #endif
 
-/* Head dimension of every K/V row (the pages qualify only D = 128). */
+/* Head dimensions: pools, quantize-on-write and decode take either; the
+ * prefill path runs at FP8KV_HEAD_DIM. */
 #define FP8KV_HEAD_DIM 128
+#define FP8KV_HEAD_DIM_256 256
 /* Largest finite E4M3FN magnitude; a row's scale is amax / FP8KV_E4M3_MAX. */
 #define FP8KV_E4M3_MAX 448.0f
 /* Upper bound on decode key-splits per (request, KV head). */
 #define FP8KV_MAX_SPLITS 256
+/* Upper bound on query rows per request in one decode call. */
+#define FP8KV_MAX_QUERY_ROWS 8
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
     FP8KV_ERR_INVALID_ARG = 1, /* null pointer, non-positive or inconsistent size */
-    FP8KV_ERR_UNSUPPORTED = 2, /* head_dim != 128, unsupported GQA ratio, not gfx950 */
+    FP8KV_ERR_UNSUPPORTED = 2, /* head_dim not 128/256 (128 for prefill), GQA ratio, not gfx950 */
     FP8KV_ERR_ALIGNMENT = 3,   /* a base pointer or stride breaks the alignment contract */
     FP8KV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
     FP8KV_ERR_HIP = 5          /* the HIP runtime rejected a launch or a query */
@@ -62,9 +68,9 @@ typedef enum fp8kv_status {
  * scale; issue #280, "Current proof-of-concept limitations": dynamic scales per
  * token and per KV head).
  *
- * Physical row r, KV head g:
- *   K codes   k_codes  + r * code_row_stride + g * 128   (128 bytes)
- *   V codes   v_codes  + r * code_row_stride + g * 128   (128 bytes)
+ * Physical row r, KV head g, with D = head_dim (128 or 256):
+ *   K codes   k_codes  + r * code_row_stride + g * D     (D bytes)
+ *   V codes   v_codes  + r * code_row_stride + g * D     (D bytes)
  *   K scale   k_scales[r * scale_row_stride + g]         (fp32)
  *   V scale   v_scales[r * scale_row_stride + g]         (fp32)
  * Value of element d: decode_e4m3fn(code[d]) * scale.
@@ -72,7 +78,7 @@ typedef enum fp8kv_status {
  * Alignment contract (FreeToken PR #897 description: packed reads need
  * 16-byte-aligned bases and row/head strides): k_codes, v_codes and
  * code_row_stride are multiples of 16 bytes; k_scales and v_scales are 4-byte
- * aligned.  code_row_stride >= n_kv_heads * 128 and scale_row_stride >=
+ * aligned.  code_row_stride >= n_kv_heads * D and scale_row_stride >=
  * n_kv_heads.  Strides let the four arrays be separate allocations or
  * interleave inside one per-row record.
  */
@@ -83,7 +89,7 @@ typedef struct fp8kv_pool_layer {
     float *v_scales;
     int64_t num_rows;         /* physical rows in the pool */
     int32_t n_kv_heads;       /* KV heads per row */
-    int32_t head_dim;         /* must be FP8KV_HEAD_DIM */
+    int32_t head_dim;         /* FP8KV_HEAD_DIM or FP8KV_HEAD_DIM_256 */
     int64_t code_row_stride;  /* bytes between rows of k_codes / v_codes */
     int64_t scale_row_stride; /* floats between rows of k_scales / v_scales */
 } fp8kv_pool_layer;
@@ -94,14 +100,14 @@ typedef struct fp8kv_pool_layer {
  * "What changes": each row stores E4M3 codes plus its own FP32 scale).
  *
  * For token t in [0, n_tokens), KV head g, separately for K and V, with x the
- * 128 bf16 values at k + t * src_token_stride + g * 128 (resp. v):
+ * D = pool->head_dim bf16 values at k + t * src_token_stride + g * D (resp. v):
  *   amax = max_d |x_d|;   s = fl32(amax / 448)   (IEEE fp32 division)
  *   code_d = E4M3FN round-to-nearest-even of fl32(x_d / s), saturated to +-448
  *   (a row with amax == 0 stores s = 0 and codes +0 / -0 following x_d's sign)
  * and stores the codes and s at physical row slots[t].
  *
- * k, v:            device bf16 [n_tokens][n_kv_heads][128] with token stride
- *                  src_token_stride elements (>= n_kv_heads*128, a multiple of
+ * k, v:            device bf16 [n_tokens][n_kv_heads][D] with token stride
+ *                  src_token_stride elements (>= n_kv_heads*D, a multiple of
  *                  8); bases 16-byte aligned.
  * slots:           device int32 [n_tokens], each in [0, pool->num_rows); slots
  *                  must be distinct within one call.  An out-of-range slot is
@@ -114,19 +120,21 @@ fp8kv_status fp8kv_quantize_rows(const fp8kv_pool_layer *pool, const uint16_t *k
                                  void *stream);
 
 /*
- * Bytes of device workspace the decode calls need for `batch` requests of
- * `n_q_heads` query heads with at most `max_splits` splits per request
+ * Bytes of device workspace the decode calls need for `n_queries` query rows
+ * (batch * n_qrows; batch for the one-row calls) of `n_q_heads` query heads
+ * of dimension `head_dim` with at most `max_splits` splits per request
  * (0 = FP8KV_MAX_SPLITS): a 256-byte header, then one fp32 output vector and
- * one log-sum-exp per request, query head and split slot.  Returns 0 for
+ * one log-sum-exp per query row, query head and split slot.  Returns 0 for
  * invalid arguments.
  */
-size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_splits);
+size_t fp8kv_decode_workspace_bytes(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits);
 
 /*
  * fp8kv_decode_attn -- one-token-per-request GQA attention over the FP8 pool
  * (FreeToken PR #897 description and "Fresh R9700 stage-1 A/B": BF16 query,
  * D = 128, GQA 4/8, page size 1, split-K stage 1 followed by a merge kernel;
- * PR #853 "What changes": rows hold E4M3 codes and per-row FP32 scales).
+ * "Regression and CUDA isolation": D = 256 as well; PR #853 "What changes":
+ * rows hold E4M3 codes and per-row FP32 scales).  D = pool->head_dim.
  *
  * For request b and query head h, with G = n_q_heads / n_kv_heads, KV head
  * g = h / G, L = seq_lens[b] and rows r_t = row_table[b * table_stride + t]:
@@ -141,7 +149,8 @@ size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t ma
  * merge combines them by log-sum-exp.  Results agree to rounding for every
  * split count.
  *
- * q:            device bf16 [batch][n_q_heads][128], contiguous, 16-byte aligned.
+ * q:            device bf16 [batch][n_q_heads][D], contiguous, 16-byte aligned
+ *               (D = pool->head_dim).
  * row_table:    device int32, row b at row_table + b * table_stride.
  *               Entries below seq_lens[b] name the request's rows.  Entries
  *               in [seq_lens[b], max_seq_len) (padding) are read and masked
@@ -157,8 +166,8 @@ size_t fp8kv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t ma
  *               <= table_stride.
  * n_q_heads:    a multiple of pool->n_kv_heads with G in {1, 2, 4, 8, 16}.
  * workspace:    device, 256-byte aligned, >= fp8kv_decode_workspace_bytes(
- *               batch, n_q_heads, max_splits) bytes; contents are scratch.
- * out:          device bf16 [batch][n_q_heads][128], 16-byte aligned.
+ *               batch, n_q_heads, D, max_splits) bytes; contents are scratch.
+ * out:          device bf16 [batch][n_q_heads][D], 16-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP.
  */
 fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
@@ -180,15 +189,48 @@ fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer *pool, const uint16_t *q
                                  void *stream);
 
 /*
- * fp8kv_decode_merge -- the merge (stage 2) of fp8kv_decode_attn: combines the
+ * fp8kv_decode_merge -- the merge (stage 2) of the decode calls: combines the
  * partials a preceding fp8kv_decode_stage1 on the same stream wrote into
- * `workspace` (called with the same batch, n_q_heads and max_splits) by
- * log-sum-exp and writes bf16 out[batch][n_q_heads][128].
- * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, HIP.
+ * `workspace` (n_queries = its batch; the same n_q_heads, head dim and
+ * max_splits) by log-sum-exp and writes bf16 out[n_queries][n_q_heads][head_dim].
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim), ALIGNMENT, WORKSPACE, HIP.
  */
-fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_splits,
+fp8kv_status fp8kv_decode_merge(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits,
                                 const void *workspace, size_t workspace_bytes, uint16_t *out,
                                 void *stream);
+
+/*
+ * fp8kv_decode_attn_rows -- decode attention for several query rows per
+ * request and an optional sliding key window (FreeToken PR #897 description:
+ * the multi-row decode of #900 runs up to 8 query rows per request; "Regression
+ * and CUDA isolation": 1/3/8 query rows and an odd sliding window are part of
+ * the qualified matrix).
+ *
+ * Request b holds positions 0 .. L-1 (L = seq_lens[b]) at rows
+ * row_table[b * table_stride + t].  Its query row i (0 <= i < n_qrows) sits at
+ * position p = L - n_qrows + i (its own K/V are already in the pool) and
+ * attends causally to positions lo .. p, lo = max(0, p - window + 1) when
+ * window > 0 and lo = 0 when window == 0; a row with p < 0 gets zeros.  Each
+ * row is fp8kv_decode_attn's formula over its own positions.  n_qrows == 1
+ * with window == 0 is fp8kv_decode_attn.
+ *
+ * Rows share the reads of the K/V codes: the G * n_qrows (query row, head)
+ * pairs of a KV head are the columns of the MFMA tiles, up to 64 per
+ * workgroup at D = 128 and 32 at D = 256 (wider shapes run more workgroups
+ * over the same rows).
+ *
+ * q, out:       device bf16 [batch][n_qrows][n_q_heads][D], 16-byte aligned.
+ * n_qrows:      1 .. FP8KV_MAX_QUERY_ROWS.
+ * window:       >= 0 (0 = no window).
+ * workspace:    >= fp8kv_decode_workspace_bytes(batch * n_qrows, n_q_heads,
+ *               D, max_splits) bytes.
+ * Other arguments and the errors are those of fp8kv_decode_attn.
+ */
+fp8kv_status fp8kv_decode_attn_rows(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch, int32_t n_qrows,
+                                    int32_t n_q_heads, const int32_t *row_table, int64_t table_stride,
+                                    const int32_t *seq_lens, int32_t max_seq_len, int32_t window, float sm_scale,
+                                    int32_t max_splits, void *workspace, size_t workspace_bytes, uint16_t *out,
+                                    void *stream);
 
 /*
  * fp8kv_decode_attn_append -- one decode step with the new token's
@@ -208,8 +250,8 @@ fp8kv_status fp8kv_decode_merge(int32_t batch, int32_t n_q_heads, int32_t max_sp
  * a launch per step.
  *
  * k_new, v_new:      device bf16, token b at k_new + b * new_token_stride,
- *                    [n_kv_heads][128] each; 16-byte aligned, stride a
- *                    multiple of 8 elements and >= n_kv_heads * 128.
+ *                    [n_kv_heads][D] each; 16-byte aligned, stride a
+ *                    multiple of 8 elements and >= n_kv_heads * D.
  * new_slots:         device int32 [batch], 4-byte aligned: physical rows of
  *                    `pool`, distinct between requests, named by no position
  *                    below p_b of any request (clamped like table entries).
@@ -228,6 +270,7 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer *pool, const uint16
 
 /*
  * fp8kv_prefill_attn -- attention of one prefill chunk over historical FP8 rows
+ * of a pool with head_dim == 128
  * (FreeToken PR #853, "What changes": the prefill path reconstructs historical
  * FP8 rows once per layer into one shared BF16 workspace; current-chunk K/V
  * remain BF16; "Paired end-to-end A/B": the 8K historical-prefix + 8K

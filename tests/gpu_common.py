@@ -50,7 +50,7 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str):
 
 def build_pool(case, layout: str = "separate") -> fk.Fp8KvPool:
     """Quantize every pool row of a DecodeCase through the HIP path (row r -> slot r)."""
-    pool = fk.Fp8KvPool(case.pool_rows, case.n_kv_heads, layout=layout, device=DEV)
+    pool = fk.Fp8KvPool(case.pool_rows, case.n_kv_heads, layout=layout, device=DEV, head_dim=case.head_dim)
     slots = torch.arange(case.pool_rows, dtype=torch.int32, device=DEV)
     fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.k_rows), to_dev_bf16(case.v_rows), slots)
     return pool

@@ -20,7 +20,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = B.declared_symbols()
     assert set(names) >= {"fp8kv_quantize_rows", "fp8kv_decode_attn", "fp8kv_prefill_attn",
-                          "fp8kv_decode_attn_append", "fp8kv_decode_stage1", "fp8kv_decode_merge",
+                          "fp8kv_decode_attn_append", "fp8kv_decode_attn_rows", "fp8kv_decode_stage1",
+                          "fp8kv_decode_merge",
                           "fp8kv_decode_workspace_bytes", "fp8kv_status_string"}
     for n in names:
         assert hasattr(lib, n), n
@@ -47,9 +48,17 @@ def _quant(lib, pool, k=A, v=A, stride=512, slots=A, n=4):
 def _decode(lib, pool, q=A, batch=1, hq=32, table=A, tstride=1024, lens=A, maxlen=1000, sm=0.088,
             splits=0, ws=A, wsb=None, out=A):
     if wsb is None:
-        wsb = lib.fp8kv_decode_workspace_bytes(batch, hq, splits)
+        wsb = lib.fp8kv_decode_workspace_bytes(batch, hq, pool.head_dim, splits)
     return lib.fp8kv_decode_attn(ctypes.byref(pool), q, batch, hq, table, tstride, lens, maxlen, sm, splits,
                                  ws, wsb, out, None)
+
+
+def _rows(lib, pool, q=A, batch=1, nq=3, hq=32, table=A, tstride=1024, lens=A, maxlen=1000, window=0, sm=0.088,
+          splits=0, ws=A, wsb=None, out=A):
+    if wsb is None:
+        wsb = lib.fp8kv_decode_workspace_bytes(batch * max(nq, 1), hq, pool.head_dim, splits)
+    return lib.fp8kv_decode_attn_rows(ctypes.byref(pool), q, batch, nq, hq, table, tstride, lens, maxlen, window, sm,
+                                      splits, ws, wsb, out, None)
 
 
 def _prefill(lib, pool, q=A, kc=A, vc=A, T=16, hq=32, rows=A, P=8, wsk=A, wsv=A, cap=8, sm=0.088, out=A):
@@ -60,6 +69,9 @@ def test_quantize_validation(lib):
     assert lib.fp8kv_quantize_rows(None, A, A, 512, A, 4, None) == INVALID
     assert _quant(lib, _pool(k_codes=0)) == INVALID
     assert _quant(lib, _pool(head_dim=64)) == UNSUPPORTED
+    assert _quant(lib, _pool(head_dim=192, code_row_stride=768)) == UNSUPPORTED
+    assert _quant(lib, _pool(head_dim=256)) == INVALID               # code_row_stride 512 < 4 * 256
+    assert _quant(lib, _pool(head_dim=256, code_row_stride=1024)) == INVALID  # token stride 512 < 4 * 256
     assert _quant(lib, _pool(num_rows=0)) == INVALID
     assert _quant(lib, _pool(code_row_stride=256)) == INVALID        # < Hkv * 128
     assert _quant(lib, _pool(scale_row_stride=2)) == INVALID
@@ -91,21 +103,41 @@ def test_decode_validation(lib):
     assert _decode(lib, p, ws=0) == WORKSPACE
     assert _decode(lib, p, wsb=100) == WORKSPACE
     assert _decode(lib, p, ws=A + 16) == ALIGN
-    assert _decode(lib, _pool(head_dim=256)) == UNSUPPORTED
+    assert _decode(lib, _pool(head_dim=256)) == INVALID               # code_row_stride 512 < 4 * 256
+    p256 = _pool(head_dim=256, code_row_stride=1024)
+    small = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
+    assert _decode(lib, p256, wsb=small) == WORKSPACE                 # D = 256 partials need twice the room
+
+
+def test_decode_rows_validation(lib):
+    p = _pool()
+    assert _rows(lib, p, nq=0) == INVALID
+    assert _rows(lib, p, nq=9) == INVALID                             # more than FP8KV_MAX_QUERY_ROWS
+    assert _rows(lib, p, window=-1) == INVALID
+    assert _rows(lib, p, hq=12) == UNSUPPORTED
+    assert _rows(lib, p, out=0) == INVALID
+    assert _rows(lib, p, out=A + 2) == ALIGN
+    assert _rows(lib, p, q=A + 2) == ALIGN
+    one_row = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
+    assert _rows(lib, p, nq=3, wsb=one_row) == WORKSPACE              # partials for 3 rows
+    assert _rows(lib, p, batch=0) == INVALID
+    assert _rows(lib, p, tstride=999) == INVALID
 
 
 def test_decode_stage_validation(lib):
     p = _pool()
-    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
     s1 = lambda **kw: lib.fp8kv_decode_stage1(ctypes.byref(p), kw.get("q", A), 1, kw.get("hq", 32), A, 1024, A,
                                               1000, 0.088, 0, kw.get("ws", A), kw.get("wsb", wsb), None)
     assert s1(q=0) == INVALID
     assert s1(hq=12) == UNSUPPORTED
     assert s1(wsb=wsb - 1) == WORKSPACE
     assert s1(ws=A + 64) == ALIGN
-    m = lambda **kw: lib.fp8kv_decode_merge(kw.get("b", 1), 32, kw.get("splits", 0), kw.get("ws", A),
-                                            kw.get("wsb", wsb), kw.get("out", A), None)
+    m = lambda **kw: lib.fp8kv_decode_merge(kw.get("b", 1), 32, kw.get("d", 128), kw.get("splits", 0),
+                                            kw.get("ws", A), kw.get("wsb", wsb), kw.get("out", A), None)
     assert m(b=0) == INVALID
+    assert m(d=64) == UNSUPPORTED
+    assert m(d=256) == WORKSPACE                                      # the D = 128 workspace is too small
     assert m(out=0) == INVALID
     assert m(ws=0) == WORKSPACE
     assert m(splits=300, wsb=100) == WORKSPACE
@@ -113,7 +145,7 @@ def test_decode_stage_validation(lib):
 
 
 def _append(lib, p, **kw):
-    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, p.head_dim, 0)
     return lib.fp8kv_decode_attn_append(ctypes.byref(p), kw.get("q", A), 1, kw.get("hq", 32), kw.get("kn", A),
                                         kw.get("vn", 2 * A), kw.get("nstride", 512), kw.get("slots", A), A, 1024, A,
                                         kw.get("maxlen", 1000), 0.088, 0, A, kw.get("wsb", wsb), kw.get("out", A),
@@ -133,14 +165,19 @@ def test_decode_append_validation(lib):
     assert _append(lib, p, kn=A + 8) == ALIGN
     assert _append(lib, p, hq=12) == UNSUPPORTED
     assert _append(lib, p, wsb=10) == WORKSPACE
+    p256 = _pool(head_dim=256, code_row_stride=1024)
+    assert _append(lib, p256, nstride=512) == INVALID                # shorter than Hkv * 256
+    assert _append(lib, p256, nstride=1024, kn=A + 8) == ALIGN
 
 
 def test_decode_workspace_bytes(lib):
     f = lib.fp8kv_decode_workspace_bytes
-    assert f(1, 32, 64) == 256 + 1 * 32 * 64 * 129 * 4
-    assert f(2, 16, 0) == 256 + 2 * 16 * 256 * 129 * 4               # 0 = the library's cap
-    assert f(1, 8, 10_000) == 256 + 1 * 8 * 256 * 129 * 4
-    assert f(0, 8, 1) == 0 and f(1, 0, 1) == 0 and f(1, 8, -1) == 0
+    assert f(1, 32, 128, 64) == 256 + 1 * 32 * 64 * 129 * 4
+    assert f(2, 16, 128, 0) == 256 + 2 * 16 * 256 * 129 * 4          # 0 = the library's cap
+    assert f(1, 8, 128, 10_000) == 256 + 1 * 8 * 256 * 129 * 4
+    assert f(3, 32, 256, 64) == 256 + 3 * 32 * 64 * 257 * 4
+    assert f(0, 8, 128, 1) == 0 and f(1, 0, 128, 1) == 0 and f(1, 8, 128, -1) == 0
+    assert f(1, 8, 64, 1) == 0
 
 
 def test_prefill_validation(lib):
@@ -156,6 +193,7 @@ def test_prefill_validation(lib):
     assert _prefill(lib, p, wsv=A + 2) == ALIGN
     assert _prefill(lib, p, kc=A + 4) == ALIGN
     assert _prefill(lib, p, sm=float("nan")) == INVALID
+    assert _prefill(lib, _pool(head_dim=256, code_row_stride=1024)) == UNSUPPORTED  # prefill runs at D = 128
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0,
@@ -165,8 +203,10 @@ def test_valid_arguments_reach_the_device_check(lib):
     fails (no GPU here) with FP8KV_ERR_HIP; only runs where no device is visible."""
     assert _quant(lib, _pool()) == HIP
     assert _decode(lib, _pool()) == HIP
+    assert _decode(lib, _pool(head_dim=256, code_row_stride=1024)) == HIP
+    assert _rows(lib, _pool(), nq=8, window=17) == HIP
     assert _prefill(lib, _pool()) == HIP
-    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 0)
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
     assert lib.fp8kv_decode_stage1(ctypes.byref(_pool()), A, 1, 32, A, 1024, A, 1000, 0.088, 0, A, wsb, None) == HIP
-    assert lib.fp8kv_decode_merge(1, 32, 0, A, wsb, A, None) == HIP
+    assert lib.fp8kv_decode_merge(1, 32, 128, 0, A, wsb, A, None) == HIP
     assert _append(lib, _pool()) == HIP
