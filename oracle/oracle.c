@@ -51,6 +51,11 @@
  *   - a sliding window of W keys ([897] "Regression and CUDA isolation": the
  *     integration cases include an odd sliding window) lets the query at
  *     position p see positions p-W+1 .. p.
+ *   - the INT8 KV format ([897] description and "Regression and CUDA
+ *     isolation" name INT8 KV beside FP8 and BF16, with no definition) is the
+ *     symmetric per-row counterpart of the FP8 one: s = fl32(amax / 127),
+ *     code = round-half-even(fl32(x / s)) clamped to [-127, 127], stored as a
+ *     two's-complement byte; value = code * s.
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off.
  * No fast-math: fp32 divisions and products must be IEEE round-to-nearest.
@@ -153,7 +158,29 @@ uint8_t oracle_e4m3_encode(float y) {
     return sign | (uint8_t)code;
 }
 
+/* --------------------------------------------------------------- INT8 -- */
+
+/* Round a finite binary32 to the nearest integer, ties to even, clamped to
+ * [-127, 127] (the symmetric INT8 KV format). */
+int8_t oracle_int8_encode(float y) {
+    double a = (double)y, n = floor(a), frac = a - n;
+    if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0))
+        n += 1.0;
+    if (n > 127.0)
+        n = 127.0;
+    if (n < -127.0)
+        n = -127.0;
+    return (int8_t)n;
+}
+
+/* Value of an INT8 code byte (two's complement). */
+double oracle_int8_decode(uint8_t c) { return (double)(int8_t)c; }
+
 /* ---------------------------------------------------------- quantize -- */
+
+/* KV code formats. */
+#define ORACLE_FORMAT_E4M3 0
+#define ORACLE_FORMAT_INT8 1
 
 /* Quantize one row of D bf16 values ([853] "What changes": one FP32 scale
  * per physical K/V row; [280]: dynamic per-token / per-KV-head scale).
@@ -176,18 +203,49 @@ static void quantize_row(const uint16_t *x, int32_t D, uint8_t *codes, float *sc
     *scale = s;
 }
 
+/* The INT8 counterpart: amax = max |x|, s = fl32(amax / 127),
+ * c_d = int8_encode(fl32(x_d / s)); amax == 0 gives s = 0 and zero codes. */
+static void quantize_row_int8(const uint16_t *x, int32_t D, uint8_t *codes, float *scale) {
+    float xf[ORACLE_MAX_HEAD_DIM];
+    float amax = 0.0f, s;
+    int d;
+    for (d = 0; d < D; ++d) {
+        xf[d] = bf16_to_float(x[d]);
+        if (fabsf(xf[d]) > amax)
+            amax = fabsf(xf[d]);
+    }
+    s = amax / 127.0f;
+    for (d = 0; d < D; ++d)
+        codes[d] = (uint8_t)((amax == 0.0f) ? 0 : oracle_int8_encode(xf[d] / s));
+    *scale = s;
+}
+
 /* rows: [n_rows][head_dim] bf16 bits, contiguous.  codes: [n_rows][head_dim];
- * scales: [n_rows].  head_dim in [1, ORACLE_MAX_HEAD_DIM]; returns 0, or -1 for
- * an unsupported head_dim. */
-int32_t oracle_quantize_rows(const uint16_t *rows, int64_t n_rows, int32_t head_dim, uint8_t *codes,
-                             float *scales) {
+ * scales: [n_rows].  format: ORACLE_FORMAT_E4M3 or ORACLE_FORMAT_INT8.
+ * head_dim in [1, ORACLE_MAX_HEAD_DIM]; returns 0, or -1 for an unsupported
+ * head_dim or format. */
+int32_t oracle_quantize_rows(const uint16_t *rows, int64_t n_rows, int32_t head_dim, int32_t format,
+                             uint8_t *codes, float *scales) {
     int64_t r;
     if (head_dim <= 0 || head_dim > ORACLE_MAX_HEAD_DIM)
         return -1;
+    if (format != ORACLE_FORMAT_E4M3 && format != ORACLE_FORMAT_INT8)
+        return -1;
 #pragma omp parallel for schedule(static)
-    for (r = 0; r < n_rows; ++r)
-        quantize_row(rows + r * head_dim, head_dim, codes + r * head_dim, scales + r);
+    for (r = 0; r < n_rows; ++r) {
+        if (format == ORACLE_FORMAT_INT8)
+            quantize_row_int8(rows + r * head_dim, head_dim, codes + r * head_dim, scales + r);
+        else
+            quantize_row(rows + r * head_dim, head_dim, codes + r * head_dim, scales + r);
+    }
     return 0;
+}
+
+/* Value table of one code format. */
+static void code_values(int32_t format, double lut[256]) {
+    int i;
+    for (i = 0; i < 256; ++i)
+        lut[i] = (format == ORACLE_FORMAT_INT8) ? oracle_int8_decode((uint8_t)i) : oracle_e4m3_decode((uint8_t)i);
 }
 
 /* --------------------------------------------------------- attention -- */
@@ -209,10 +267,11 @@ int32_t oracle_quantize_rows(const uint16_t *rows, int64_t n_rows, int32_t head_
  *   khat_t = decode(k code) * k_scale,  vhat_t = decode(v code) * v_scale (fp64)
  *   z_t    = sm_scale * sum_d q_d * khat_t[d]
  *   out    = sum_t exp(z_t - max z) vhat_t / sum_t exp(z_t - max z)
+ * with decode the E4M3FN or the INT8 value of a code byte (`format`).
  * A query row that sees no position (p < 0) gets an all-zero output.
- * Returns 0, or -1 for an unsupported head_dim. */
+ * Returns 0, or -1 for an unsupported head_dim or format. */
 int32_t oracle_decode_attention(const uint16_t *q, int32_t batch, int32_t n_qrows, int32_t n_q_heads,
-                                int32_t n_kv_heads, int32_t head_dim,
+                                int32_t n_kv_heads, int32_t head_dim, int32_t format,
                                 const uint8_t *k_codes, const uint8_t *v_codes,
                                 const float *k_scales, const float *v_scales,
                                 int64_t code_row_stride, int64_t scale_row_stride,
@@ -222,11 +281,11 @@ int32_t oracle_decode_attention(const uint16_t *q, int32_t batch, int32_t n_qrow
     int32_t group = n_q_heads / n_kv_heads;
     int64_t job;
     double lut[256];
-    int i;
     if (D <= 0 || D > ORACLE_MAX_HEAD_DIM)
         return -1;
-    for (i = 0; i < 256; ++i)
-        lut[i] = oracle_e4m3_decode((uint8_t)i);
+    if (format != ORACLE_FORMAT_E4M3 && format != ORACLE_FORMAT_INT8)
+        return -1;
+    code_values(format, lut);
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (job = 0; job < (int64_t)batch * n_qrows * n_q_heads; ++job) {
@@ -282,12 +341,15 @@ int32_t oracle_decode_attention(const uint16_t *q, int32_t batch, int32_t n_qrow
 
 /* Rebuild historical FP8 rows as bf16 ([853] "What changes": historical FP8
  * rows are reconstructed once per layer into one shared BF16 workspace).
- * ws[j][g][d] = bf16_rne(fl32(decode(code) * scale)) for pool row rows[j].
+ * ws[j][g][d] = bf16_rne(fl32(decode(code) * scale)) for pool row rows[j], with
+ * decode the E4M3FN or INT8 value of the code (`format`).
  * ws: [n_rows][n_kv_heads][head_dim] bf16 bits. */
 void oracle_reconstruct(const uint8_t *codes, const float *scales, int64_t code_row_stride,
-                        int64_t scale_row_stride, int32_t n_kv_heads, int32_t head_dim, const int32_t *rows,
-                        int64_t n_rows, uint16_t *ws) {
+                        int64_t scale_row_stride, int32_t n_kv_heads, int32_t head_dim, int32_t format,
+                        const int32_t *rows, int64_t n_rows, uint16_t *ws) {
     int64_t j;
+    double lut[256];
+    code_values(format, lut);
 #pragma omp parallel for schedule(static)
     for (j = 0; j < n_rows; ++j) {
         int64_t row = rows[j];
@@ -298,7 +360,7 @@ void oracle_reconstruct(const uint8_t *codes, const float *scales, int64_t code_
             float s = scales[row * scale_row_stride + g];
             uint16_t *w = ws + (j * n_kv_heads + g) * head_dim;
             for (d = 0; d < head_dim; ++d) {
-                float v = (float)oracle_e4m3_decode(c[d]) * s; /* exact decode, one fp32 rounding */
+                float v = (float)lut[c[d]] * s; /* exact decode, one fp32 rounding */
                 w[d] = float_to_bf16_rne(v);
             }
         }
