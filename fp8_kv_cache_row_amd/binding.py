@@ -20,6 +20,7 @@ import torch
 
 HEAD_DIM = 128           # prefill, and the default pool head dim
 HEAD_DIMS = (128, 256)   # pool / quantize / decode head dims
+CODE_FORMATS = {"e4m3": 0, "int8": 1}
 MAX_QUERY_ROWS = 8
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8kv.so")
 _HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp8kv.h")
@@ -45,6 +46,8 @@ class PoolLayer(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("code_row_stride", ctypes.c_int64),
         ("scale_row_stride", ctypes.c_int64),
+        ("code_format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -137,13 +140,17 @@ class Fp8KvPool:
     layout="interleaved": one record per row holding K codes, V codes, K scales,
       V scales back to back (rounded up to 16 bytes), so every byte of a row is
       in one contiguous span.
+    code_format: "e4m3" (OCP E4M3FN, scale amax/448) or "int8" (symmetric, scale amax/127).
     """
 
     def __init__(self, num_rows: int, n_kv_heads: int, layout: str = "separate",
-                 device: Optional[torch.device] = None, head_dim: int = HEAD_DIM):
+                 device: Optional[torch.device] = None, head_dim: int = HEAD_DIM, code_format: str = "e4m3"):
         dev = device or torch.device("cuda", torch.cuda.current_device())
         self.num_rows, self.n_kv_heads, self.layout = int(num_rows), int(n_kv_heads), layout
         self.head_dim = int(head_dim)
+        if code_format not in CODE_FORMATS:
+            raise ValueError(f"unknown code format {code_format!r}")
+        self.code_format = code_format
         H, D = self.n_kv_heads, self.head_dim
         if layout == "separate":
             self.k_codes = torch.zeros((num_rows, H, D), dtype=torch.uint8, device=dev)
@@ -167,7 +174,7 @@ class Fp8KvPool:
         else:
             raise ValueError(f"unknown pool layout {layout!r}")
         self.layer = PoolLayer(ptrs[0], ptrs[1], ptrs[2], ptrs[3], self.num_rows, H, D,
-                               code_stride, scale_stride)
+                               code_stride, scale_stride, CODE_FORMATS[code_format], 0)
 
     def scales(self):
         """(k_scales, v_scales) as float32 [R][Hkv] tensors (copies for the interleaved layout)."""

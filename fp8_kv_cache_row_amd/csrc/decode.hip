@@ -17,8 +17,8 @@
 //    contraction, 8 bytes of V per key, 16 lanes covering one whole 128-byte V
 //    row.  All loads of both steps are in flight before the first wait; only
 //    row indices and scales pass through LDS.
-//  * QK^T runs on the bf16 MFMA 16x16x32 with E4M3 codes widened exactly to
-//    bf16.  S^T = K * Q^T puts keys on the MFMA rows and the G query heads of
+//  * QK^T runs on the bf16 MFMA 16x16x32 with E4M3 (or INT8) codes widened
+//    exactly to bf16.  S^T = K * Q^T puts keys on the MFMA rows and the G query heads of
 //    the group on the columns, so each lane holds 8 keys of one head: the
 //    per-head maximum needs two cross-lane steps, and those 8 keys are exactly
 //    the k-slots this lane feeds to the P*V MFMA, so P never moves between
@@ -60,10 +60,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //           the columns are the G heads of one row and G is a template value.
 //   WINDOW  a sliding key window: the key range starts at the first row's
 //           lowest visible position, so the table read waits for the length.
-template <int G_, int D_, int NT_, bool MULTI_, bool WINDOW_>
+//   F       the code format (E4M3FN or INT8), widened exactly to bf16.
+template <int G_, int D_, int NT_, bool MULTI_, bool WINDOW_, int F_>
 struct Stage1 {
-  static constexpr int G = G_, D = D_, NT = NT_;
+  static constexpr int G = G_, D = D_, NT = NT_, F = F_;
   static constexpr bool MULTI = MULTI_, WINDOW = WINDOW_;
+  using Code = Codec<F_>;
   // Registers: NT * D / 16 accumulators of 4 floats each, NT * D / 32 query
   // operands and one or two steps of codes in flight.  Wide shapes run 4
   // waves (one per SIMD, 512 registers each) instead of 8.
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
 #pragma unroll
       for (int kk = 0; kk < C::kQK; ++kk) {
         const u32x4 w0 = kr[st][0][kk >> 1], w1 = kr[st][1][kk >> 1];
-        const bf16x8 a0 = (kk & 1) ? fp8x8_to_bf16x8(w0.z, w0.w) : fp8x8_to_bf16x8(w0.x, w0.y);
-        const bf16x8 a1 = (kk & 1) ? fp8x8_to_bf16x8(w1.z, w1.w) : fp8x8_to_bf16x8(w1.x, w1.y);
+        const bf16x8 a0 = (kk & 1) ? C::Code::widen8(w0.z, w0.w) : C::Code::widen8(w0.x, w0.y);
+        const bf16x8 a1 = (kk & 1) ? C::Code::widen8(w1.z, w1.w) : C::Code::widen8(w1.x, w1.y);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           s0[t] = mfma16x16x32(a0, qb[t][kk], s0[t]);
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
         transpose4x4_bytes(vr[st][4][w], vr[st][5][w], vr[st][6][w], vr[st][7][w], hi[0], hi[1], hi[2], hi[3]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bf16x8 vb = fp8x8_to_bf16x8(lo[e], hi[e]);
+          const bf16x8 vb = C::Code::widen8(lo[e], hi[e]);
 #pragma unroll
           for (int t = 0; t < NT; ++t) o[t][4 * w + e] = mfma16x16x32(pa[t], vb, o[t][4 * w + e]);
         }
@@ -466,7 +468,7 @@ struct LaneVec {
   typedef uint32_t U __attribute__((ext_vector_type(E / 2)));
 };
 
-template <int D, bool APPEND>
+template <int D, bool APPEND, int F = kE4M3>
 __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t* __restrict__ header,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_lse,
@@ -561,18 +563,19 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
       }
       ka = wave_max(ka);
       va = wave_max(va);
-      const float sk = e4m3_row_scale(ka), sv = e4m3_row_scale(va);
+      using Code = Codec<F>;
+      const float sk = Code::scale(ka), sv = Code::scale(va);
       uint32_t kc = 0u, vc = 0u;  // E codes, byte e = element e
-      kc = f32x2_to_fp8x2<false>(e4m3_prescaled(kx[0], ka, sk), e4m3_prescaled(kx[1], ka, sk), kc);
-      vc = f32x2_to_fp8x2<false>(e4m3_prescaled(vx[0], va, sv), e4m3_prescaled(vx[1], va, sv), vc);
+      kc = Code::template pack2<false>(Code::prescale(kx[0], ka, sk), Code::prescale(kx[1], ka, sk), kc);
+      vc = Code::template pack2<false>(Code::prescale(vx[0], va, sv), Code::prescale(vx[1], va, sv), vc);
       if constexpr (E == 4) {
-        kc = f32x2_to_fp8x2<true>(e4m3_prescaled(kx[2], ka, sk), e4m3_prescaled(kx[3], ka, sk), kc);
-        vc = f32x2_to_fp8x2<true>(e4m3_prescaled(vx[2], va, sv), e4m3_prescaled(vx[3], va, sv), vc);
+        kc = Code::template pack2<true>(Code::prescale(kx[2], ka, sk), Code::prescale(kx[3], ka, sk), kc);
+        vc = Code::template pack2<true>(Code::prescale(vx[2], va, sv), Code::prescale(vx[3], va, sv), vc);
       }
       // Score and value from the decoded codes, as stage 1 sees every other row.
       float kd[4], vd[4];
-      fp8x4_to_f32x4(kc, kd);
-      fp8x4_to_f32x4(vc, vd);
+      Code::widen4(kc, kd);
+      Code::widen4(vc, vd);
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) part += qx[e] * kd[e];
@@ -659,32 +662,58 @@ hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const Deco
 }
 
 // One row per request: G is a template value.
-template <int D, bool WINDOW>
+template <int D, bool WINDOW, int F>
 hipError_t launch_stage1_single(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
                                 hipStream_t stream) {
   switch (sh.n_q_heads / pool.n_kv_heads) {
-    case 1: return launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 2: return launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 4: return launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 8: return launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 16: return launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 1: return launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 2: return launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 4: return launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 8: return launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 16: return launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Several rows per request: NT column tiles per workgroup, G at run time.
-template <int D, bool WINDOW>
+template <int D, bool WINDOW, int F>
 hipError_t launch_stage1_multi(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
                                const DecodeGeometry& geo, const DecodeWorkspace& ws, hipStream_t stream) {
   switch (geo.col_tiles) {
-    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW>>(pool, q, sh, qk, geo, ws, 0, stream);
-    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW>>(pool, q, sh, qk, geo, ws, 0, stream);
+    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, 0, stream);
+    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, 0, stream);
     case 4:
-      if constexpr (D == 128) return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW>>(pool, q, sh, qk, geo, ws, 0, stream);
+      if constexpr (D == 128)
+        return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, 0, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
+}
+
+// Head dim and window of one code format.
+template <int F>
+hipError_t launch_stage1_format(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
+                                const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
+                                hipStream_t stream) {
+  const bool window = sh.window > 0;
+  if (sh.n_qrows == 1 && geo.n_col_groups == 1 && geo.col_tiles == 1) {
+    if (pool.head_dim == 128)
+      return window ? launch_stage1_single<128, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                    : launch_stage1_single<128, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    if (pool.head_dim == 256)
+      return window ? launch_stage1_single<256, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                    : launch_stage1_single<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    return hipErrorInvalidValue;
+  }
+  if (key_trim != 0) return hipErrorInvalidValue;
+  if (pool.head_dim == 128)
+    return window ? launch_stage1_multi<128, true, F>(pool, q, sh, qk, geo, ws, stream)
+                  : launch_stage1_multi<128, false, F>(pool, q, sh, qk, geo, ws, stream);
+  if (pool.head_dim == 256)
+    return window ? launch_stage1_multi<256, true, F>(pool, q, sh, qk, geo, ws, stream)
+                  : launch_stage1_multi<256, false, F>(pool, q, sh, qk, geo, ws, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -703,23 +732,8 @@ hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const D
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
                                 hipStream_t stream) {
   const float qk = sm_scale * kLog2e;
-  const bool window = sh.window > 0;
-  if (sh.n_qrows == 1 && geo.n_col_groups == 1 && geo.col_tiles == 1) {
-    if (pool.head_dim == 128)
-      return window ? launch_stage1_single<128, true>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                    : launch_stage1_single<128, false>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    if (pool.head_dim == 256)
-      return window ? launch_stage1_single<256, true>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                    : launch_stage1_single<256, false>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    return hipErrorInvalidValue;
-  }
-  if (key_trim != 0) return hipErrorInvalidValue;
-  if (pool.head_dim == 128)
-    return window ? launch_stage1_multi<128, true>(pool, q, sh, qk, geo, ws, stream)
-                  : launch_stage1_multi<128, false>(pool, q, sh, qk, geo, ws, stream);
-  if (pool.head_dim == 256)
-    return window ? launch_stage1_multi<256, true>(pool, q, sh, qk, geo, ws, stream)
-                  : launch_stage1_multi<256, false>(pool, q, sh, qk, geo, ws, stream);
+  if (pool.format == kInt8) return launch_stage1_format<kInt8>(pool, q, sh, qk, geo, ws, key_trim, stream);
+  if (pool.format == kE4M3) return launch_stage1_format<kE4M3>(pool, q, sh, qk, geo, ws, key_trim, stream);
   return hipErrorInvalidValue;
 }
 
@@ -737,12 +751,19 @@ hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32
                            pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads,
                            (uint32_t)(pool.num_rows - 1), app.sm_scale * kLog2e};
   const dim3 grid((unsigned)((int64_t)batch * n_q_heads));
-  if (pool.head_dim == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128, true>), grid, dim3(kMergeBlock), 0, stream, ws.header, ws.part_o,
-                       ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
-  else if (pool.head_dim == 256)
-    hipLaunchKernelGGL((decode_merge_kernel<256, true>), grid, dim3(kMergeBlock), 0, stream, ws.header, ws.part_o,
-                       ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  const bool i8 = pool.format == kInt8;
+  if (pool.head_dim == 128 && !i8)
+    hipLaunchKernelGGL((decode_merge_kernel<128, true, kE4M3>), grid, dim3(kMergeBlock), 0, stream, ws.header,
+                       ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  else if (pool.head_dim == 128 && i8)
+    hipLaunchKernelGGL((decode_merge_kernel<128, true, kInt8>), grid, dim3(kMergeBlock), 0, stream, ws.header,
+                       ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  else if (pool.head_dim == 256 && !i8)
+    hipLaunchKernelGGL((decode_merge_kernel<256, true, kE4M3>), grid, dim3(kMergeBlock), 0, stream, ws.header,
+                       ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
+  else if (pool.head_dim == 256 && i8)
+    hipLaunchKernelGGL((decode_merge_kernel<256, true, kInt8>), grid, dim3(kMergeBlock), 0, stream, ws.header,
+                       ws.part_o, ws.part_lse, ws.split_stride, n_split, n_q_heads, a, out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

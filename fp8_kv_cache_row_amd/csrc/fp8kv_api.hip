@@ -9,9 +9,10 @@
 #include <string.h>
 
 #include "fp8kv.h"
-#include "fp8kv_launch.h"
+#include "fp8kv_device.h"
 
 static_assert(FP8KV_MAX_SPLITS == FP8KV_MAX_SPLITS_INTERNAL, "split cap mismatch");
+static_assert(FP8KV_CODE_E4M3 == fp8kv::kE4M3 && FP8KV_CODE_INT8 == fp8kv::kInt8, "code format mismatch");
 
 namespace {
 
@@ -38,6 +39,7 @@ fp8kv_status check_pool(const fp8kv_pool_layer* p) {
   if (!p || !p->k_codes || !p->v_codes || !p->k_scales || !p->v_scales) return FP8KV_ERR_INVALID_ARG;
   if (p->num_rows <= 0 || p->num_rows > INT32_MAX || p->n_kv_heads <= 0) return FP8KV_ERR_INVALID_ARG;
   if (p->head_dim != FP8KV_HEAD_DIM && p->head_dim != FP8KV_HEAD_DIM_256) return FP8KV_ERR_UNSUPPORTED;
+  if (p->code_format != FP8KV_CODE_E4M3 && p->code_format != FP8KV_CODE_INT8) return FP8KV_ERR_UNSUPPORTED;
   if (p->code_row_stride < (int64_t)p->n_kv_heads * p->head_dim) return FP8KV_ERR_INVALID_ARG;
   if (p->scale_row_stride < p->n_kv_heads) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(p->k_codes, 16) || !aligned(p->v_codes, 16) || (p->code_row_stride % 16) != 0)
@@ -48,7 +50,7 @@ fp8kv_status check_pool(const fp8kv_pool_layer* p) {
 
 PoolView view_of(const fp8kv_pool_layer* p) {
   return PoolView{p->k_codes, p->v_codes, p->k_scales, p->v_scales, p->code_row_stride, p->scale_row_stride,
-                  p->n_kv_heads, p->head_dim, p->num_rows};
+                  p->n_kv_heads, p->head_dim, p->num_rows, p->code_format};
 }
 
 // Per-device facts, queried once: gfx950 or not, and the compute-unit count.

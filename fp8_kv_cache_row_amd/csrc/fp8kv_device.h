@@ -79,6 +79,55 @@ __device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float* o) {
   o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
 }
 
+// Byte k of w as a signed INT8 code, exactly as f32.
+__device__ __forceinline__ float i8_at(uint32_t w, int k) { return (float)(int8_t)(uint8_t)(w >> (8 * k)); }
+
+// KV code formats (the values of fp8kv_pool_layer.code_format).
+enum CodeFormat : int { kE4M3 = 0, kInt8 = 1 };
+
+// Per-format quantize-on-write and widening.  scale(amax) is the row scale;
+// prescale(x, amax, s) is the value handed to pack2 (E4M3: x/s clamped to the
+// format's range, rounded to nearest even by the hardware convert; INT8: x/s
+// rounded half to even and clamped to +-127); an all-zero row has s = 0 and
+// zero codes.  widen8 turns eight code bytes into an exact bf16x8 MFMA
+// operand (every E4M3FN value and every integer up to 127 is exact in bf16);
+// widen4 gives four f32.
+template <int F>
+struct Codec;
+
+template <>
+struct Codec<kE4M3> {
+  static __device__ __forceinline__ float scale(float amax) { return e4m3_row_scale(amax); }
+  static __device__ __forceinline__ float prescale(float x, float amax, float s) { return e4m3_prescaled(x, amax, s); }
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t pack2(float a, float b, uint32_t old) {
+    return f32x2_to_fp8x2<HI>(a, b, old);
+  }
+  static __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) { return fp8x8_to_bf16x8(lo, hi); }
+  static __device__ __forceinline__ void widen4(uint32_t w, float* o) { fp8x4_to_f32x4(w, o); }
+};
+
+template <>
+struct Codec<kInt8> {
+  static __device__ __forceinline__ float scale(float amax) { return amax / 127.0f; }
+  static __device__ __forceinline__ float prescale(float x, float amax, float s) {
+    return (amax == 0.0f) ? 0.0f : __builtin_rintf(fminf(fmaxf(x / s, -127.0f), 127.0f));
+  }
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t pack2(float a, float b, uint32_t old) {
+    const uint32_t v = ((uint32_t)(int)a & 0xffu) | (((uint32_t)(int)b & 0xffu) << 8);
+    return HI ? ((old & 0x0000ffffu) | (v << 16)) : ((old & 0xffff0000u) | v);
+  }
+  static __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
+    const uint4 u = make_uint4(f32x2_to_bf16x2(i8_at(lo, 0), i8_at(lo, 1)), f32x2_to_bf16x2(i8_at(lo, 2), i8_at(lo, 3)),
+                               f32x2_to_bf16x2(i8_at(hi, 0), i8_at(hi, 1)), f32x2_to_bf16x2(i8_at(hi, 2), i8_at(hi, 3)));
+    return __builtin_bit_cast(bf16x8, u);
+  }
+  static __device__ __forceinline__ void widen4(uint32_t w, float* o) {
+    o[0] = i8_at(w, 0); o[1] = i8_at(w, 1); o[2] = i8_at(w, 2); o[3] = i8_at(w, 3);
+  }
+};
+
 // v_mfma_f32_16x16x32_bf16: D(16x16) += A(16x32) * B(32x16).
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, each as eight
 // consecutive k-slots of k-group (l / 16); it receives D rows 4*(l/16)+i,

@@ -20,6 +20,7 @@ struct PoolView {
   int32_t n_kv_heads;
   int32_t head_dim;  // 128 or 256
   int64_t num_rows;
+  int32_t format;    // CodeFormat: 0 E4M3FN, 1 INT8
 };
 
 // Decode launch geometry: each workgroup covers `chunk` consecutive keys of

@@ -19,7 +19,8 @@ namespace {
 constexpr int kBlock = 256;
 
 // Rows are enumerated as ((token * 2 + kv) * n_kv_heads + head), kv 0 = K, 1 = V.
-template <int D>
+// F is the code format (E4M3FN, or the symmetric INT8 counterpart).
+template <int D, int F>
 __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_token_stride,
     const int32_t* __restrict__ slots, int64_t n_rows, int32_t n_kv_heads, uint8_t* __restrict__ k_codes,
@@ -46,14 +47,15 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kLanesPerRow));
 
-  const float s = e4m3_row_scale(amax);
+  using C = Codec<F>;
+  const float s = C::scale(amax);
   float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = e4m3_prescaled(x[i], amax, s);
-  uint32_t lo = f32x2_to_fp8x2<false>(y[0], y[1], 0u);
-  lo = f32x2_to_fp8x2<true>(y[2], y[3], lo);
-  uint32_t hi = f32x2_to_fp8x2<false>(y[4], y[5], 0u);
-  hi = f32x2_to_fp8x2<true>(y[6], y[7], hi);
+  for (int i = 0; i < 8; ++i) y[i] = C::prescale(x[i], amax, s);
+  uint32_t lo = C::template pack2<false>(y[0], y[1], 0u);
+  lo = C::template pack2<true>(y[2], y[3], lo);
+  uint32_t hi = C::template pack2<false>(y[4], y[5], 0u);
+  hi = C::template pack2<true>(y[6], y[7], hi);
 
   const int64_t slot = min((uint32_t)slots[t], max_row);  // out-of-range slots are clamped, never followed
   uint8_t* dst = (kv ? v_codes : k_codes) + slot * code_row_stride + (int64_t)g * D + sub * 8;
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_kernel(
 // ws[j][head][d] = bf16_rne(fl32(decode(code) * scale)).
 constexpr int kLanesPerRow = kHeadDim / 8;
 constexpr int kRowsPerBlock = kBlock / kLanesPerRow;
+template <int F>
 __global__ __launch_bounds__(kBlock) void reconstruct_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, int64_t code_row_stride,
@@ -83,8 +86,8 @@ __global__ __launch_bounds__(kBlock) void reconstruct_kernel(
   const uint2 c = *reinterpret_cast<const uint2*>(src);
   const float s = (kv ? v_scales : k_scales)[prow * scale_row_stride + g];
   float f[8];
-  fp8x4_to_f32x4(c.x, f);
-  fp8x4_to_f32x4(c.y, f + 4);
+  Codec<F>::widen4(c.x, f);
+  Codec<F>::widen4(c.y, f + 4);
   uint4 o;
   o.x = f32x2_to_bf16x2(f[0] * s, f[1] * s);
   o.y = f32x2_to_bf16x2(f[2] * s, f[3] * s);
@@ -94,6 +97,16 @@ __global__ __launch_bounds__(kBlock) void reconstruct_kernel(
   *reinterpret_cast<uint4*>(dst) = o;
 }
 
+template <int D, int F>
+void launch_quantize_df(const PoolView& pool, const uint16_t* k, const uint16_t* v, int64_t src_token_stride,
+                        const int32_t* slots, int64_t n_rows, hipStream_t stream) {
+  constexpr int rows_per_block = kBlock / (D / 8);
+  const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((quantize_rows_kernel<D, F>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
+                     src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes, pool.k_scales,
+                     pool.v_scales, pool.code_row_stride, pool.scale_row_stride, (uint32_t)(pool.num_rows - 1));
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const uint16_t* v,
@@ -101,18 +114,13 @@ hipError_t launch_quantize_rows(const PoolView& pool, const uint16_t* k, const u
                                 hipStream_t stream) {
   const int64_t n_rows = (int64_t)n_tokens * 2 * pool.n_kv_heads;
   if (n_rows == 0) return hipSuccess;
-  const int rows_per_block = kBlock / (pool.head_dim / 8);
-  const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+  const bool i8 = pool.format == kInt8;
   if (pool.head_dim == 128)
-    hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
-                       src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
-                       pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride,
-                       (uint32_t)(pool.num_rows - 1));
+    i8 ? launch_quantize_df<128, kInt8>(pool, k, v, src_token_stride, slots, n_rows, stream)
+       : launch_quantize_df<128, kE4M3>(pool, k, v, src_token_stride, slots, n_rows, stream);
   else if (pool.head_dim == 256)
-    hipLaunchKernelGGL(quantize_rows_kernel<256>, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k, v,
-                       src_token_stride, slots, n_rows, pool.n_kv_heads, pool.k_codes, pool.v_codes,
-                       pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride,
-                       (uint32_t)(pool.num_rows - 1));
+    i8 ? launch_quantize_df<256, kInt8>(pool, k, v, src_token_stride, slots, n_rows, stream)
+       : launch_quantize_df<256, kE4M3>(pool, k, v, src_token_stride, slots, n_rows, stream);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -124,10 +132,10 @@ hipError_t launch_reconstruct(const PoolView& pool, const int32_t* prefix_rows, 
   if (n_rows == 0) return hipSuccess;
   if (pool.head_dim != kHeadDim) return hipErrorInvalidValue;
   const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(reconstruct_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, pool.k_codes,
-                     pool.v_codes, pool.k_scales, pool.v_scales, pool.code_row_stride,
-                     pool.scale_row_stride, prefix_rows, n_rows, pool.n_kv_heads, (uint32_t)(pool.num_rows - 1), ws_k,
-                     ws_v);
+  auto kernel = pool.format == kInt8 ? reconstruct_kernel<kInt8> : reconstruct_kernel<kE4M3>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, pool.k_codes, pool.v_codes,
+                     pool.k_scales, pool.v_scales, pool.code_row_stride, pool.scale_row_stride, prefix_rows, n_rows,
+                     pool.n_kv_heads, (uint32_t)(pool.num_rows - 1), ws_k, ws_v);
   return hipGetLastError();
 }
 

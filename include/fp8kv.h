@@ -52,11 +52,14 @@ extern "C" {
 #define FP8KV_MAX_SPLITS 256
 /* Upper bound on query rows per request in one decode call. */
 #define FP8KV_MAX_QUERY_ROWS 8
+/* Code formats of a pool (fp8kv_pool_layer.code_format). */
+#define FP8KV_CODE_E4M3 0 /* OCP E4M3FN, scale amax / 448 */
+#define FP8KV_CODE_INT8 1 /* symmetric INT8, scale amax / 127 */
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
     FP8KV_ERR_INVALID_ARG = 1, /* null pointer, non-positive or inconsistent size */
-    FP8KV_ERR_UNSUPPORTED = 2, /* head_dim not 128/256 (128 for prefill), GQA ratio, not gfx950 */
+    FP8KV_ERR_UNSUPPORTED = 2, /* head_dim not 128/256 (128 for prefill), code format, GQA ratio, not gfx950 */
     FP8KV_ERR_ALIGNMENT = 3,   /* a base pointer or stride breaks the alignment contract */
     FP8KV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
     FP8KV_ERR_HIP = 5          /* the HIP runtime rejected a launch or a query */
@@ -73,7 +76,12 @@ typedef enum fp8kv_status {
  *   V codes   v_codes  + r * code_row_stride + g * D     (D bytes)
  *   K scale   k_scales[r * scale_row_stride + g]         (fp32)
  *   V scale   v_scales[r * scale_row_stride + g]         (fp32)
- * Value of element d: decode_e4m3fn(code[d]) * scale.
+ * Value of element d: decode(code[d]) * scale, where decode is the OCP E4M3FN
+ * value of the byte (code_format FP8KV_CODE_E4M3) or the byte read as a
+ * two's-complement integer (FP8KV_CODE_INT8: the pages list INT8 KV beside
+ * FP8, FreeToken PR #897 description and "Regression and CUDA isolation";
+ * this library takes it as the symmetric per-row counterpart, scale
+ * amax / 127, codes in [-127, 127]).
  *
  * Alignment contract (FreeToken PR #897 description: packed reads need
  * 16-byte-aligned bases and row/head strides): k_codes, v_codes and
@@ -92,6 +100,8 @@ typedef struct fp8kv_pool_layer {
     int32_t head_dim;         /* FP8KV_HEAD_DIM or FP8KV_HEAD_DIM_256 */
     int64_t code_row_stride;  /* bytes between rows of k_codes / v_codes */
     int64_t scale_row_stride; /* floats between rows of k_scales / v_scales */
+    int32_t code_format;      /* FP8KV_CODE_E4M3 (0) or FP8KV_CODE_INT8 */
+    int32_t reserved;         /* must be 0 */
 } fp8kv_pool_layer;
 
 /*
@@ -104,7 +114,9 @@ typedef struct fp8kv_pool_layer {
  *   amax = max_d |x_d|;   s = fl32(amax / 448)   (IEEE fp32 division)
  *   code_d = E4M3FN round-to-nearest-even of fl32(x_d / s), saturated to +-448
  *   (a row with amax == 0 stores s = 0 and codes +0 / -0 following x_d's sign)
- * and stores the codes and s at physical row slots[t].
+ * and stores the codes and s at physical row slots[t].  An INT8 pool stores
+ *   s = fl32(amax / 127),  code_d = round-half-even(fl32(x_d / s)) clamped to
+ *   [-127, 127]  (amax == 0: s = 0, codes 0).
  *
  * k, v:            device bf16 [n_tokens][n_kv_heads][D] with token stride
  *                  src_token_stride elements (>= n_kv_heads*D, a multiple of

@@ -48,9 +48,10 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str):
     return rel, mab
 
 
-def build_pool(case, layout: str = "separate") -> fk.Fp8KvPool:
+def build_pool(case, layout: str = "separate", fmt: str = "e4m3") -> fk.Fp8KvPool:
     """Quantize every pool row of a DecodeCase through the HIP path (row r -> slot r)."""
-    pool = fk.Fp8KvPool(case.pool_rows, case.n_kv_heads, layout=layout, device=DEV, head_dim=case.head_dim)
+    pool = fk.Fp8KvPool(case.pool_rows, case.n_kv_heads, layout=layout, device=DEV, head_dim=case.head_dim,
+                        code_format=fmt)
     slots = torch.arange(case.pool_rows, dtype=torch.int32, device=DEV)
     fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.k_rows), to_dev_bf16(case.v_rows), slots)
     return pool
@@ -72,9 +73,9 @@ def assert_bits_equal(a: np.ndarray, b: np.ndarray, what: str):
     assert bad == 0, f"{what}: {bad} of {a.size} elements differ"
 
 
-def oracle_pool(case):
-    kc, ks = oracle.quantize_rows(case.k_rows)
-    vc, vs = oracle.quantize_rows(case.v_rows)
+def oracle_pool(case, fmt: str = "e4m3"):
+    kc, ks = oracle.quantize_rows(case.k_rows, fmt)
+    vc, vs = oracle.quantize_rows(case.v_rows, fmt)
     return kc, vc, ks, vs
 
 

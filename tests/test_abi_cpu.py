@@ -27,6 +27,15 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_pool_struct_matches_the_header():
+    """The ctypes mirror has the C struct's size and field offsets."""
+    assert ctypes.sizeof(B.PoolLayer) == 72
+    offs = {name: getattr(B.PoolLayer, name).offset for name, _ in B.PoolLayer._fields_}
+    assert offs == {"k_codes": 0, "v_codes": 8, "k_scales": 16, "v_scales": 24, "num_rows": 32, "n_kv_heads": 40,
+                    "head_dim": 44, "code_row_stride": 48, "scale_row_stride": 56, "code_format": 64,
+                    "reserved": 68}
+
+
 def test_status_strings(lib):
     for s in range(6):
         assert B.status_string(s).startswith("FP8KV_")
@@ -35,10 +44,11 @@ def test_status_strings(lib):
 
 def _pool(**kw):
     p = dict(k_codes=A, v_codes=2 * A, k_scales=3 * A, v_scales=4 * A, num_rows=100, n_kv_heads=4,
-             head_dim=128, code_row_stride=512, scale_row_stride=4)
+             head_dim=128, code_row_stride=512, scale_row_stride=4, code_format=0)
     p.update(kw)
     return B.PoolLayer(p["k_codes"], p["v_codes"], p["k_scales"], p["v_scales"], p["num_rows"],
-                       p["n_kv_heads"], p["head_dim"], p["code_row_stride"], p["scale_row_stride"])
+                       p["n_kv_heads"], p["head_dim"], p["code_row_stride"], p["scale_row_stride"],
+                       p["code_format"], 0)
 
 
 def _quant(lib, pool, k=A, v=A, stride=512, slots=A, n=4):
@@ -69,6 +79,8 @@ def test_quantize_validation(lib):
     assert lib.fp8kv_quantize_rows(None, A, A, 512, A, 4, None) == INVALID
     assert _quant(lib, _pool(k_codes=0)) == INVALID
     assert _quant(lib, _pool(head_dim=64)) == UNSUPPORTED
+    assert _quant(lib, _pool(code_format=2)) == UNSUPPORTED
+    assert _quant(lib, _pool(code_format=-1)) == UNSUPPORTED
     assert _quant(lib, _pool(head_dim=192, code_row_stride=768)) == UNSUPPORTED
     assert _quant(lib, _pool(head_dim=256)) == INVALID               # code_row_stride 512 < 4 * 256
     assert _quant(lib, _pool(head_dim=256, code_row_stride=1024)) == INVALID  # token stride 512 < 4 * 256
@@ -203,6 +215,7 @@ def test_valid_arguments_reach_the_device_check(lib):
     fails (no GPU here) with FP8KV_ERR_HIP; only runs where no device is visible."""
     assert _quant(lib, _pool()) == HIP
     assert _decode(lib, _pool()) == HIP
+    assert _decode(lib, _pool(code_format=1)) == HIP
     assert _decode(lib, _pool(head_dim=256, code_row_stride=1024)) == HIP
     assert _rows(lib, _pool(), nq=8, window=17) == HIP
     assert _prefill(lib, _pool()) == HIP

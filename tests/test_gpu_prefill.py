@@ -13,10 +13,10 @@ pytestmark = pytest.mark.gpu
 D = 128
 
 
-def _run(case, layout="separate", q_idx=None, check_ws=True):
+def _run(case, layout="separate", q_idx=None, check_ws=True, fmt="e4m3"):
     """Quantize the prefix into the pool, run prefill, then quantize the chunk; compare."""
     P, T, H = case.prefix_k.shape[0], case.q.shape[0], case.n_kv_heads
-    pool = fk.Fp8KvPool(case.pool_rows, H, layout=layout, device=DEV)
+    pool = fk.Fp8KvPool(case.pool_rows, H, layout=layout, device=DEV, code_format=fmt)
     if P:
         fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.prefix_k), to_dev_bf16(case.prefix_v), to_dev(case.prefix_rows))
     ws_k = torch.empty((max(P, 1), H, D), dtype=torch.bfloat16, device=DEV)
@@ -27,21 +27,21 @@ def _run(case, layout="separate", q_idx=None, check_ws=True):
     torch.cuda.synchronize()
 
     # oracle: its own codes, its own reconstruction, fp64 attention
-    okc, oks = oracle.quantize_rows(case.prefix_k)
-    ovc, ovs = oracle.quantize_rows(case.prefix_v)
+    okc, oks = oracle.quantize_rows(case.prefix_k, fmt)
+    ovc, ovs = oracle.quantize_rows(case.prefix_v, fmt)
     R = case.pool_rows
     pk = np.zeros((R, H, D), np.uint8)
     pv = np.zeros((R, H, D), np.uint8)
     sk = np.zeros((R, H), np.float32)
     sv = np.zeros((R, H), np.float32)
     pk[case.prefix_rows], pv[case.prefix_rows], sk[case.prefix_rows], sv[case.prefix_rows] = okc, ovc, oks, ovs
-    ows_k = oracle.reconstruct(pk, sk, case.prefix_rows, H) if P else None
-    ows_v = oracle.reconstruct(pv, sv, case.prefix_rows, H) if P else None
+    ows_k = oracle.reconstruct(pk, sk, case.prefix_rows, H, fmt) if P else None
+    ows_v = oracle.reconstruct(pv, sv, case.prefix_rows, H, fmt) if P else None
     if P and check_ws:
         assert_bits_equal(ws_k[:P].view(torch.int16).cpu().numpy().view(np.uint16), ows_k, "ws_k")
         assert_bits_equal(ws_v[:P].view(torch.int16).cpu().numpy().view(np.uint16), ows_v, "ws_v")
     # the chunk's own rows landed in the pool bit-exactly
-    ck, cs = oracle.quantize_rows(case.k_cur)
+    ck, cs = oracle.quantize_rows(case.k_cur, fmt)
     kc_dev, _ = pool.codes()
     ks_dev, _ = pool.scales()
     assert_bits_equal(kc_dev.cpu().numpy()[case.chunk_slots], ck, "chunk K codes")
@@ -79,3 +79,20 @@ def test_chunked_prefill_8k_prefix_8k_chunk():
     idx = np.unique(np.concatenate([np.arange(0, T, 256), np.arange(T - 8, T)]))
     got, ref = _run(case, q_idx=idx)
     assert_close(got, ref, "8K+8K sampled")
+
+
+@pytest.mark.parametrize("P,T,Hq,Hkv", [(0, 37, 32, 4), (100, 37, 32, 4), (257, 130, 16, 4), (1000, 300, 8, 8)])
+def test_small_prefills_int8_pool(P, T, Hq, Hkv):
+    say(f"prefill over an INT8 pool P={P} T={T} Hq={Hq} Hkv={Hkv}")
+    case = wl.chunked_prefill(seed=P + T + 1, n_prefix=P, n_chunk=T, n_q_heads=Hq, n_kv_heads=Hkv)
+    got, ref = _run(case, fmt="int8")
+    assert_close(got, ref, f"int8 P={P} T={T}")
+
+
+def test_chunked_prefill_8k_prefix_8k_chunk_int8_pool():
+    say("prefill 8K prefix + 8K chunk over an INT8 pool (sampled rows vs oracle)")
+    case = wl.chunked_prefill(2)
+    T = case.q.shape[0]
+    idx = np.unique(np.concatenate([np.arange(0, T, 512), np.arange(T - 4, T)]))
+    got, ref = _run(case, q_idx=idx, fmt="int8", layout="interleaved")
+    assert_close(got, ref, "int8 8K+8K sampled")
