@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) instead")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8K-prefix + 8K-chunk prefill timing")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the head-dim-256, multi-row and sliding-window decode timings")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run plain 64 MiB device copies (a known-size kernel for HBM byte counters)")
     return ap.parse_args()
@@ -134,6 +136,138 @@ def prefill_timing(fk, wl, dev, reps: int = 5):
             "reconstruct_plus_attention_ms": round(ms, 4), "attention_flop": flop,
             "tflops": round(tflops, 2), "mfma_bf16_frac_of_2500": round(tflops / 2500.0, 4),
             "quantize_chunk_us": round(qms * 1e3, 3)}
+
+
+def capture_graph(stream, body, n):
+    """A HIP graph of n calls body(i) on `stream` (after one untimed eager pass)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            body(i)
+    stream.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n):
+            body(i)
+    return g
+
+
+def time_graph(stream, g, per_graph, total, warmup):
+    """ms per call of a graph holding per_graph calls, replayed to >= total calls;
+    HIP events on the graph's stream."""
+    import torch
+    reps = max(1, -(-total // per_graph))
+    for _ in range(max(1, -(-warmup // per_graph))):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * per_graph), reps * per_graph
+
+
+def rotated_pools(fk, case, layout, n, dev, bf, fmt="e4m3"):
+    """n identical copies of a case's quantized pool (cold HBM when rotated)."""
+    import torch
+    base = fk.Fp8KvPool(case.pool_rows, case.n_kv_heads, layout=layout, device=dev, head_dim=case.head_dim,
+                        code_format=fmt)
+    fk.fp8kv_quantize_rows(base, bf(case.k_rows), bf(case.v_rows),
+                           torch.arange(case.pool_rows, dtype=torch.int32, device=dev))
+    pools = [base]
+    for _ in range(n - 1):
+        p = fk.Fp8KvPool(case.pool_rows, case.n_kv_heads, layout=layout, device=dev, head_dim=case.head_dim,
+                         code_format=fmt)
+        for dst, src in zip(p._buffers, base._buffers):
+            dst.copy_(src)
+        pools.append(p)
+    torch.cuda.synchronize()
+    return pools
+
+
+def variants_timing(fk, wl, dev, args, bf):
+    """The decode variants at 32K context, each over rotated cold pools:
+    head dim 256 (fused append step and stage 1 alone), 3 and 8 causal query
+    rows per request, an odd 4,095-key sliding window, and the INT8 KV
+    format (fused append step and stage 1 alone)."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.Stream(device=dev)
+    n = max(1, args.pools)
+    steps = max(48, args.steps // 2)
+    res = {}
+
+    def run(name, case, body_for, kv_bytes, flop=None, extra=None, fmt="e4m3"):
+        pools = rotated_pools(fk, case, args.layout, n, dev, bf, fmt)
+        body = body_for(case, pools)
+        g = capture_graph(stream, body, n)
+        ms, _ = time_graph(stream, g, n, steps, args.warmup)
+        gbps = kv_bytes / (ms * 1e-3) / 1e9
+        r = {"us": round(ms * 1e3, 3), "kv_bytes": kv_bytes, "kv_gbps": round(gbps, 1),
+             "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        if flop:
+            r["flop"] = flop
+            r["tflops"] = round(flop / (ms * 1e-3) / 1e12, 2)
+        if extra:
+            r.update(extra)
+        res[name] = r
+        del pools, g
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    def append_body(case, pools):
+        q, nk, nv = bf(case.q), bf(case.new_k), bf(case.new_v)
+        t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
+        slot = torch.from_numpy(case.table[:, -1].copy()).to(dev)
+        ws = fk.decode_workspace(1, case.n_q_heads, device=dev, head_dim=case.head_dim)
+        out = torch.empty_like(q)
+        return lambda i: fk.fp8kv_decode_attn_append(pools[i % n], q, nk, nv, slot, t, sl, case.max_seq_len,
+                                                     case.sm_scale, workspace=ws, out=out, stream=stream)
+
+    def stage1_body(case, pools):
+        q = bf(case.q)
+        t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
+        ws = fk.decode_workspace(1, case.n_q_heads, device=dev, head_dim=case.head_dim)
+        return lambda i: fk.fp8kv_decode_stage1(pools[i % n], q, t, sl, case.max_seq_len, case.sm_scale,
+                                                workspace=ws, stream=stream)
+
+    def rows_body(window):
+        def make(case, pools):
+            q = bf(case.q if case.q.ndim == 4 else case.q[:, None])
+            t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
+            ws = fk.decode_workspace(q.shape[1], case.n_q_heads, device=dev, head_dim=case.head_dim)
+            out = torch.empty_like(q)
+            return lambda i: fk.fp8kv_decode_attn_rows(pools[i % n], q, t, sl, case.max_seq_len, case.sm_scale,
+                                                       window=window, workspace=ws, out=out, stream=stream)
+        return make
+
+    c256 = wl.layer_decode(0, head_dim=256)
+    kv256 = c256.max_seq_len * c256.n_kv_heads * 2 * (256 + 4)
+    run("d256_append_step", c256, append_body, kv256,
+        extra={"workload": "32K-context GQA-8 decode step at head dim 256 (32 q / 4 KV heads)"})
+    run("d256_stage1", c256, stage1_body, kv256)
+    del c256
+    for nq in (3, 8):
+        c = wl.layer_decode(0, with_new_token=False, n_qrows=nq)
+        kv = c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+        L = c.max_seq_len
+        pairs = nq * L - nq * (nq - 1) // 2          # causal (row, key) pairs per head
+        run(f"rows{nq}", c, rows_body(0), kv, flop=4.0 * 128 * pairs * c.n_q_heads,
+            extra={"workload": f"32K-context GQA-8 decode, {nq} causal query rows per request"})
+    c = wl.layer_decode(0)
+    kv = c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+    run("int8_append_step", c, append_body, kv, fmt="int8",
+        extra={"workload": "32K-context GQA-8 decode step over an INT8 pool (scale amax/127)"})
+    run("int8_stage1", c, stage1_body, kv, fmt="int8")
+    c = wl.layer_decode(0, with_new_token=False)
+    W = 4095
+    run("window4095", c, rows_body(W), W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
+        extra={"workload": "32K-context GQA-8 decode with a 4,095-key sliding window"})
+    return res
 
 
 def calibration_copies(dev, mib: int = 64, n: int = 4):
@@ -258,31 +392,10 @@ def main():
             raise B.Fp8KvError(st, "decode step (three calls)")
 
     def capture(body, n):
-        """A HIP graph of n calls body(i) on `stream`."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for i in range(n):          # untimed eager pass (also allocator warm-up)
-                body(i)
-        stream.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
-                body(i)
-        return g
+        return capture_graph(stream, body, n)
 
     def timed(g, per_graph, total):
-        reps = max(1, -(-total // per_graph))
-        for _ in range(max(1, -(-args.warmup // per_graph))):
-            g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * per_graph), reps * per_graph  # ms per call
+        return time_graph(stream, g, per_graph, total, args.warmup)  # ms per call
 
     per = n_pools if n_pools > 1 else 12
     g_step = capture(step, per)
@@ -349,6 +462,11 @@ def main():
     }
     if not args.no_prefill:
         res["prefill"] = prefill_timing(fk, wl, dev)
+    if not args.no_variants:
+        del g_step, g_step3, g_s1, g_m, g_q, pools
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res["variants"] = variants_timing(fk, wl, dev, args, bf)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(res), flush=True)
