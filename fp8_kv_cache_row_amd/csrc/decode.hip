@@ -71,7 +71,7 @@ struct Stage1 {
   // waves (one per SIMD, 512 registers each) instead of 8.
   static constexpr int kWaves = (NT * D >= 512) ? 4 : kDecodeWaves;
   static constexpr int kBlock = kWaves * kWave;
-  static constexpr int kSteps = (D == 128 && NT == 1) ? kDecodeTilesPerWave : 1;  // 32-key steps loaded at once
+  static constexpr int kSteps = (D == 128 || kWaves == 4) ? kDecodeTilesPerWave : 1;  // 32-key steps loaded at once
   static constexpr int kGroupKeys = kSteps * kDecodeTileKeys;
   // Row indices and scales are loaded one key per lane; a 32-key group leaves
   // the upper half-wave reading duplicates into padding.
@@ -726,7 +726,19 @@ hipError_t launch_merge_d(int64_t n_rows_heads, const DecodeWorkspace& ws, int32
 
 }  // namespace
 
-int32_t decode_max_col_tiles(int32_t head_dim) { return head_dim == 128 ? 4 : 2; }
+// Column tiles per workgroup: beyond them, further column groups re-read the
+// rows (mostly from L2).  At D = 128, two 8-wave workgroups of 2 tiles beat
+// one 4-wave workgroup of 4 tiles (64 columns, 32K keys: 23.9 vs 26.6 us):
+// the wide shape's 512 registers per wave leave one wave per SIMD.
+#ifndef FP8KV_DECODE_MAX_TILES_128
+#define FP8KV_DECODE_MAX_TILES_128 2
+#endif
+#ifndef FP8KV_DECODE_MAX_TILES_256
+#define FP8KV_DECODE_MAX_TILES_256 2
+#endif
+int32_t decode_max_col_tiles(int32_t head_dim) {
+  return head_dim == 128 ? FP8KV_DECODE_MAX_TILES_128 : FP8KV_DECODE_MAX_TILES_256;
+}
 
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float sm_scale,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
