@@ -2,6 +2,8 @@
 and every host-side validation error comes back as its status code before any
 HIP call is made."""
 import ctypes
+import os
+import subprocess
 
 import pytest
 import torch
@@ -223,3 +225,16 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert lib.fp8kv_decode_stage1(ctypes.byref(_pool()), A, 1, 32, A, 1024, A, 1000, 0.088, 0, A, wsb, None) == HIP
     assert lib.fp8kv_decode_merge(1, 32, 128, 0, A, wsb, A, None) == HIP
     assert _append(lib, _pool()) == HIP
+
+
+def test_header_is_plain_c99_and_the_library_links(tmp_path, lib):
+    """A C99 program compiled with -Wall -Werror against include/fp8kv.h, linked
+    to libfp8kv.so, runs the host-side validation paths (no device work)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    pkg = os.path.dirname(B.lib_path())
+    exe = tmp_path / "abi_from_c"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                    os.path.dirname(B.header_path()), os.path.join(here, "c", "abi_from_c.c"), "-o", str(exe),
+                    "-L", pkg, "-lfp8kv", f"-Wl,-rpath,{pkg}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "abi_from_c: ok" in r.stdout, r.stdout + r.stderr
