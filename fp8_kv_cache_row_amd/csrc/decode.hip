@@ -439,9 +439,12 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
 // The workgroup of the group's first query head writes the codes and scales
 // to the token's row new_slots[b]; every load of the kernel is independent
 // (one round trip).
-constexpr int kMergeBlock = 256;
-constexpr int kMergeWaves = kMergeBlock / kWave;
-constexpr int kMergeBatch = 16;  // splits per wave loaded at once
+#ifndef FP8KV_MERGE_WAVES
+#define FP8KV_MERGE_WAVES 8
+#endif
+constexpr int kMergeWaves = FP8KV_MERGE_WAVES;
+constexpr int kMergeBlock = kMergeWaves * kWave;
+constexpr int kMergeBatch = 64 / kMergeWaves;  // splits per wave loaded at once (64 per workgroup)
 static_assert(FP8KV_MAX_SPLITS_INTERNAL <= kMergeWaves * kMergeBatch * 4, "merge passes stay few");
 
 struct AppendKernelArgs {
