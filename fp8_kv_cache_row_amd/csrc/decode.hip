@@ -6,7 +6,11 @@
 // (page size 1, randomized physical slots) and a merge kernel combines the
 // partials.  FreeToken PR #853 "What changes": per-row FP32 scales.
 //
-// gfx950 design (not the pages' RDNA4 kernel):
+// gfx950 design (not the pages' RDNA4 kernel), described for the headline
+// shape (one query row per request, head dim 128, E4M3 codes); the template
+// parameters below generalize it to head dim 256, several query rows per
+// request (FreeToken PR #897 description: #900's multi-row decode), a sliding
+// key window and INT8 codes ("Regression and CUDA isolation" lists all four):
 //  * A workgroup (8 waves) covers one split of one (request, KV head); a wave
 //    takes two 32-key steps at a time.  The request length is read with a
 //    vector load next to the first (speculative, host-bounded) table read, so
@@ -14,13 +18,14 @@
 //    group is fetched.
 //  * Every lane loads exactly the code bytes its MFMA operands need, straight
 //    into registers: for keys on the MFMA rows, 16-byte K chunks; for the P*V
-//    contraction, 8 bytes of V per key, 16 lanes covering one whole 128-byte V
-//    row.  All loads of both steps are in flight before the first wait; only
-//    row indices and scales pass through LDS.
+//    contraction, D/16 bytes of V per key, 16 lanes covering one whole V row.
+//    All loads of a group are in flight before the first wait; only row
+//    indices and scales pass through LDS.
 //  * QK^T runs on the bf16 MFMA 16x16x32 with E4M3 (or INT8) codes widened
-//    exactly to bf16.  S^T = K * Q^T puts keys on the MFMA rows and the G query heads of
-//    the group on the columns, so each lane holds 8 keys of one head: the
-//    per-head maximum needs two cross-lane steps, and those 8 keys are exactly
+//    exactly to bf16.  S^T = K * Q^T puts keys on the MFMA rows and the
+//    columns -- the G query heads of the group, or (query row, head) pairs --
+//    on the MFMA columns, so each lane holds 8 keys of one column: the
+//    column maximum needs two cross-lane steps, and those 8 keys are exactly
 //    the k-slots this lane feeds to the P*V MFMA, so P never moves between
 //    lanes.  The per-row K scale and the softmax scale multiply the score tile
 //    after the MFMA; the per-row V scale is folded into P.
@@ -425,11 +430,12 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
 }
 
 // Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) over the
-// splits of (b, h).  One workgroup per (request, query row, query head); wave w
-// takes splits w, w+4, ...: it loads their lse and o vectors together
-// (clamped indices, no branches), keeps its own maximum, and the four waves
-// combine through LDS -- a single memory round trip.  Lane l owns
-// d = E*l .. E*l + E-1 (E = D / 64).
+// splits of (b, h).  One workgroup per (request, query row, query head) of
+// W waves (8; 2, 4 and 16 were measured slower on the 32K step); wave w takes
+// splits w, w+W, ...: it loads their lse and o vectors together (clamped
+// indices, no branches), keeps its own maximum, and the waves combine through
+// LDS -- a single memory round trip.  Lane l owns d = E*l .. E*l + E-1
+// (E = D / 64).
 //
 // With APPEND (one query row per request), wave 0 also takes the request's
 // new token (position seq_lens[b] - 1, left out of stage 1): it quantizes the
