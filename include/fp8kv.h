@@ -163,8 +163,11 @@ size_t fp8kv_decode_workspace_bytes(int32_t n_queries, int32_t n_q_heads, int32_
  *
  * q:            device bf16 [batch][n_q_heads][D], contiguous, 16-byte aligned
  *               (D = pool->head_dim).
- * row_table:    device int32, row b at row_table + b * table_stride.
- *               Entries below seq_lens[b] name the request's rows.  Entries
+ * row_table:    device int32, row b at row_table + b * table_stride; all
+ *               batch * table_stride entries must be readable (the kernels
+ *               read entries up to max(max_seq_len, 1) of a row before the
+ *               length is known).  Entries below seq_lens[b] name the
+ *               request's rows.  Entries
  *               in [seq_lens[b], max_seq_len) (padding) are read and masked
  *               out (weight 0).  Every kernel clamps a row index to
  *               [0, num_rows) before using it (an out-of-range entry reads
