@@ -192,8 +192,9 @@ def rotated_pools(fk, case, layout, n, dev, bf, fmt="e4m3"):
 def variants_timing(fk, wl, dev, args, bf):
     """The decode variants at 32K context, each over rotated cold pools:
     head dim 256 (fused append step and stage 1 alone), 3 and 8 causal query
-    rows per request, an odd 4,095-key sliding window, and the INT8 KV
-    format (fused append step and stage 1 alone)."""
+    rows per request, an odd 4,095-key sliding window, the INT8 KV format
+    (fused append step and stage 1 alone), and the 48-layer step at 40,000
+    context."""
     import numpy as np
     import torch
     stream = torch.cuda.Stream(device=dev)
@@ -263,6 +264,32 @@ def variants_timing(fk, wl, dev, args, bf):
     run("int8_append_step", c, append_body, kv, fmt="int8",
         extra={"workload": "32K-context GQA-8 decode step over an INT8 pool (scale amax/127)"})
     run("int8_stage1", c, stage1_body, kv, fmt="int8")
+    # the 48-layer step at 40,000 context: one fused call per layer over 48
+    # distinct 40,290-row pools (2 GB, larger than the Infinity Cache, so every
+    # layer reads its rows from HBM); one layer's draws are copied into all
+    # 48 pools, which does not change the timing
+    table = wl.model_step_table(0)
+    c = wl.model_step_layer(0, table)
+    layers = 48
+    pools = rotated_pools(fk, c, args.layout, layers, dev, bf)
+    q, nk, nv = bf(c.q), bf(c.new_k), bf(c.new_v)
+    t, sl = torch.from_numpy(c.table).to(dev), torch.from_numpy(c.seq_lens).to(dev)
+    slot = torch.from_numpy(c.table[:, -1].copy()).to(dev)
+    ws = fk.decode_workspace(1, c.n_q_heads, device=dev)
+    out = torch.empty_like(q)
+    g = capture_graph(stream, lambda i: fk.fp8kv_decode_attn_append(pools[i], q, nk, nv, slot, t, sl, c.max_seq_len,
+                                                                    c.sm_scale, workspace=ws, out=out, stream=stream),
+                      layers)
+    ms, _ = time_graph(stream, g, layers, layers * 8, layers)
+    kv = layers * c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+    res["model_step_48x40k"] = {"workload": "48-layer decode step at 40,000 context (one token: quantize-on-write + "
+                                            "attention per layer), 40,290-row pools, 2.04 GB",
+                                "us_per_step": round(ms * layers * 1e3, 2), "us_per_layer": round(ms * 1e3, 3),
+                                "kv_bytes": kv, "kv_gbps": round(kv / (ms * layers * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(kv / (ms * layers * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del pools, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     c = wl.layer_decode(0, with_new_token=False)
     W = 4095
     run("window4095", c, rows_body(W), W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
