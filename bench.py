@@ -55,7 +55,10 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) instead")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8K-prefix + 8K-chunk prefill timing")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the head-dim-256, multi-row and sliding-window decode timings")
+                    help="skip the head-dim-256, multi-row, sliding-window and INT8 decode timings")
+    ap.add_argument("--model-step", action="store_true",
+                    help="also time the 48-layer step at 40,000 context (2 GB of pools; it runs the headline's "
+                         "stage-1 kernel, so profiles of the headline are taken without it)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run plain 64 MiB device copies (a known-size kernel for HBM byte counters)")
     return ap.parse_args()
@@ -264,10 +267,21 @@ def variants_timing(fk, wl, dev, args, bf):
     run("int8_append_step", c, append_body, kv, fmt="int8",
         extra={"workload": "32K-context GQA-8 decode step over an INT8 pool (scale amax/127)"})
     run("int8_stage1", c, stage1_body, kv, fmt="int8")
-    # the 48-layer step at 40,000 context: one fused call per layer over 48
-    # distinct 40,290-row pools (2 GB, larger than the Infinity Cache, so every
-    # layer reads its rows from HBM); one layer's draws are copied into all
-    # 48 pools, which does not change the timing
+    if args.model_step:
+        res["model_step_48x40k"] = model_step_timing(fk, wl, dev, args, bf, stream)
+    c = wl.layer_decode(0, with_new_token=False)
+    W = 4095
+    run("window4095", c, rows_body(W), W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
+        extra={"workload": "32K-context GQA-8 decode with a 4,095-key sliding window"})
+    return res
+
+
+def model_step_timing(fk, wl, dev, args, bf, stream):
+    """The 48-layer step at 40,000 context: one fused call per layer over 48
+    distinct 40,290-row pools (2 GB, larger than the Infinity Cache, so every
+    layer reads its rows from HBM); one layer's draws are copied into all 48
+    pools, which does not change the timing."""
+    import torch
     table = wl.model_step_table(0)
     c = wl.model_step_layer(0, table)
     layers = 48
@@ -282,19 +296,11 @@ def variants_timing(fk, wl, dev, args, bf):
                       layers)
     ms, _ = time_graph(stream, g, layers, layers * 8, layers)
     kv = layers * c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
-    res["model_step_48x40k"] = {"workload": "48-layer decode step at 40,000 context (one token: quantize-on-write + "
-                                            "attention per layer), 40,290-row pools, 2.04 GB",
-                                "us_per_step": round(ms * layers * 1e3, 2), "us_per_layer": round(ms * 1e3, 3),
-                                "kv_bytes": kv, "kv_gbps": round(kv / (ms * layers * 1e-3) / 1e9, 1),
-                                "hbm_frac": round(kv / (ms * layers * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-    del pools, g
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    c = wl.layer_decode(0, with_new_token=False)
-    W = 4095
-    run("window4095", c, rows_body(W), W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
-        extra={"workload": "32K-context GQA-8 decode with a 4,095-key sliding window"})
-    return res
+    return {"workload": "48-layer decode step at 40,000 context (one token: quantize-on-write + attention per "
+                        "layer), 40,290-row pools, 2.04 GB",
+            "us_per_step": round(ms * layers * 1e3, 2), "us_per_layer": round(ms * 1e3, 3),
+            "kv_bytes": kv, "kv_gbps": round(kv / (ms * layers * 1e-3) / 1e9, 1),
+            "hbm_frac": round(kv / (ms * layers * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def calibration_copies(dev, mib: int = 64, n: int = 4):
@@ -435,6 +441,14 @@ def main():
     m_ms, _ = timed(g_m, per, args.steps)
     g_q = capture(lambda i: quant(pools[i % n_pools]), per)
     q_ms, _ = timed(g_q, per, args.steps)
+    # warm column: the same step replayed over one pool (Infinity-Cache resident)
+    def step_warm(i):
+        st = append(pools[0])
+        if st:
+            raise B.Fp8KvError(st, "decode step (warm)")
+
+    g_warm = capture(step_warm, per)
+    warm_ms, _ = timed(g_warm, per, args.steps)
 
     # correctness guard on the benchmarked configuration (cheap): the fused step
     # against the two-call decode, with another split count, over the pool the
@@ -475,6 +489,7 @@ def main():
         "pct_hbm_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_layer": kv_bytes,
         "us_per_layer_three_calls": round(step3_ms * 1e3, 3),
+        "us_per_layer_warm": round(warm_ms * 1e3, 3),
         "kernels_us": {"quantize_new_row": round(q_ms * 1e3, 3), "decode_stage1": round(s1_ms * 1e3, 3),
                        "decode_merge": round(m_ms * 1e3, 3)},
         "roofline": {
@@ -490,7 +505,7 @@ def main():
     if not args.no_prefill:
         res["prefill"] = prefill_timing(fk, wl, dev)
     if not args.no_variants:
-        del g_step, g_step3, g_s1, g_m, g_q, pools
+        del g_step, g_step3, g_s1, g_m, g_q, g_warm, pools
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         res["variants"] = variants_timing(fk, wl, dev, args, bf)
