@@ -290,3 +290,30 @@ def test_rows_window_graph_replay():
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs"
         _ = (q.float() * 2).sum().item()
     assert_close(bf16_to_f64(eager), _oracle(case, window=4097), "graph rows+window")
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two decode calls with their own workspaces on two streams at once (the
+    library keeps no per-call state): each result matches its own oracle."""
+    say("two decode calls on two streams at once (D=128 one row, D=256 three rows + window)")
+    a = wl.layer_decode(80, ctx=9000, pool_rows=9100, with_new_token=False)
+    b = wl.layer_decode(81, ctx=7000, pool_rows=7100, head_dim=256, with_new_token=False, n_qrows=3)
+    pa, pb = build_pool(a), build_pool(b)
+    qa, ta, la = to_dev_bf16(a.q), to_dev(a.table), to_dev(a.seq_lens)
+    qb, tb, lb = to_dev_bf16(b.q), to_dev(b.table), to_dev(b.seq_lens)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a, outs_b = [], []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            outs_a.append(fk.fp8kv_decode_attn(pa, qa, ta, la, a.max_seq_len, a.sm_scale, stream=s1))
+        with torch.cuda.stream(s2):
+            outs_b.append(fk.fp8kv_decode_attn_rows(pb, qb, tb, lb, b.max_seq_len, b.sm_scale, window=2047,
+                                                    stream=s2))
+    torch.cuda.synchronize()
+    ref_a, ref_b = _oracle(a), _oracle(b, window=2047)
+    for i in range(4):
+        assert_close(bf16_to_f64(outs_a[i]), ref_a, f"stream 1 call {i}")
+        assert_close(bf16_to_f64(outs_b[i]), ref_b, f"stream 2 call {i}")
+        assert torch.equal(outs_a[i].view(torch.int16), outs_a[0].view(torch.int16))
+        assert torch.equal(outs_b[i].view(torch.int16), outs_b[0].view(torch.int16))
