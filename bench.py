@@ -200,11 +200,12 @@ def variants_timing(fk, wl, dev, args, bf):
     steps = max(48, args.steps // 2)
     res = {}
 
-    def run(name, case, body_for, kv_bytes, flop=None, extra=None, fmt="e4m3"):
-        pools = rotated_pools(fk, case, args.layout, n, dev, bf, fmt)
+    def run(name, case, body_for, kv_bytes, flop=None, extra=None, fmt="e4m3", copies=None):
+        nc = copies or n
+        pools = rotated_pools(fk, case, args.layout, nc, dev, bf, fmt)
         body = body_for(case, pools)
-        g = capture_graph(stream, body, n)
-        ms, _ = time_graph(stream, g, n, steps, args.warmup)
+        g = capture_graph(stream, body, nc)
+        ms, _ = time_graph(stream, g, nc, steps, args.warmup)
         gbps = kv_bytes / (ms * 1e-3) / 1e9
         r = {"us": round(ms * 1e3, 3), "kv_bytes": kv_bytes, "kv_gbps": round(gbps, 1),
              "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
@@ -221,17 +222,20 @@ def variants_timing(fk, wl, dev, args, bf):
     def append_body(case, pools):
         q, nk, nv = bf(case.q), bf(case.new_k), bf(case.new_v)
         t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
-        slot = torch.from_numpy(case.table[:, -1].copy()).to(dev)
-        ws = fk.decode_workspace(1, case.n_q_heads, device=dev, head_dim=case.head_dim)
+        # request b's new token sits at its last position
+        last = case.table[np.arange(case.table.shape[0]), case.seq_lens.astype(np.int64) - 1]
+        slot = torch.from_numpy(np.ascontiguousarray(last, dtype=np.int32)).to(dev)
+        ws = fk.decode_workspace(case.table.shape[0], case.n_q_heads, device=dev, head_dim=case.head_dim)
         out = torch.empty_like(q)
-        return lambda i: fk.fp8kv_decode_attn_append(pools[i % n], q, nk, nv, slot, t, sl, case.max_seq_len,
-                                                     case.sm_scale, workspace=ws, out=out, stream=stream)
+        return lambda i: fk.fp8kv_decode_attn_append(pools[i % len(pools)], q, nk, nv, slot, t, sl,
+                                                     case.max_seq_len, case.sm_scale, workspace=ws, out=out,
+                                                     stream=stream)
 
     def stage1_body(case, pools):
         q = bf(case.q)
         t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
-        ws = fk.decode_workspace(1, case.n_q_heads, device=dev, head_dim=case.head_dim)
-        return lambda i: fk.fp8kv_decode_stage1(pools[i % n], q, t, sl, case.max_seq_len, case.sm_scale,
+        ws = fk.decode_workspace(case.table.shape[0], case.n_q_heads, device=dev, head_dim=case.head_dim)
+        return lambda i: fk.fp8kv_decode_stage1(pools[i % len(pools)], q, t, sl, case.max_seq_len, case.sm_scale,
                                                 workspace=ws, stream=stream)
 
     def rows_body(window):
@@ -262,6 +266,16 @@ def variants_timing(fk, wl, dev, args, bf):
     run("int8_append_step", c, append_body, kv, fmt="int8",
         extra={"workload": "32K-context GQA-8 decode step over an INT8 pool (scale amax/127)"})
     run("int8_stage1", c, stage1_body, kv, fmt="int8")
+    # 16 requests with seeded lengths in [1,024, 32,768] (272,568 rows, 288 MB of
+    # codes and scales per pool copy: larger than the Infinity Cache, so 4
+    # rotated copies keep it cold), 16 q / 4 KV heads
+    c = wl.batched_decode(0, with_new_token=True)
+    kv = int(c.seq_lens.astype(np.int64).sum()) * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+    run("batched16_append_step", c, append_body, kv, copies=min(n, 4),
+        extra={"workload": "16 requests, lengths 1,024-32,768 (272,568 rows), GQA 4 (16 q / 4 KV heads), "
+                           "one decode step with quantize-on-write"})
+    run("batched16_stage1", c, stage1_body, kv, copies=min(n, 4))
+    del c
     if args.model_step:
         res["model_step_48x40k"] = model_step_timing(fk, wl, dev, args, bf, stream)
     c = wl.layer_decode(0, with_new_token=False)

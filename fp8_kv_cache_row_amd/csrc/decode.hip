@@ -126,10 +126,20 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
   const int wave = threadIdx.x / kWave;
   const int n = lane & 15;
   const int j = lane >> 4;
-  const int split = blockIdx.x;
-  const int g = C::MULTI ? (int)blockIdx.y / n_col_groups : (int)blockIdx.y;
-  const int cg = C::MULTI ? (int)blockIdx.y - g * n_col_groups : 0;
-  const int b = blockIdx.z;
+  // Grid (8 * Hkv, ceil(n_split / 8), batch * column groups): workgroup
+  // x + 8 Hkv (y + Y z) is dispatched to XCD x & 7, so the Hkv workgroups of
+  // one (request, column group, split) run on one XCD, next to each other in
+  // its dispatch order: they share that XCD's L2 lines of the table and of the
+  // rows' scales, and the DRAM pages of each row record.
+  // When n_split is not a multiple of 8, the workgroups past the last split
+  // redo the last one and store nothing (no branch at the top: it would
+  // split the entry block and serialize the argument loads).
+  const int split_raw = 8 * (int)blockIdx.y + (int)(blockIdx.x & 7u);
+  const bool owner = split_raw < n_split;
+  const int split = min(split_raw, n_split - 1);
+  const int g = (int)(blockIdx.x >> 3);
+  const int b = C::MULTI ? (int)blockIdx.z / n_col_groups : (int)blockIdx.z;
+  const int cg = C::MULTI ? (int)blockIdx.z - b * n_col_groups : 0;
   const int n_cols = G * n_qrows;  // columns of this KV head
   const int h0 = g * G;
 
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
       for (int idx = threadIdx.x; idx < kPassCols * 32; idx += kBlock) {
         const int col = idx >> 5;
         const int c = (cg * NT + t) * 16 + col;
-        if (c >= n_cols) continue;
+        if (c >= n_cols || !owner) continue;
         const int i = C::MULTI ? (c >> g_shift) : 0;
         const int dp = 4 * (idx & 31);
         const int d = kNB * (dp >> 3) + 8 * half + (dp & 7);
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
   // The split count for a merge launched without one.  Written last: a branch
   // at the top would split the entry block and serialize the argument loads
   // ahead of the first table read.
-  if (split == 0 && blockIdx.y == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
+  if (split == 0 && g == 0 && cg == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 }
 
 // Stage 2: out[b][h] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) over the
@@ -659,7 +669,9 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
 template <class C>
 hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk_scale_log2,
                              const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim, hipStream_t stream) {
-  dim3 grid((unsigned)geo.n_split, (unsigned)(pool.n_kv_heads * geo.n_col_groups), (unsigned)sh.batch);
+  const int64_t z = (int64_t)sh.batch * geo.n_col_groups;
+  if (z > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(8 * pool.n_kv_heads), (unsigned)((geo.n_split + 7) / 8), (unsigned)z);
   int g_shift = 0;
   while ((1 << g_shift) < sh.n_q_heads / pool.n_kv_heads) ++g_shift;
   hipLaunchKernelGGL(decode_stage1_kernel<C>, grid, dim3(C::kBlock), 0, stream, pool.k_codes, pool.v_codes,

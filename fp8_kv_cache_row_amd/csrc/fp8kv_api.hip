@@ -91,6 +91,11 @@ int32_t split_cap(int32_t max_splits) {
 // otherwise).  Several query rows put G * n_qrows columns on the MFMA tiles:
 // as many 16-column tiles per workgroup as the head dim allows, and more
 // column groups beyond that.
+#ifndef FP8KV_DECODE_MAX_CHUNK
+#define FP8KV_DECODE_MAX_CHUNK 512
+#endif
+constexpr int64_t kMaxChunkKeys = FP8KV_DECODE_MAX_CHUNK;
+
 fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t group,
                                       int32_t n_qrows, int32_t max_seq_len, int32_t window, int32_t max_splits,
                                       int n_cu) {
@@ -116,7 +121,17 @@ fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t
   if (ns > useful) ns = useful;
   int64_t chunk = (L + ns - 1) / ns;
   chunk = (chunk + unit - 1) / unit * unit;
+  if (kMaxChunkKeys > 0 && chunk > 2 * kMaxChunkKeys) {
+    int64_t ns2 = (L + kMaxChunkKeys - 1) / kMaxChunkKeys;
+    if (ns2 > split_cap(max_splits)) ns2 = split_cap(max_splits);
+    chunk = (L + ns2 - 1) / ns2;
+    chunk = (chunk + unit - 1) / unit * unit;
+  }
   ns = (L + chunk - 1) / chunk;
+  // Whole rows of 8 splits in the grid (one per XCD); the extra splits start
+  // past the span and hold no keys.
+  const int64_t ns8 = (ns + 7) / 8 * 8;
+  if (ns8 <= split_cap(max_splits)) ns = ns8;
   return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk, col_tiles, n_col_groups};
 }
 
