@@ -66,17 +66,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //   WINDOW  a sliding key window: the key range starts at the first row's
 //           lowest visible position, so the table read waits for the length.
 //   F       the code format (E4M3FN or INT8), widened exactly to bf16.
-template <int G_, int D_, int NT_, bool MULTI_, bool WINDOW_, int F_>
+//   STREAM  one 32-key step in flight per wave and two workgroups per compute
+//           unit (at most 128 registers), for grids of several rounds.
+template <int G_, int D_, int NT_, bool MULTI_, bool WINDOW_, int F_, bool STREAM_ = false>
 struct Stage1 {
   static constexpr int G = G_, D = D_, NT = NT_, F = F_;
-  static constexpr bool MULTI = MULTI_, WINDOW = WINDOW_;
+  static constexpr bool MULTI = MULTI_, WINDOW = WINDOW_, STREAM = STREAM_;
   using Code = Codec<F_>;
   // Registers: NT * D / 16 accumulators of 4 floats each, NT * D / 32 query
   // operands and one or two steps of codes in flight.  Wide shapes run 4
   // waves (one per SIMD, 512 registers each) instead of 8.
   static constexpr int kWaves = (NT * D >= 512) ? 4 : kDecodeWaves;
   static constexpr int kBlock = kWaves * kWave;
-  static constexpr int kSteps = (D == 128 || kWaves == 4) ? kDecodeTilesPerWave : 1;  // 32-key steps loaded at once
+  static constexpr int kSteps = STREAM ? 1 : ((D == 128 || kWaves == 4) ? kDecodeTilesPerWave : 1);  // 32-key steps loaded at once
+  static constexpr int kWavesPerEU = STREAM ? 2 * kWaves / 4 : 1;  // minimum waves per SIMD the registers allow
+  static_assert(!STREAM || (D == 128 && NT == 1 && !MULTI && !WINDOW && kWaves == 8), "streaming shape: one row, D = 128");
   static constexpr int kGroupKeys = kSteps * kDecodeTileKeys;
   // Row indices and scales are loaded one key per lane; a 32-key group leaves
   // the upper half-wave reading duplicates into padding.
@@ -109,7 +113,7 @@ __device__ __forceinline__ void load_v_words(const uint8_t* p, uint32_t (&w)[W])
 }
 
 template <class C>
-__global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
+__global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kWavesPerEU))) void decode_stage1_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, uint32_t code_row_stride,
     uint32_t scale_row_stride, const uint16_t* __restrict__ q, int32_t n_q_heads, int32_t n_qrows, int32_t g_shift,
@@ -206,6 +210,24 @@ __global__ __launch_bounds__(C::kBlock) void decode_stage1_kernel(
     k0 = key_begin + wave * kGroupKeys;
   }
   const int key_end = min(key_begin + chunk, len - key_trim);  // keys this split covers
+  if constexpr (C::STREAM) {
+    // A split past its request's length (the grid is sized by the longest
+    // request) stores its empty partial -- o = 0, lse = -inf, which the merge
+    // weights by zero -- and leaves without the wave merge.
+    if (key_end <= key_begin) {
+      if (owner) {
+        for (int idx = threadIdx.x; idx < G * (D / 4); idx += kBlock) {
+          const int col = idx / (D / 4);
+          const int d = 4 * (idx - col * (D / 4));
+          const int64_t ph = ((int64_t)b * n_q_heads + h0 + col) * split_stride + split;
+          *reinterpret_cast<float4*>(part_o + ph * D + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (d == 0) part_lse[ph] = -INFINITY;
+        }
+      }
+      if (split == 0 && g == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
+      return;
+    }
+  }
   int cend[NT], clo[NT];  // the lane's columns see keys [clo, cend) of this split
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -687,12 +709,25 @@ template <int D, bool WINDOW, int F>
 hipError_t launch_stage1_single(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
                                 hipStream_t stream) {
+  // The streaming shape exists for head dim 128 without a window.
+  constexpr bool kCanStream = D == 128 && !WINDOW;
+  const bool st = kCanStream && geo.stream;
   switch (sh.n_q_heads / pool.n_kv_heads) {
-    case 1: return launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 2: return launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 4: return launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 8: return launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 16: return launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 1:
+      return st ? launch_stage1_cfg<Stage1<1, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                : launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 2:
+      return st ? launch_stage1_cfg<Stage1<2, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                : launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 4:
+      return st ? launch_stage1_cfg<Stage1<4, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                : launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 8:
+      return st ? launch_stage1_cfg<Stage1<8, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                : launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 16:
+      return st ? launch_stage1_cfg<Stage1<16, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                : launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
     default: return hipErrorInvalidValue;
   }
 }

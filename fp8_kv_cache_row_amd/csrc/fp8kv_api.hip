@@ -95,6 +95,10 @@ int32_t split_cap(int32_t max_splits) {
 #define FP8KV_DECODE_MAX_CHUNK 512
 #endif
 constexpr int64_t kMaxChunkKeys = FP8KV_DECODE_MAX_CHUNK;
+#ifndef FP8KV_DECODE_STREAM
+#define FP8KV_DECODE_STREAM 1
+#endif
+constexpr bool kStreamDecode = FP8KV_DECODE_STREAM;
 
 fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t group,
                                       int32_t n_qrows, int32_t max_seq_len, int32_t window, int32_t max_splits,
@@ -121,7 +125,9 @@ fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t
   if (ns > useful) ns = useful;
   int64_t chunk = (L + ns - 1) / ns;
   chunk = (chunk + unit - 1) / unit * unit;
+  bool stream = false;
   if (kMaxChunkKeys > 0 && chunk > 2 * kMaxChunkKeys) {
+    stream = kStreamDecode;
     int64_t ns2 = (L + kMaxChunkKeys - 1) / kMaxChunkKeys;
     if (ns2 > split_cap(max_splits)) ns2 = split_cap(max_splits);
     chunk = (L + ns2 - 1) / ns2;
@@ -132,7 +138,7 @@ fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t
   // past the span and hold no keys.
   const int64_t ns8 = (ns + 7) / 8 * 8;
   if (ns8 <= split_cap(max_splits)) ns = ns8;
-  return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk, col_tiles, n_col_groups};
+  return fp8kv::DecodeGeometry{(int32_t)ns, (int32_t)chunk, col_tiles, n_col_groups, stream && n_qrows == 1 && window == 0 && head_dim == 128};
 }
 
 size_t partial_bytes(int64_t n_queries, int64_t n_q_heads, int64_t head_dim, int64_t split_stride) {

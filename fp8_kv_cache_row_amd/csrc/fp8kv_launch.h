@@ -33,6 +33,10 @@ struct DecodeGeometry {
   int32_t chunk;  // multiple of kDecodeTileKeys
   int32_t col_tiles;
   int32_t n_col_groups;
+  // Several workgroup rounds per compute unit: one 32-key step in flight per
+  // wave and at most 128 registers, so two workgroups share a compute unit
+  // and one's loads cover the other's start-up and epilogue.
+  bool stream;
 };
 
 // The decode problem: q [batch][n_qrows][n_q_heads][head_dim]; query row i of

@@ -145,7 +145,9 @@ def test_batched_16_requests_gqa4():
     assert int(case.seq_lens.sum()) == 272568
     pool = build_pool(case)
     ref = _oracle_decode(case)
-    for cap in (0, 8):
+    # caps 3 and 13 leave a partial row of 8 splits in the grid (the extra
+    # workgroups redo the last split and store nothing)
+    for cap in (0, 8, 3, 13):
         out = bf16_to_f64(run_decode(pool, case, max_splits=cap))
         assert_close(out, ref, f"batched cap={cap}")
         for b in range(case.batch):

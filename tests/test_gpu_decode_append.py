@@ -131,7 +131,7 @@ def test_append_batched_16_requests():
     case = wl.batched_decode(0, with_new_token=True)
     pool = build_pool(case)
     ref_pools, ref = _oracle_step(case)
-    for cap in (0, 8):
+    for cap in (0, 8, 13):
         if cap:
             pool = build_pool(case)
         out = bf16_to_f64(_run_append(pool, case, max_splits=cap))
