@@ -692,7 +692,7 @@ template <class C>
 hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk_scale_log2,
                              const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim, hipStream_t stream) {
   const int64_t z = (int64_t)sh.batch * geo.n_col_groups;
-  if (z > 65535) return hipErrorInvalidValue;
+  if (z > FP8KV_MAX_DECODE_GROUPS_INTERNAL) return hipErrorInvalidValue;  // the entry points reject it first
   const dim3 grid((unsigned)(8 * pool.n_kv_heads), (unsigned)((geo.n_split + 7) / 8), (unsigned)z);
   int g_shift = 0;
   while ((1 << g_shift) < sh.n_q_heads / pool.n_kv_heads) ++g_shift;

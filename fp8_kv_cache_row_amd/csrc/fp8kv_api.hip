@@ -12,6 +12,7 @@
 #include "fp8kv_device.h"
 
 static_assert(FP8KV_MAX_SPLITS == FP8KV_MAX_SPLITS_INTERNAL, "split cap mismatch");
+static_assert(FP8KV_MAX_DECODE_GROUPS == FP8KV_MAX_DECODE_GROUPS_INTERNAL, "decode group cap mismatch");
 static_assert(FP8KV_CODE_E4M3 == fp8kv::kE4M3 && FP8KV_CODE_INT8 == fp8kv::kInt8, "code format mismatch");
 
 namespace {
@@ -100,17 +101,23 @@ constexpr int64_t kMaxChunkKeys = FP8KV_DECODE_MAX_CHUNK;
 #endif
 constexpr bool kStreamDecode = FP8KV_DECODE_STREAM;
 
-fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t group,
-                                      int32_t n_qrows, int32_t max_seq_len, int32_t window, int32_t max_splits,
-                                      int n_cu) {
-  int32_t col_tiles = 1, n_col_groups = 1;
+// Column tiles per workgroup and column groups per (request, KV head).
+void column_split(int32_t head_dim, int32_t group, int32_t n_qrows, int32_t* col_tiles, int32_t* n_col_groups) {
+  *col_tiles = 1;
+  *n_col_groups = 1;
   if (n_qrows > 1) {
     const int32_t tiles = (group * n_qrows + 15) / 16;
     const int32_t cap = fp8kv::decode_max_col_tiles(head_dim);
-    col_tiles = 1;
-    while (col_tiles < tiles && col_tiles < cap) col_tiles *= 2;
-    n_col_groups = (tiles + col_tiles - 1) / col_tiles;
+    while (*col_tiles < tiles && *col_tiles < cap) *col_tiles *= 2;
+    *n_col_groups = (tiles + *col_tiles - 1) / *col_tiles;
   }
+}
+
+fp8kv::DecodeGeometry choose_geometry(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t group,
+                                      int32_t n_qrows, int32_t max_seq_len, int32_t window, int32_t max_splits,
+                                      int n_cu) {
+  int32_t col_tiles, n_col_groups;
+  column_split(head_dim, group, n_qrows, &col_tiles, &n_col_groups);
   const int64_t unit = fp8kv::kDecodeTileKeys;
   int64_t span = max_seq_len;
   if (window > 0 && (int64_t)window + n_qrows - 1 < span) span = (int64_t)window + n_qrows - 1;
@@ -170,6 +177,11 @@ fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, 
   if ((int64_t)batch * n_qrows > INT32_MAX / 2) return FP8KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
   if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
+  {
+    int32_t col_tiles, n_col_groups;
+    column_split(pool->head_dim, n_q_heads / pool->n_kv_heads, n_qrows, &col_tiles, &n_col_groups);
+    if ((int64_t)batch * n_col_groups > FP8KV_MAX_DECODE_GROUPS) return FP8KV_ERR_UNSUPPORTED;
+  }
   if (is_nan(sm_scale)) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4)) return FP8KV_ERR_ALIGNMENT;
   if (!workspace ||

@@ -61,6 +61,8 @@ struct DecodeShape {
 #endif
 // Must equal FP8KV_MAX_SPLITS of the public header (checked in the C ABI).
 #define FP8KV_MAX_SPLITS_INTERNAL 256
+// Requests (times column groups) per decode launch: they share one grid dimension.
+#define FP8KV_MAX_DECODE_GROUPS_INTERNAL 65535
 
 constexpr int kDecodeWaves = FP8KV_DECODE_WAVES;                 // waves per stage-1 workgroup (narrow shapes)
 constexpr int kDecodeTileKeys = 32;                              // keys per wave per MFMA step

@@ -52,6 +52,9 @@ extern "C" {
 #define FP8KV_MAX_SPLITS 256
 /* Upper bound on query rows per request in one decode call. */
 #define FP8KV_MAX_QUERY_ROWS 8
+/* Upper bound on requests per decode call (times ceil(G * n_qrows / 32) for
+ * several query rows): they share one launch dimension. */
+#define FP8KV_MAX_DECODE_GROUPS 65535
 /* Code formats of a pool (fp8kv_pool_layer.code_format). */
 #define FP8KV_CODE_E4M3 0 /* OCP E4M3FN, scale amax / 448 */
 #define FP8KV_CODE_INT8 1 /* symmetric INT8, scale amax / 127 */
@@ -180,10 +183,14 @@ size_t fp8kv_decode_workspace_bytes(int32_t n_queries, int32_t n_q_heads, int32_
  * max_seq_len:  host-side upper bound on seq_lens (sizes the launch), >= 0,
  *               <= table_stride.
  * n_q_heads:    a multiple of pool->n_kv_heads with G in {1, 2, 4, 8, 16}.
+ * batch:        1 .. FP8KV_MAX_DECODE_GROUPS (one launch dimension holds the
+ *               requests; for fp8kv_decode_attn_rows it holds the requests
+ *               times ceil(G * n_qrows / 32), which must not exceed it).
  * workspace:    device, 256-byte aligned, >= fp8kv_decode_workspace_bytes(
  *               batch, n_q_heads, D, max_splits) bytes; contents are scratch.
  * out:          device bf16 [batch][n_q_heads][D], 16-byte aligned.
- * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (G, head_dim, batch over the limit),
+ *         ALIGNMENT, WORKSPACE, HIP.
  */
 fp8kv_status fp8kv_decode_attn(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
                                int32_t n_q_heads, const int32_t *row_table, int64_t table_stride,

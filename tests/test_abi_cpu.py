@@ -117,6 +117,7 @@ def test_decode_validation(lib):
     assert _decode(lib, p, ws=0) == WORKSPACE
     assert _decode(lib, p, wsb=100) == WORKSPACE
     assert _decode(lib, p, ws=A + 16) == ALIGN
+    assert _decode(lib, p, batch=65536, wsb=1 << 62) == UNSUPPORTED  # over FP8KV_MAX_DECODE_GROUPS
     assert _decode(lib, _pool(head_dim=256)) == INVALID               # code_row_stride 512 < 4 * 256
     p256 = _pool(head_dim=256, code_row_stride=1024)
     small = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
@@ -135,6 +136,8 @@ def test_decode_rows_validation(lib):
     one_row = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
     assert _rows(lib, p, nq=3, wsb=one_row) == WORKSPACE              # partials for 3 rows
     assert _rows(lib, p, batch=0) == INVALID
+    # 8 rows of GQA 8 are 64 columns: two column groups of 32 share the launch dimension
+    assert _rows(lib, p, nq=8, batch=32768, wsb=1 << 62) == UNSUPPORTED
     assert _rows(lib, p, tstride=999) == INVALID
 
 
@@ -220,6 +223,10 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert _decode(lib, _pool(code_format=1)) == HIP
     assert _decode(lib, _pool(head_dim=256, code_row_stride=1024)) == HIP
     assert _rows(lib, _pool(), nq=8, window=17) == HIP
+    # the largest accepted batches (FP8KV_MAX_DECODE_GROUPS launch groups)
+    assert _decode(lib, _pool(), batch=65535, wsb=1 << 62) == HIP
+    assert _rows(lib, _pool(), nq=8, batch=32767, wsb=1 << 62) == HIP    # two column groups per request
+    assert _rows(lib, _pool(), nq=3, batch=65535, wsb=1 << 62) == HIP    # 24 columns: one group
     assert _prefill(lib, _pool()) == HIP
     wsb = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
     assert lib.fp8kv_decode_stage1(ctypes.byref(_pool()), A, 1, 32, A, 1024, A, 1000, 0.088, 0, A, wsb, None) == HIP
