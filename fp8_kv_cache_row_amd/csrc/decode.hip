@@ -525,7 +525,9 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int n_split = n_split_arg >= 0 ? n_split_arg : header[0];
+  // A split count read from the workspace is clamped to its capacity, so a
+  // workspace that no stage 1 wrote cannot send the loads past it.
+  const int n_split = n_split_arg >= 0 ? n_split_arg : min(max(header[0], 0), split_stride);
   const float* lse_p = part_lse + bh * split_stride;
   const float* po = part_o + bh * split_stride * D + E * lane;
 

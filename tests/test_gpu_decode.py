@@ -257,6 +257,33 @@ def test_stage1_then_merge_equals_full_call():
         assert torch.equal(full.view(torch.int16), two.view(torch.int16)), cap
 
 
+def test_stage1_then_merge_streaming_with_an_empty_first_request():
+    """Splits of more than 1,024 keys take the streaming stage-1 shape, where a
+    split past its request's length stores an empty partial and leaves early;
+    with request 0 empty, split 0 of request 0 is such a split and must still
+    write the split count that a separately launched merge reads from the
+    workspace (pre-filled with garbage here)."""
+    say("decode: streaming stage 1 + merge with request 0 empty, garbage-filled workspace")
+    case = wl.batched_decode(11, n_req=6, lo=3000, hi=9000)
+    lens = case.seq_lens.copy()
+    lens[0] = 0
+    pool = build_pool(case)
+    ref = _oracle_decode(case, seq_lens=lens)
+    q, t, sl = to_dev_bf16(case.q), to_dev(case.table), to_dev(lens)
+    for cap in (2, 5):
+        ws = fk.decode_workspace(case.batch, case.n_q_heads, max_splits=cap)
+        ws.fill_(0x7F)
+        fk.fp8kv_decode_stage1(pool, q, t, sl, case.max_seq_len, case.sm_scale, max_splits=cap, workspace=ws)
+        two = fk.fp8kv_decode_merge(ws, case.batch, case.n_q_heads, max_splits=cap)
+        full = fk.fp8kv_decode_attn(pool, q, t, sl, case.max_seq_len, case.sm_scale, max_splits=cap)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == cap, "split count in the workspace header"
+        assert torch.equal(full.view(torch.int16), two.view(torch.int16)), cap
+        got = bf16_to_f64(two)
+        assert np.all(got[0] == 0.0), "an empty request gets zeros"
+        assert_close(got[1:], ref[1:], f"streaming cap={cap}")
+
+
 def test_out_of_range_padding_entries_are_clamped():
     """Padding entries (positions >= seq_lens[b]) holding -1, INT32_MAX or rows
     past the pool are clamped by the kernels to a real row and masked: the
