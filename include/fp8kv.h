@@ -215,6 +215,9 @@ fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer *pool, const uint16_t *q
  * partials a preceding fp8kv_decode_stage1 on the same stream wrote into
  * `workspace` (n_queries = its batch; the same n_q_heads, head dim and
  * max_splits) by log-sum-exp and writes bf16 out[n_queries][n_q_heads][head_dim].
+ * The split count comes from the workspace header that stage 1 wrote; it is
+ * clamped to the workspace's split capacity, so a workspace no stage 1 wrote
+ * gives meaningless output but no access outside the workspace.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim), ALIGNMENT, WORKSPACE, HIP.
  */
 fp8kv_status fp8kv_decode_merge(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits,
