@@ -126,6 +126,24 @@ def test_gqa_ratios(G, Hkv):
     assert_close(bf16_to_f64(run_decode(pool, case, max_splits=2)), ref, f"G={G} streaming")
 
 
+def test_long_context_at_the_split_cap():
+    """131,072 keys of one request: 256 splits of 512 keys (FP8KV_MAX_SPLITS),
+    the streaming stage-1 shape, and a merge folding 256 partials per head in
+    four load batches."""
+    say("decode 131,072 keys, 32 q / 4 KV heads: 256 splits, streaming stage 1")
+    case = wl.layer_decode(12, ctx=131072, pool_rows=131072 + 300)
+    pool = build_pool(case)
+    ref_pools = oracle_pool(case)
+    lens = case.seq_lens - 1  # 131,071 keys: the last split is one key short
+    ref = _oracle_decode(case, ref_pools, seq_lens=lens)
+    out = run_decode(pool, case, seq_lens=lens)
+    assert_close(bf16_to_f64(out), ref, "131,071 keys")
+    ws = fk.fp8kv_decode_stage1(pool, to_dev_bf16(case.q), to_dev(case.table), to_dev(case.seq_lens),
+                                case.max_seq_len, case.sm_scale)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 256, "split count"
+
+
 def test_row_permutation_invariance():
     say("decode: permuting the physical rows (and the table) leaves the output unchanged")
     case = wl.layer_decode(5, ctx=2000, pool_rows=2500, with_new_token=False)
