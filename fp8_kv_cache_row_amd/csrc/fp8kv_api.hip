@@ -91,8 +91,8 @@ int32_t split_cap(int32_t max_splits) {
 // span (the window plus the extra query rows with a window, max_seq_len
 // otherwise).  When that one round would give splits of more than 2 x 512
 // keys (a batch, a long context), splits take 512 keys over several rounds,
-// and one-row D = 128 calls switch to the streaming stage-1 shape (two
-// workgroups per CU).  The split count is padded with empty splits to a
+// and one-row D = 128 calls switch to the streaming stage-1 shape (three
+// 4-wave workgroups per CU).  The split count is padded with empty splits to a
 // multiple of 8 (one grid row per XCD) when the workspace cap allows.
 // Several query rows put G * n_qrows columns on the MFMA tiles: as many
 // 16-column tiles per workgroup as the head dim allows, and more column

@@ -33,9 +33,9 @@ struct DecodeGeometry {
   int32_t chunk;  // multiple of kDecodeTileKeys
   int32_t col_tiles;
   int32_t n_col_groups;
-  // Several workgroup rounds per compute unit: one 32-key step in flight per
-  // wave and at most 128 registers, so two workgroups share a compute unit
-  // and one's loads cover the other's start-up and epilogue.
+  // Several workgroup rounds per compute unit: 4-wave workgroups of at most
+  // 168 registers, so three share a compute unit and one's loads cover the
+  // others' start-up and epilogue.
   bool stream;
 };
 
