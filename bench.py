@@ -325,29 +325,42 @@ def calibration_copies(dev, mib: int = 64, n: int = 4):
 
 def cpu_baseline(case, budget_s: float):
     """The oracle (as it stands) on the host: quantize the new K/V row + fp64
-    decode attention over all 32,768 rows, repeated until the time budget."""
-    import numpy as np
-
+    decode attention over all 32,768 rows, repeated until the time budget, on
+    all host threads and then on one."""
     import oracle
     kc, ks = oracle.quantize_rows(case.k_rows)
     vc, vs = oracle.quantize_rows(case.v_rows)
     row = int(case.table[0, -1])
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        nkc, nks = oracle.quantize_rows(case.new_k)
-        nvc, nvs = oracle.quantize_rows(case.new_v)
-        kc[row], ks[row], vc[row], vs[row] = nkc[0], nks[0], nvc[0], nvs[0]
-        oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale, case.n_kv_heads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
     kv = case.max_seq_len * case.n_kv_heads * KV_BYTES_PER_ROW_HEAD
-    return {"value": round(kv * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+
+    def timed(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            nkc, nks = oracle.quantize_rows(case.new_k)
+            nvc, nvs = oracle.quantize_rows(case.new_v)
+            kc[row], ks[row], vc[row], vs[row] = nkc[0], nks[0], nvc[0], nvs[0]
+            oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale,
+                                    case.n_kv_heads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    cores = oracle.num_threads()
+    reps, el = timed(budget_s)
+    oracle.set_num_threads(1)
+    try:
+        reps1, el1 = timed(budget_s / 2)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(kv * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"full 32K-context layer step (quantize new K/V row + fp64 decode attention, "
                       f"32 q heads x 32,768 rows) repeated {reps} times in {el:.1f} s",
-            "us_per_layer": round(el / reps * 1e6, 1)}
+            "us_per_layer": round(el / reps * 1e6, 1),
+            "single_core": {"value": round(kv * reps1 / el1 / 1e9, 3), "unit": "GB/s",
+                            "us_per_layer": round(el1 / reps1 * 1e6, 1),
+                            "sample": f"the same step repeated {reps1} times in {el1:.1f} s on 1 thread"}}
 
 
 def main():

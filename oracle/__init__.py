@@ -78,12 +78,19 @@ def lib() -> ctypes.CDLL:
         L.oracle_bf16_workspace_bytes.restype = _i64
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = _i32
+        L.oracle_set_num_threads.argtypes = [_i32]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Host threads for later oracle calls from this thread (timing only)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------------ codec --

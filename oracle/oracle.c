@@ -450,3 +450,13 @@ int32_t oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Host threads for the following calls from this thread (timing runs only;
+ * results do not depend on it). */
+void oracle_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
