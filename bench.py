@@ -64,12 +64,13 @@ def parse():
     return ap.parse_args()
 
 
-STAGE1_SOURCES = ("decode.hip", "fp8kv_device.h", "fp8kv_launch.h")
+STAGE1_SOURCES = ("decode.hip", "fp8kv_device.h", "fp8kv_launch.h", "fp8kv_api.hip")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the stage-1 kernel is built from (its byte counters
-    are only reused while these are unchanged)."""
+    """Hash of the sources the stage-1 kernel and its launch geometry (split
+    choice) are built from: its byte counters are only reused while these are
+    unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_kv_cache_row_amd", "csrc")
     for name in STAGE1_SOURCES:
