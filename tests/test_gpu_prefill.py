@@ -54,7 +54,7 @@ def _run(case, layout="separate", q_idx=None, check_ws=True, fmt="e4m3"):
 
 @pytest.mark.parametrize("P,T,Hq,Hkv", [(0, 1, 8, 1), (0, 37, 32, 4), (64, 1, 32, 4), (100, 37, 32, 4),
                                          (257, 130, 16, 4), (1000, 300, 8, 8), (33, 65, 32, 2),
-                                         (500, 200, 4, 4)])
+                                         (500, 200, 4, 4), (200, 90, 8, 4), (1500, 777, 32, 4)])
 def test_small_prefills(P, T, Hq, Hkv):
     say(f"prefill P={P} T={T} Hq={Hq} Hkv={Hkv}")
     case = wl.chunked_prefill(seed=P + T, n_prefix=P, n_chunk=T, n_q_heads=Hq, n_kv_heads=Hkv)
@@ -96,3 +96,36 @@ def test_chunked_prefill_8k_prefix_8k_chunk_int8_pool():
     idx = np.unique(np.concatenate([np.arange(0, T, 512), np.arange(T - 4, T)]))
     got, ref = _run(case, q_idx=idx, fmt="int8", layout="interleaved")
     assert_close(got, ref, "int8 8K+8K sampled")
+
+
+def test_prefill_graph_replay_matches_eager():
+    """Reconstruct + attention captured in a HIP graph and replayed three times,
+    with eager work and synchronizations between the replays: every replay's
+    output and workspace are bit-identical to the eager call's."""
+    say("prefill P=700 T=300 captured in a graph, 3 replays vs eager")
+    case = wl.chunked_prefill(seed=5, n_prefix=700, n_chunk=300)
+    P, H = case.prefix_k.shape[0], case.n_kv_heads
+    pool = fk.Fp8KvPool(case.pool_rows, H, device=DEV)
+    fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.prefix_k), to_dev_bf16(case.prefix_v), to_dev(case.prefix_rows))
+    q, kc, vc, rows = to_dev_bf16(case.q), to_dev_bf16(case.k_cur), to_dev_bf16(case.v_cur), to_dev(case.prefix_rows)
+    ws_k = torch.empty((P, H, D), dtype=torch.bfloat16, device=DEV)
+    ws_v = torch.empty_like(ws_k)
+    out = torch.empty_like(q)
+    stream = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(stream):
+        fk.fp8kv_prefill_attn(pool, q, kc, vc, rows, ws_k, ws_v, case.sm_scale, out=out, stream=stream)
+    stream.synchronize()
+    ref_out, ref_k, ref_v = out.clone(), ws_k.clone(), ws_v.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fk.fp8kv_prefill_attn(pool, q, kc, vc, rows, ws_k, ws_v, case.sm_scale, out=out, stream=stream)
+    for rep in range(3):
+        out.fill_(0)
+        ws_k.fill_(0)
+        ws_v.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}: out"
+        assert torch.equal(ws_k.view(torch.int16), ref_k.view(torch.int16)), f"replay {rep}: ws_k"
+        assert torch.equal(ws_v.view(torch.int16), ref_v.view(torch.int16)), f"replay {rep}: ws_v"
