@@ -191,9 +191,10 @@ def rotated_pools(fk, case, layout, n, dev, bf, fmt="e4m3"):
 def variants_timing(fk, wl, dev, args, bf):
     """The decode variants at 32K context, each over rotated cold pools:
     head dim 256 (fused append step and stage 1 alone), 3 and 8 causal query
-    rows per request, an odd 4,095-key sliding window, the INT8 KV format
-    (fused append step and stage 1 alone), and the 48-layer step at 40,000
-    context."""
+    rows per request, the INT8 KV format (fused append step and stage 1
+    alone), the 16-request GQA-4 batch (fused step and stage 1 alone), an odd
+    4,095-key sliding window (query rows call, and the fused step), and with
+    --model-step the 48-layer step at 40,000 context."""
     import numpy as np
     import torch
     stream = torch.cuda.Stream(device=dev)
@@ -220,7 +221,7 @@ def variants_timing(fk, wl, dev, args, bf):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
-    def append_body(case, pools):
+    def append_body(case, pools, window=0):
         q, nk, nv = bf(case.q), bf(case.new_k), bf(case.new_v)
         t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
         # request b's new token sits at its last position
@@ -230,7 +231,7 @@ def variants_timing(fk, wl, dev, args, bf):
         out = torch.empty_like(q)
         return lambda i: fk.fp8kv_decode_attn_append(pools[i % len(pools)], q, nk, nv, slot, t, sl,
                                                      case.max_seq_len, case.sm_scale, workspace=ws, out=out,
-                                                     stream=stream)
+                                                     stream=stream, window=window)
 
     def stage1_body(case, pools):
         q = bf(case.q)
@@ -283,6 +284,11 @@ def variants_timing(fk, wl, dev, args, bf):
     W = 4095
     run("window4095", c, rows_body(W), W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
         extra={"workload": "32K-context GQA-8 decode with a 4,095-key sliding window"})
+    c = wl.layer_decode(0)
+    run("window4095_append_step", c, lambda case, pools: append_body(case, pools, W),
+        W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
+        extra={"workload": "32K-context GQA-8 decode step (new token quantized on write) with a 4,095-key "
+                           "sliding window"})
     return res
 
 

@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
     L.fp8kv_decode_attn_append.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, f32, i32, vp, sz,
                                            vp, vp]
     L.fp8kv_decode_attn_append.restype = ctypes.c_int
+    L.fp8kv_decode_attn_append_window.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, i32, f32, i32,
+                                                  vp, sz, vp, vp]
+    L.fp8kv_decode_attn_append_window.restype = ctypes.c_int
     L.fp8kv_decode_stage1.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
     L.fp8kv_decode_stage1.restype = ctypes.c_int
     L.fp8kv_decode_merge.argtypes = [i32, i32, i32, i32, vp, sz, vp, vp]
@@ -290,9 +293,10 @@ def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tens
                              new_slots: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
                              max_seq_len: int, sm_scale: float, max_splits: int = 0,
                              workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                             stream=None) -> torch.Tensor:
+                             stream=None, window: int = 0) -> torch.Tensor:
     """One decode step: quantize each request's new token (k_new/v_new bf16 [B][Hkv][D]) into
-    pool row new_slots[b] (== row_table[b][seq_lens[b] - 1]) and attend over positions [0, seq_lens[b])."""
+    pool row new_slots[b] (== row_table[b][seq_lens[b] - 1]) and attend over positions [0, seq_lens[b])
+    (the last `window` of them when window > 0: fp8kv_decode_attn_append_window)."""
     a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
     B, D = a["B"], pool.head_dim
     _dev_check(k_new, "k_new", torch.bfloat16)
@@ -310,6 +314,14 @@ def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tens
         raise ValueError("new_slots must have B entries")
     if out is None:
         out = torch.empty_like(q)
+    if window:
+        st = load().fp8kv_decode_attn_append_window(a["pool"], a["q"], B, a["Hq"], _ptr(_bits(k_new)),
+                                                    _ptr(_bits(v_new)), stride, _ptr(new_slots), a["table"],
+                                                    a["table_stride"], a["seq_lens"], a["max_seq_len"], int(window),
+                                                    a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],
+                                                    _ptr(_bits(out)), _stream(stream))
+        _check(st, "fp8kv_decode_attn_append_window")
+        return out
     st = load().fp8kv_decode_attn_append(a["pool"], a["q"], B, a["Hq"], _ptr(_bits(k_new)), _ptr(_bits(v_new)), stride,
                                          _ptr(new_slots), a["table"], a["table_stride"], a["seq_lens"],
                                          a["max_seq_len"], a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],

@@ -293,15 +293,15 @@ fp8kv_status fp8kv_decode_attn_rows(const fp8kv_pool_layer* pool, const uint16_t
                     sm_scale, max_splits, workspace, out, nullptr, stream);
 }
 
-fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
-                                      int32_t n_q_heads, const uint16_t* k_new, const uint16_t* v_new,
-                                      int64_t new_token_stride, const int32_t* new_slots,
-                                      const int32_t* row_table, int64_t table_stride,
-                                      const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
-                                      int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
-                                      void* stream) {
-  fp8kv_status st = check_decode_args(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0,
-                                      sm_scale, max_splits, workspace, workspace_bytes);
+fp8kv_status fp8kv_decode_attn_append_window(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                                             int32_t n_q_heads, const uint16_t* k_new, const uint16_t* v_new,
+                                             int64_t new_token_stride, const int32_t* new_slots,
+                                             const int32_t* row_table, int64_t table_stride,
+                                             const int32_t* seq_lens, int32_t max_seq_len, int32_t window,
+                                             float sm_scale, int32_t max_splits, void* workspace,
+                                             size_t workspace_bytes, uint16_t* out, void* stream) {
+  fp8kv_status st = check_decode_args(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
+                                      window, sm_scale, max_splits, workspace, workspace_bytes);
   if (st != FP8KV_OK) return st;
   if (!out || !k_new || !v_new || !new_slots || max_seq_len < 1) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(new_slots, 4)) return FP8KV_ERR_ALIGNMENT;
@@ -309,8 +309,22 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16
   if (!aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || (new_token_stride % 8) != 0)
     return FP8KV_ERR_ALIGNMENT;
   const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale};
-  return run_decode(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0, sm_scale,
+  // Stage 1 covers the window's cached positions [p - window + 1, p); the new
+  // token at p is always inside the window, and the merge adds it.
+  return run_decode(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window, sm_scale,
                     max_splits, workspace, out, &app, stream);
+}
+
+fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                                      int32_t n_q_heads, const uint16_t* k_new, const uint16_t* v_new,
+                                      int64_t new_token_stride, const int32_t* new_slots,
+                                      const int32_t* row_table, int64_t table_stride,
+                                      const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                      int32_t max_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
+                                      void* stream) {
+  return fp8kv_decode_attn_append_window(pool, q, batch, n_q_heads, k_new, v_new, new_token_stride, new_slots,
+                                         row_table, table_stride, seq_lens, max_seq_len, 0, sm_scale, max_splits,
+                                         workspace, workspace_bytes, out, stream);
 }
 
 fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q, const uint16_t* k_cur,

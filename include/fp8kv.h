@@ -294,6 +294,26 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer *pool, const uint16
                                       size_t workspace_bytes, uint16_t *out, void *stream);
 
 /*
+ * fp8kv_decode_attn_append_window -- fp8kv_decode_attn_append with a sliding
+ * key window (FreeToken PR #897, "Regression and CUDA isolation": an odd
+ * sliding window is among the decode cases): the new token at p_b attends to
+ * positions max(0, p_b - window + 1) .. p_b, itself included; window == 0 means
+ * no window and is exactly fp8kv_decode_attn_append.  The effect is that of
+ *   fp8kv_quantize_rows(pool, k_new, v_new, new_token_stride, new_slots, batch)
+ * followed by fp8kv_decode_attn_rows with one query row and the same window.
+ *
+ * window:       >= 0.  Other arguments, the workspace and the errors are
+ *               those of fp8kv_decode_attn_append.
+ */
+fp8kv_status fp8kv_decode_attn_append_window(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                                             int32_t n_q_heads, const uint16_t *k_new, const uint16_t *v_new,
+                                             int64_t new_token_stride, const int32_t *new_slots,
+                                             const int32_t *row_table, int64_t table_stride,
+                                             const int32_t *seq_lens, int32_t max_seq_len, int32_t window,
+                                             float sm_scale, int32_t max_splits, void *workspace,
+                                             size_t workspace_bytes, uint16_t *out, void *stream);
+
+/*
  * fp8kv_prefill_attn -- attention of one prefill chunk over historical FP8 rows
  * of a pool with head_dim == 128
  * (FreeToken PR #853, "What changes": the prefill path reconstructs historical

@@ -169,6 +169,22 @@ def _append(lib, p, **kw):
                                         None)
 
 
+def _append_window(lib, p, window, **kw):
+    wsb = lib.fp8kv_decode_workspace_bytes(1, 32, p.head_dim, 0)
+    return lib.fp8kv_decode_attn_append_window(ctypes.byref(p), kw.get("q", A), 1, 32, kw.get("kn", A), 2 * A, 512,
+                                               A, A, 1024, A, kw.get("maxlen", 1000), window, 0.088, 0, A,
+                                               kw.get("wsb", wsb), kw.get("out", A), None)
+
+
+def test_decode_append_window_validation(lib):
+    p = _pool()
+    assert _append_window(lib, p, -1) == INVALID                     # negative window
+    assert _append_window(lib, p, 17, kn=0) == INVALID
+    assert _append_window(lib, p, 17, maxlen=0) == INVALID
+    assert _append_window(lib, p, 17, kn=A + 8) == ALIGN
+    assert _append_window(lib, p, 17, wsb=10) == WORKSPACE
+
+
 def test_decode_append_validation(lib):
     p = _pool()
     assert _append(lib, p, kn=0) == INVALID
@@ -232,6 +248,7 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert lib.fp8kv_decode_stage1(ctypes.byref(_pool()), A, 1, 32, A, 1024, A, 1000, 0.088, 0, A, wsb, None) == HIP
     assert lib.fp8kv_decode_merge(1, 32, 128, 0, A, wsb, A, None) == HIP
     assert _append(lib, _pool()) == HIP
+    assert _append_window(lib, _pool(), 17) == HIP
 
 
 def test_header_is_plain_c99_and_the_library_links(tmp_path, lib):

@@ -174,3 +174,61 @@ def test_append_graph_replay():
     ref_pools, ref = _oracle_step(case)
     _check_pool(pool, ref_pools, "graph")
     assert_close(bf16_to_f64(eager), ref, "graph")
+
+
+def _run_append_window(pool, case, window, max_splits=0):
+    lens = case.seq_lens
+    slots = np.array([case.table[b, lens[b] - 1] for b in range(case.batch)], np.int32)
+    out = fk.fp8kv_decode_attn_append(pool, to_dev_bf16(case.q), to_dev_bf16(case.new_k), to_dev_bf16(case.new_v),
+                                      to_dev(slots), to_dev(case.table), to_dev(np.asarray(lens, np.int32)),
+                                      int(lens.max()), case.sm_scale, max_splits=max_splits, window=window)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_step_window(case, window):
+    pools, _ = _oracle_step(case)
+    kc, vc, ks, vs = pools
+    out = oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale,
+                                  case.n_kv_heads, window=window)
+    return pools, out
+
+
+@pytest.mark.parametrize("W,L,D", [(1, 100, 128), (17, 1, 128), (17, 5000, 128), (4095, 32768, 128),
+                                   (4095, 3000, 128), (255, 20000, 256)])
+def test_append_window(W, L, D):
+    """The fused step with a sliding window: the pool ends up exactly as with
+    fp8kv_quantize_rows of the new token, and the new token (position L - 1)
+    attends to positions L - W .. L - 1 (W = 1: only itself)."""
+    say(f"decode+append with window {W}, {L} keys, D={D}")
+    case = wl.layer_decode(80 + W % 7, ctx=L, pool_rows=L + 59, head_dim=D)
+    pool = build_pool(case)
+    ref_pools, ref = _oracle_step_window(case, W)
+    out = bf16_to_f64(_run_append_window(pool, case, W))
+    _check_pool(pool, ref_pools, f"window {W}")
+    assert_close(out, ref, f"window {W} L={L}")
+
+
+@pytest.mark.parametrize("cap", [0, 3, 8])
+def test_append_window_batched(cap):
+    say(f"decode+append with window 1,023, 16 requests, max_splits={cap}")
+    case = wl.batched_decode(81, n_req=16, lo=1, hi=6000, with_new_token=True)
+    pool = build_pool(case)
+    ref_pools, ref = _oracle_step_window(case, 1023)
+    out = bf16_to_f64(_run_append_window(pool, case, 1023, max_splits=cap))
+    _check_pool(pool, ref_pools, f"window batched cap={cap}")
+    assert_close(out, ref, f"window batched cap={cap}")
+
+
+def test_append_window_covering_everything_is_the_plain_append():
+    """A window of at least the request length masks nothing: the windowed
+    stage 1 and merge give the plain fused step's output bit for bit."""
+    say("decode+append: a window covering every position == no window (bit-exact)")
+    case = wl.layer_decode(82, ctx=3000, pool_rows=3100)
+    pool_a = build_pool(case)
+    pool_b = build_pool(case)
+    a = _run_append(pool_a, case)
+    b = _run_append_window(pool_b, case, 3001)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for x, y in zip(pool_arrays(pool_a), pool_arrays(pool_b)):
+        assert_bits_equal(x, y, "pool")
