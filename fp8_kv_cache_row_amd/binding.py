@@ -83,6 +83,9 @@ def load() -> ctypes.CDLL:
     L.fp8kv_decode_attn_append_window.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, i32, f32, i32,
                                                   vp, sz, vp, vp]
     L.fp8kv_decode_attn_append_window.restype = ctypes.c_int
+    L.fp8kv_decode_attn_rows_append.argtypes = [P, vp, i32, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, i32, f32,
+                                                i32, vp, sz, vp, vp]
+    L.fp8kv_decode_attn_rows_append.restype = ctypes.c_int
     L.fp8kv_decode_stage1.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
     L.fp8kv_decode_stage1.restype = ctypes.c_int
     L.fp8kv_decode_merge.argtypes = [i32, i32, i32, i32, vp, sz, vp, vp]
@@ -286,6 +289,39 @@ def fp8kv_decode_attn_rows(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Te
                                        a["seq_lens"], a["max_seq_len"], int(window), a["sm_scale"], a["max_splits"],
                                        a["ws"], a["ws_bytes"], _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_decode_attn_rows")
+    return out
+
+
+def fp8kv_decode_attn_rows_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  new_slots: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                                  max_seq_len: int, sm_scale: float, window: int = 0, max_splits: int = 0,
+                                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                                  stream=None) -> torch.Tensor:
+    """Several new tokens per request in one step: quantize token j of request b (k_new/v_new bf16
+    [B][n_qrows][Hkv][D]) into pool row new_slots[b][j] (== row_table[b][seq_lens[b] - n_qrows + j])
+    and attend with the n_qrows causal query rows (q bf16 [B][n_qrows][Hq][D]), optionally within a
+    sliding window of `window` keys."""
+    a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace,
+                                multi=True)
+    B, nq, D = a["B"], a["nq"], pool.head_dim
+    _dev_check(k_new, "k_new", torch.bfloat16)
+    _dev_check(v_new, "v_new", torch.bfloat16)
+    shape = (B, nq, pool.n_kv_heads, D)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new/v_new must be {list(shape)}, got {tuple(k_new.shape)} / {tuple(v_new.shape)}")
+    if not k_new.is_contiguous() or not v_new.is_contiguous():
+        raise ValueError("k_new and v_new must be contiguous")
+    _dev_check(new_slots, "new_slots", torch.int32)
+    if new_slots.numel() != B * nq or not new_slots.is_contiguous():
+        raise ValueError("new_slots must be a contiguous [B][n_qrows] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().fp8kv_decode_attn_rows_append(a["pool"], a["q"], B, nq, a["Hq"], _ptr(_bits(k_new)),
+                                              _ptr(_bits(v_new)), pool.n_kv_heads * D, _ptr(new_slots), a["table"],
+                                              a["table_stride"], a["seq_lens"], a["max_seq_len"], int(window),
+                                              a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],
+                                              _ptr(_bits(out)), _stream(stream))
+    _check(st, "fp8kv_decode_attn_rows_append")
     return out
 
 

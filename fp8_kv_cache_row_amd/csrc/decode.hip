@@ -203,9 +203,10 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 
   // Positions: request length len; query row i sits at p_i = len - n_qrows + i
   // and sees positions [lo_i, p_i] (lo_i = p_i + 1 - window with a window).
-  // With key_trim = 1 (one row) the last position is left to the merge.
+  // With key_trim = k the last k positions (the new tokens of an appending
+  // call) are left to the merge.
   const int len = min(__builtin_amdgcn_readfirstlane(len_lane), max_seq_len);
-  const int first_end = len - n_qrows + 1 - key_trim;  // end of the first row's keys
+  const int first_end = min(len - n_qrows + 1, len - key_trim);  // end of the first row's keys
   int last_lo = 0;                                     // largest lowest visible position
   if constexpr (C::WINDOW) {
     const int first_lo = max(0, len - n_qrows + 1 - window);
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int p = len - n_qrows + col_row[t];
-    cend[t] = min(p + 1 - key_trim, key_end);
+    cend[t] = min(p + 1, key_end);
     clo[t] = C::WINDOW ? max(0, p + 1 - window) : 0;
   }
 
@@ -505,6 +506,8 @@ struct AppendKernelArgs {
   int32_t n_kv_heads;
   uint32_t max_row;
   float qk_scale_log2;
+  int32_t n_qrows;  // new tokens (and query rows) per request
+  int32_t window;   // 0: every new token j <= i is visible to query row i
 };
 
 // E consecutive values per lane: bf16 bit patterns in E/2 dwords, fp32 in a vector.
@@ -540,14 +543,24 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   vecu k2 = {}, v2 = {}, q2 = {};
   int64_t slot = 0;
   int64_t b = 0, g = 0;
+  // Query row i of request b; wave j < n_new takes new token j (position
+  // seq_lens[b] - n_qrows + j), visible to row i when j <= i and inside the
+  // window.
+  int qi = 0, n_new = 0;
+  bool visible = false;
   if constexpr (APPEND) {
-    b = bh / n_q_heads;
+    const int64_t bq = bh / n_q_heads;
+    b = bq / app.n_qrows;
+    qi = (int)(bq - b * app.n_qrows);
+    n_new = qi + 1;
     const int h = (int)(bh % n_q_heads);
     g = h / (n_q_heads / app.n_kv_heads);
-    if (wave == 0) {
-      slot = min((uint32_t)app.new_slots[b], app.max_row);  // out-of-range slots are clamped, never followed
-      k2 = *reinterpret_cast<const vecu*>(app.k_new + b * app.new_token_stride + g * D + E * lane);
-      v2 = *reinterpret_cast<const vecu*>(app.v_new + b * app.new_token_stride + g * D + E * lane);
+    visible = wave < n_new && (app.window == 0 || qi - wave < app.window);
+    if (wave < n_new) {
+      const int64_t tok = b * app.n_qrows + wave;
+      slot = min((uint32_t)app.new_slots[tok], app.max_row);  // out-of-range slots are clamped, never followed
+      k2 = *reinterpret_cast<const vecu*>(app.k_new + tok * app.new_token_stride + g * D + E * lane);
+      v2 = *reinterpret_cast<const vecu*>(app.v_new + tok * app.new_token_stride + g * D + E * lane);
       q2 = *reinterpret_cast<const vecu*>(app.q + bh * D + E * lane);
     }
   }
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   float lse_new = -INFINITY;
   vecf o_new = {};
   if constexpr (APPEND) {
-    if (wave == 0) {
+    if (wave < n_new) {
       // Quantize the K and V rows (D values over the wave, E per lane).
       float kx[E], vx[E], qx[E];
       float ka = 0.f, va = 0.f;
@@ -631,8 +644,10 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
       lse_new = dot * sk * app.qk_scale_log2;
 #pragma unroll
       for (int e = 0; e < E; ++e) o_new[e] = vd[e] * sv;
-      // One workgroup per (request, KV head) stores the row.
-      if ((bh % n_q_heads) % (n_q_heads / app.n_kv_heads) == 0) {
+      // One workgroup per (request, KV head) stores the rows: the one of the
+      // group's first query head and the last query row, which holds every
+      // new token.
+      if ((bh % n_q_heads) % (n_q_heads / app.n_kv_heads) == 0 && qi == app.n_qrows - 1) {
         uint8_t* kdst = app.k_codes + slot * app.code_row_stride + g * D + E * lane;
         uint8_t* vdst = app.v_codes + slot * app.code_row_stride + g * D + E * lane;
         if constexpr (E == 2) {
@@ -657,7 +672,7 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   }
 
   if constexpr (APPEND) {
-    if (wave == 0) {  // the new token as one more single-key partial
+    if (visible) {  // the wave's new token as one more single-key partial
       const float mx = fmaxf(m_w, lse_new);
       const float a = __builtin_amdgcn_exp2f(m_w - mx);
       const float w = __builtin_amdgcn_exp2f(lse_new - mx);
@@ -742,13 +757,14 @@ hipError_t launch_stage1_single(const PoolView& pool, const uint16_t* q, const D
 // Several rows per request: NT column tiles per workgroup, G at run time.
 template <int D, bool WINDOW, int F>
 hipError_t launch_stage1_multi(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
-                               const DecodeGeometry& geo, const DecodeWorkspace& ws, hipStream_t stream) {
+                               const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
+                               hipStream_t stream) {
   switch (geo.col_tiles) {
-    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, 0, stream);
-    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, 0, stream);
+    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
     case 4:
       if constexpr (D == 128)
-        return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, 0, stream);
+        return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -769,13 +785,12 @@ hipError_t launch_stage1_format(const PoolView& pool, const uint16_t* q, const D
                     : launch_stage1_single<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
     return hipErrorInvalidValue;
   }
-  if (key_trim != 0) return hipErrorInvalidValue;
   if (pool.head_dim == 128)
-    return window ? launch_stage1_multi<128, true, F>(pool, q, sh, qk, geo, ws, stream)
-                  : launch_stage1_multi<128, false, F>(pool, q, sh, qk, geo, ws, stream);
+    return window ? launch_stage1_multi<128, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                  : launch_stage1_multi<128, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
   if (pool.head_dim == 256)
-    return window ? launch_stage1_multi<256, true, F>(pool, q, sh, qk, geo, ws, stream)
-                  : launch_stage1_multi<256, false, F>(pool, q, sh, qk, geo, ws, stream);
+    return window ? launch_stage1_multi<256, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
+                  : launch_stage1_multi<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
   return hipErrorInvalidValue;
 }
 
@@ -821,11 +836,12 @@ hipError_t launch_decode_merge(int64_t n_rows_heads, int32_t head_dim, const Dec
 
 hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,
                                       int32_t n_split, const AppendArgs& app, uint16_t* out, hipStream_t stream) {
+  if (app.n_qrows < 1 || app.n_qrows > kMergeWaves) return hipErrorInvalidValue;  // one wave per new token
   const AppendKernelArgs a{app.q, app.k_new, app.v_new, app.new_token_stride, app.new_slots,
                            pool.k_codes, pool.v_codes, pool.k_scales, pool.v_scales,
                            pool.code_row_stride, pool.scale_row_stride, pool.n_kv_heads,
-                           (uint32_t)(pool.num_rows - 1), app.sm_scale * kLog2e};
-  const dim3 grid((unsigned)((int64_t)batch * n_q_heads));
+                           (uint32_t)(pool.num_rows - 1), app.sm_scale * kLog2e, app.n_qrows, app.window};
+  const dim3 grid((unsigned)((int64_t)batch * app.n_qrows * n_q_heads));
   const bool i8 = pool.format == kInt8;
   if (pool.head_dim == 128 && !i8)
     hipLaunchKernelGGL((decode_merge_kernel<128, true, kE4M3>), grid, dim3(kMergeBlock), 0, stream, ws.header,

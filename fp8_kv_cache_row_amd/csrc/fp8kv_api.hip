@@ -210,7 +210,7 @@ fp8kv_status run_decode(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t
   const fp8kv::DecodeWorkspace ws = workspace_view(workspace, n_queries, n_q_heads, pool->head_dim, max_splits);
   const fp8kv::DecodeShape shape{batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? 1 : 0, s);
+  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? n_qrows : 0, s);
   if (e != hipSuccess) return FP8KV_ERR_HIP;
   if (app) return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), batch, n_q_heads, ws, geo.n_split, *app, out, s));
   if (!out) return FP8KV_OK;
@@ -308,11 +308,33 @@ fp8kv_status fp8kv_decode_attn_append_window(const fp8kv_pool_layer* pool, const
   if (new_token_stride < (int64_t)pool->n_kv_heads * pool->head_dim) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || (new_token_stride % 8) != 0)
     return FP8KV_ERR_ALIGNMENT;
-  const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale};
+  const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale, 1, window};
   // Stage 1 covers the window's cached positions [p - window + 1, p); the new
   // token at p is always inside the window, and the merge adds it.
   return run_decode(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window, sm_scale,
                     max_splits, workspace, out, &app, stream);
+}
+
+fp8kv_status fp8kv_decode_attn_rows_append(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                                           int32_t n_qrows, int32_t n_q_heads, const uint16_t* k_new,
+                                           const uint16_t* v_new, int64_t new_token_stride,
+                                           const int32_t* new_slots, const int32_t* row_table, int64_t table_stride,
+                                           const int32_t* seq_lens, int32_t max_seq_len, int32_t window,
+                                           float sm_scale, int32_t max_splits, void* workspace,
+                                           size_t workspace_bytes, uint16_t* out, void* stream) {
+  fp8kv_status st = check_decode_args(pool, q, batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens,
+                                      max_seq_len, window, sm_scale, max_splits, workspace, workspace_bytes);
+  if (st != FP8KV_OK) return st;
+  if (!out || !k_new || !v_new || !new_slots || max_seq_len < n_qrows) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(new_slots, 4)) return FP8KV_ERR_ALIGNMENT;
+  if (new_token_stride < (int64_t)pool->n_kv_heads * pool->head_dim) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || (new_token_stride % 8) != 0)
+    return FP8KV_ERR_ALIGNMENT;
+  const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale, n_qrows, window};
+  // Stage 1 covers the cached positions below the request's n_qrows new
+  // tokens; the merge of query row i adds the new tokens j <= i in its window.
+  return run_decode(pool, q, batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window,
+                    sm_scale, max_splits, workspace, out, &app, stream);
 }
 
 fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,

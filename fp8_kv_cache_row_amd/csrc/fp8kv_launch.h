@@ -109,8 +109,10 @@ struct AppendArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t new_token_stride;  // elements
-  const int32_t* new_slots;
+  const int32_t* new_slots;  // [batch][n_qrows]
   float sm_scale;
+  int32_t n_qrows;  // new tokens per request, the request's last n_qrows positions
+  int32_t window;   // sliding key window (0: none)
 };
 hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32_t n_q_heads, const DecodeWorkspace& ws,
                                       int32_t n_split, const AppendArgs& app, uint16_t* out, hipStream_t stream);

@@ -314,6 +314,42 @@ fp8kv_status fp8kv_decode_attn_append_window(const fp8kv_pool_layer *pool, const
                                              size_t workspace_bytes, uint16_t *out, void *stream);
 
 /*
+ * fp8kv_decode_attn_rows_append -- fp8kv_decode_attn_rows with the new tokens'
+ * quantize-on-write folded in: each request's last n_qrows positions are new
+ * tokens (FreeToken PR #897 description: #900's multi-row decode of up to 8
+ * query rows per request), written to their rows and attended in one call.
+ *
+ * Request b's new token j (0 <= j < n_qrows) sits at position
+ * p_bj = seq_lens[b] - n_qrows + j; its bf16 K/V are at
+ * k_new / v_new + (b * n_qrows + j) * new_token_stride ([n_kv_heads][D]) and
+ * its pool row is new_slots[b * n_qrows + j] (== row_table[b][p_bj]).  The
+ * call has the effect of
+ *   fp8kv_quantize_rows(pool, k_new, v_new, new_token_stride, new_slots,
+ *                       batch * n_qrows)
+ * followed by fp8kv_decode_attn_rows with the same arguments and window: the
+ * codes and scales land bit for bit as fp8kv_quantize_rows writes them, and
+ * query row j of request b attends causally (and within the window) over
+ * positions up to p_bj.  Stage 1 covers the cached positions below the new
+ * tokens; the merge quantizes the new tokens and adds the visible ones.
+ *
+ * q, out:       device bf16 [batch][n_qrows][n_q_heads][D], 16-byte aligned.
+ * seq_lens:     device int32 [batch], each in [n_qrows, max_seq_len].
+ * new_slots:    device int32 [batch * n_qrows], 4-byte aligned, distinct, not
+ *               named by any cached position (clamped like table entries).
+ * n_qrows:      1 .. FP8KV_MAX_QUERY_ROWS; max_seq_len >= n_qrows.
+ * Other arguments, the workspace (fp8kv_decode_workspace_bytes(batch *
+ * n_qrows, ...)) and the errors are those of fp8kv_decode_attn_rows and
+ * fp8kv_decode_attn_append.
+ */
+fp8kv_status fp8kv_decode_attn_rows_append(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                                           int32_t n_qrows, int32_t n_q_heads, const uint16_t *k_new,
+                                           const uint16_t *v_new, int64_t new_token_stride,
+                                           const int32_t *new_slots, const int32_t *row_table,
+                                           int64_t table_stride, const int32_t *seq_lens, int32_t max_seq_len,
+                                           int32_t window, float sm_scale, int32_t max_splits, void *workspace,
+                                           size_t workspace_bytes, uint16_t *out, void *stream);
+
+/*
  * fp8kv_prefill_attn -- attention of one prefill chunk over historical FP8 rows
  * of a pool with head_dim == 128
  * (FreeToken PR #853, "What changes": the prefill path reconstructs historical

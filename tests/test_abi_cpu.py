@@ -185,6 +185,25 @@ def test_decode_append_window_validation(lib):
     assert _append_window(lib, p, 17, wsb=10) == WORKSPACE
 
 
+def _rows_append(lib, p, nq=3, **kw):
+    wsb = lib.fp8kv_decode_workspace_bytes(nq, 32, p.head_dim, 0)
+    return lib.fp8kv_decode_attn_rows_append(ctypes.byref(p), kw.get("q", A), 1, nq, 32, kw.get("kn", A), 2 * A, 512,
+                                             A, A, 1024, A, kw.get("maxlen", 1000), kw.get("window", 0), 0.088, 0,
+                                             A, kw.get("wsb", wsb), kw.get("out", A), None)
+
+
+def test_decode_rows_append_validation(lib):
+    p = _pool()
+    assert _rows_append(lib, p, nq=0) == INVALID
+    assert _rows_append(lib, p, nq=9) == INVALID                     # more than FP8KV_MAX_QUERY_ROWS
+    assert _rows_append(lib, p, nq=8, maxlen=7) == INVALID           # every new token needs a position
+    assert _rows_append(lib, p, window=-1) == INVALID
+    assert _rows_append(lib, p, kn=0) == INVALID
+    assert _rows_append(lib, p, out=A + 2) == ALIGN
+    one_row = lib.fp8kv_decode_workspace_bytes(1, 32, 128, 0)
+    assert _rows_append(lib, p, nq=3, wsb=one_row) == WORKSPACE       # partials for 3 rows
+
+
 def test_decode_append_validation(lib):
     p = _pool()
     assert _append(lib, p, kn=0) == INVALID
@@ -249,6 +268,7 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert lib.fp8kv_decode_merge(1, 32, 128, 0, A, wsb, A, None) == HIP
     assert _append(lib, _pool()) == HIP
     assert _append_window(lib, _pool(), 17) == HIP
+    assert _rows_append(lib, _pool(), nq=8, window=5) == HIP
 
 
 def test_header_is_plain_c99_and_the_library_links(tmp_path, lib):
