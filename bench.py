@@ -191,7 +191,8 @@ def rotated_pools(fk, case, layout, n, dev, bf, fmt="e4m3"):
 def variants_timing(fk, wl, dev, args, bf):
     """The decode variants at 32K context, each over rotated cold pools:
     head dim 256 (fused append step and stage 1 alone), 3 and 8 causal query
-    rows per request, the INT8 KV format (fused append step and stage 1
+    rows per request (and the 8-row step with its new tokens written in the
+    same call), the INT8 KV format (fused append step and stage 1
     alone), the 16-request GQA-4 batch (fused step and stage 1 alone), an odd
     4,095-key sliding window (query rows call, and the fused step), and with
     --model-step the 48-layer step at 40,000 context."""
@@ -256,6 +257,20 @@ def variants_timing(fk, wl, dev, args, bf):
         extra={"workload": "32K-context GQA-8 decode step at head dim 256 (32 q / 4 KV heads)"})
     run("d256_stage1", c256, stage1_body, kv256)
     del c256
+    def rows_append_body(case, pools):
+        nq = case.q.shape[1]
+        rng = np.random.default_rng(1)
+        shape = (1, nq, case.n_kv_heads, 128)
+        nk, nv = bf(wl.bf16_bits(wl.draw_normal(rng, shape))), bf(wl.bf16_bits(wl.draw_normal(rng, shape, 0.5)))
+        q = bf(case.q)
+        t, sl = torch.from_numpy(case.table).to(dev), torch.from_numpy(case.seq_lens).to(dev)
+        slots = torch.from_numpy(np.ascontiguousarray(case.table[:, -nq:])).to(dev)
+        ws = fk.decode_workspace(nq, case.n_q_heads, device=dev)
+        out = torch.empty_like(q)
+        return lambda i: fk.fp8kv_decode_attn_rows_append(pools[i % len(pools)], q, nk, nv, slots, t, sl,
+                                                          case.max_seq_len, case.sm_scale, workspace=ws, out=out,
+                                                          stream=stream)
+
     for nq in (3, 8):
         c = wl.layer_decode(0, with_new_token=False, n_qrows=nq)
         kv = c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
@@ -263,6 +278,10 @@ def variants_timing(fk, wl, dev, args, bf):
         pairs = nq * L - nq * (nq - 1) // 2          # causal (row, key) pairs per head
         run(f"rows{nq}", c, rows_body(0), kv, flop=4.0 * 128 * pairs * c.n_q_heads,
             extra={"workload": f"32K-context GQA-8 decode, {nq} causal query rows per request"})
+        if nq == 8:
+            run("rows8_append_step", c, rows_append_body, kv, flop=4.0 * 128 * pairs * c.n_q_heads,
+                extra={"workload": "32K-context GQA-8 decode step with 8 new tokens quantized on write and "
+                                   "attended by their causal query rows"})
     c = wl.layer_decode(0)
     kv = c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
     run("int8_append_step", c, append_body, kv, fmt="int8",
