@@ -13,6 +13,14 @@
  * "Regression and CUDA isolation" widens the decode matrix to head dim 256,
  * 1/3/8 query rows per request and an odd sliding window.
  *
+ * Entry points: fp8kv_quantize_rows (quantize-on-write); fp8kv_decode_attn and
+ * its two stages fp8kv_decode_stage1 / fp8kv_decode_merge; fp8kv_decode_attn_rows
+ * (several query rows, sliding window); fp8kv_decode_attn_append,
+ * fp8kv_decode_attn_append_window and fp8kv_decode_attn_rows_append (a decode
+ * step with its new tokens quantized on write in the same call);
+ * fp8kv_prefill_attn (reconstruct + causal chunk attention);
+ * fp8kv_decode_workspace_bytes and fp8kv_status_string.
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
