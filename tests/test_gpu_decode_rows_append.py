@@ -110,3 +110,40 @@ def test_rows_append_one_row_is_the_fused_step():
     assert torch.equal(a.view(torch.int16), b[:, 0].view(torch.int16))
     for x, y in zip(pool_arrays(pool_a), pool_arrays(pool_b)):
         assert_bits_equal(x, y, "pool")
+
+
+def test_rows_append_graph_replay():
+    """Captured in a HIP graph and replayed three times, with eager work and
+    synchronizations between the replays: every replay's output and pool are
+    bit-identical to the eager call's (rewriting the same new tokens)."""
+    say("rows+append captured in a graph, 3 replays vs eager")
+    case = wl.layer_decode(95, ctx=6000, pool_rows=6100, with_new_token=False, n_qrows=3)
+    k, v, slots = _new_tokens(case, 3, 95)
+    pool = build_pool(case)
+    dev = {"q": to_dev_bf16(case.q), "k": to_dev_bf16(k), "v": to_dev_bf16(v), "s": to_dev(slots),
+           "t": to_dev(case.table), "l": to_dev(case.seq_lens)}
+    ws = fk.decode_workspace(3, case.n_q_heads)
+    out = torch.empty_like(dev["q"])
+    stream = torch.cuda.Stream()
+
+    def call():
+        fk.fp8kv_decode_attn_rows_append(pool, dev["q"], dev["k"], dev["v"], dev["s"], dev["t"], dev["l"],
+                                         case.max_seq_len, case.sm_scale, window=17, workspace=ws, out=out,
+                                         stream=stream)
+
+    with torch.cuda.stream(stream):
+        call()
+    stream.synchronize()
+    ref_out = out.clone()
+    ref_pool = pool_arrays(pool)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        call()
+    for rep in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}"
+        for a, b in zip(pool_arrays(pool), ref_pool):
+            assert_bits_equal(a, b, f"replay {rep}: pool")
