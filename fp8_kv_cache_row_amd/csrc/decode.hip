@@ -33,6 +33,10 @@
 //    moves (and O is rescaled) only when a step's maximum exceeds it by more
 //    than 8, so p stays below 2^8 and most steps skip the rescale.
 //  * Waves merge through LDS; one (o, log2-sum-exp) partial per split.
+//  * The grid places the KV heads of one split on one XCD, next to each other
+//    in dispatch order, so they share that XCD's L2 lines of the table and of
+//    the rows' scales; grids of several rounds (batches, long contexts) use
+//    512-key splits and a streaming shape of three 4-wave workgroups per CU.
 
 #include <math.h>
 
@@ -475,14 +479,15 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 // LDS -- a single memory round trip.  Lane l owns d = E*l .. E*l + E-1
 // (E = D / 64).
 //
-// With APPEND (one query row per request), wave 0 also takes the request's
-// new token (position seq_lens[b] - 1, left out of stage 1): it quantizes the
-// bf16 K and V rows of the head group exactly as the quantize-on-write kernel
-// does (same codec functions), scores q against the decoded codes, and folds
-// the token in as a single-key partial (o = s_v * decode(v), lse = the score).
-// The workgroup of the group's first query head writes the codes and scales
-// to the token's row new_slots[b]; every load of the kernel is independent
-// (one round trip).
+// With APPEND, the request's last n_qrows positions are new tokens, left out
+// of stage 1; in the workgroup of query row i, wave j <= i takes new token j:
+// it quantizes the token's bf16 K and V rows of the head group exactly as the
+// quantize-on-write kernel does (same codec functions), scores q against the
+// decoded codes, and, when the token lies inside the row's window, folds it in
+// as a single-key partial (o = s_v * decode(v), lse = the score).  The
+// workgroup of the group's first query head and the last query row writes the
+// codes and scales to the tokens' rows new_slots[b][j]; every load of the
+// kernel is independent (one round trip).
 #ifndef FP8KV_MERGE_WAVES
 #define FP8KV_MERGE_WAVES 8
 #endif
