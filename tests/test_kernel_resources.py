@@ -40,7 +40,15 @@ def test_no_kernel_spills(src, tmp_path):
         assert not kernels
         return
     assert kernels, "no kernels reported"
+    streaming = 0
     for name, res in kernels.items():
         print(f"{name[:90]:90s} VGPR {res.get('VGPRs')} AGPR {res.get('AGPRs')} LDS {res.get('LDS')}")
         assert res.get("ScratchSize") == 0, f"{name} uses {res.get('ScratchSize')} bytes of scratch per lane"
         assert res.get("VGPRs", 0) + res.get("AGPRs", 0) <= 512
+        # Stage1<G, D, NT, MULTI, WINDOW, F, STREAM = true>, as mangled
+        if re.search(r"Stage1ILi\d+ELi\d+ELi\d+ELb[01]ELb[01]ELi\d+ELb1E", name):
+            # the streaming shape: three 4-wave workgroups per CU need <= 168 registers
+            assert res.get("VGPRs", 0) + res.get("AGPRs", 0) <= 168, f"{name}: streaming shape over 168 registers"
+            streaming += 1
+    if os.path.basename(src) == "decode.hip":
+        assert streaming == 10, f"{streaming} streaming stage-1 instantiations (5 GQA ratios x 2 code formats)"
