@@ -80,9 +80,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(layout: str):
-    """HBM bytes per stage-1 launch from the committed rocprofv3 counter runs,
-    or None when they were taken on a different kernel source or pool layout."""
+def measured_traffic(layout: str, cold_pools: int):
+    """HBM bytes per stage-1 launch from the committed rocprofv3 counter runs
+    (taken on the default workload: 12 rotated pool copies, cold), or None when
+    they were taken on a different kernel source, pool layout or workload."""
+    if cold_pools != 12:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -547,7 +550,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.layout),
+            "traffic": measured_traffic(args.layout, 0 if args.warm else args.pools),
         },
     }
     if not args.no_prefill:
