@@ -186,12 +186,16 @@ def _run_append_window(pool, case, window, max_splits=0):
     return out
 
 
-def _oracle_step_window(case, window):
-    pools, _ = _oracle_step(case)
-    kc, vc, ks, vs = pools
+def _oracle_step_window(case, window, fmt="e4m3"):
+    kc, vc, ks, vs = oracle_pool(case, fmt)
+    nkc, nks = oracle.quantize_rows(case.new_k, fmt)
+    nvc, nvs = oracle.quantize_rows(case.new_v, fmt)
+    for b in range(case.batch):
+        row = int(case.table[b, case.seq_lens[b] - 1])
+        kc[row], vc[row], ks[row], vs[row] = nkc[b], nvc[b], nks[b], nvs[b]
     out = oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale,
-                                  case.n_kv_heads, window=window)
-    return pools, out
+                                  case.n_kv_heads, window=window, fmt=fmt)
+    return (kc, vc, ks, vs), out
 
 
 @pytest.mark.parametrize("W,L,D", [(1, 100, 128), (17, 1, 128), (17, 5000, 128), (4095, 32768, 128),
@@ -232,3 +236,14 @@ def test_append_window_covering_everything_is_the_plain_append():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     for x, y in zip(pool_arrays(pool_a), pool_arrays(pool_b)):
         assert_bits_equal(x, y, "pool")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_append_window_int8_pool(D):
+    say(f"decode+append with window 255 over an INT8 pool, D={D}")
+    case = wl.layer_decode(83, ctx=12000, pool_rows=12100, head_dim=D)
+    pool = build_pool(case, fmt="int8")
+    ref_pools, ref = _oracle_step_window(case, 255, fmt="int8")
+    out = bf16_to_f64(_run_append_window(pool, case, 255))
+    _check_pool(pool, ref_pools, f"int8 window D={D}")
+    assert_close(out, ref, f"int8 window D={D}")

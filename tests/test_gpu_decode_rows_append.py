@@ -83,15 +83,16 @@ def test_rows_append_batched(cap, W):
     assert_close(got, ref, f"batched cap={cap} W={W}")
 
 
-def test_rows_append_int8_pool():
-    say("rows+append over an INT8 pool: 8 new tokens, 9,000 keys")
-    case = wl.layer_decode(93, ctx=9000, pool_rows=9100, with_new_token=False, n_qrows=8)
-    k, v, slots = _new_tokens(case, 8, 93)
+@pytest.mark.parametrize("nq,D,W", [(8, 128, 0), (3, 256, 17), (8, 128, 5)])
+def test_rows_append_int8_pool(nq, D, W):
+    say(f"rows+append over an INT8 pool: {nq} new tokens, D={D}, window {W}, 9,000 keys")
+    case = wl.layer_decode(93 + W, ctx=9000, pool_rows=9100, with_new_token=False, n_qrows=nq, head_dim=D)
+    k, v, slots = _new_tokens(case, nq, 93 + W)
     pool = build_pool(case, fmt="int8")
-    ref_pools, ref = _oracle(case, k, v, slots, 0, fmt="int8")
-    got = _run(pool, case, k, v, slots, 0)
-    _check(pool, ref_pools, "int8")
-    assert_close(got, ref, "int8 rows+append")
+    ref_pools, ref = _oracle(case, k, v, slots, W, fmt="int8")
+    got = _run(pool, case, k, v, slots, W)
+    _check(pool, ref_pools, f"int8 nq={nq} W={W}")
+    assert_close(got, ref, f"int8 rows+append nq={nq} D={D} W={W}")
 
 
 def test_rows_append_one_row_is_the_fused_step():
