@@ -539,8 +539,10 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   // A split count read from the workspace is clamped to its capacity, so a
-  // workspace that no stage 1 wrote cannot send the loads past it.
+  // workspace that no stage 1 wrote cannot send the loads past it; a count of
+  // 0 loads split 0 (inside the workspace), folds nothing and stores zeros.
   const int n_split = n_split_arg >= 0 ? n_split_arg : min(max(header[0], 0), split_stride);
+  const int last_split = max(n_split - 1, 0);
   const float* lse_p = part_lse + bh * split_stride;
   const float* po = part_o + bh * split_stride * D + E * lane;
 
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   auto load_batch = [&](int base) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const int sidx = min(base + wave + kMergeWaves * i, n_split - 1);
+      const int sidx = min(base + wave + kMergeWaves * i, last_split);
       lr[i] = lse_p[sidx];
       v[i] = *reinterpret_cast<const vecf*>(po + (int64_t)sidx * D);
     }

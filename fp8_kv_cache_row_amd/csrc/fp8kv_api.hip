@@ -23,11 +23,14 @@ fp8kv_status from_hip(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// NaN test on the bit pattern, independent of floating-point compile flags.
-bool is_nan(float x) {
+// A softmax scale must be finite and positive: every kernel takes the running
+// maximum of scaled scores, and only a positive finite factor keeps that the
+// maximum of the raw scores (zero would also make masked keys 0 * -inf).
+// Tested on the bit pattern, independent of floating-point compile flags.
+bool valid_softmax_scale(float x) {
   uint32_t u;
   memcpy(&u, &x, sizeof(u));
-  return (u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u;
+  return (u & 0x80000000u) == 0u && (u & 0x7f800000u) != 0x7f800000u && u != 0u;
 }
 
 bool supported_group(int32_t n_q_heads, int32_t n_kv_heads) {
@@ -168,11 +171,12 @@ fp8kv::DecodeWorkspace workspace_view(void* workspace, int64_t n_queries, int32_
 
 bool valid_head_dim(int32_t d) { return d == FP8KV_HEAD_DIM || d == FP8KV_HEAD_DIM_256; }
 
-// Checks shared by every decode entry point.
-fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
-                               int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
-                               const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float sm_scale,
-                               int32_t max_splits, const void* workspace, size_t workspace_bytes) {
+// Checks shared by every decode entry point (check_decode_shape), and the
+// caller's workspace of the calls that take one (check_decode_workspace).
+fp8kv_status check_decode_shape(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
+                                int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                                const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float sm_scale,
+                                int32_t max_splits) {
   fp8kv_status st = check_pool(pool);
   if (st != FP8KV_OK) return st;
   if (!q || !row_table || !seq_lens) return FP8KV_ERR_INVALID_ARG;
@@ -187,8 +191,13 @@ fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, 
     column_split(pool->head_dim, n_q_heads / pool->n_kv_heads, n_qrows, &col_tiles, &n_col_groups);
     if ((int64_t)batch * n_col_groups > FP8KV_MAX_DECODE_GROUPS) return FP8KV_ERR_UNSUPPORTED;
   }
-  if (is_nan(sm_scale)) return FP8KV_ERR_INVALID_ARG;
+  if (!valid_softmax_scale(sm_scale)) return FP8KV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(row_table, 4) || !aligned(seq_lens, 4)) return FP8KV_ERR_ALIGNMENT;
+  return FP8KV_OK;
+}
+
+fp8kv_status check_decode_workspace(const fp8kv_pool_layer* pool, int32_t batch, int32_t n_qrows, int32_t n_q_heads,
+                                    int32_t max_splits, const void* workspace, size_t workspace_bytes) {
   if (!workspace ||
       workspace_bytes < partial_bytes((int64_t)batch * n_qrows, n_q_heads, pool->head_dim, split_cap(max_splits)))
     return FP8KV_ERR_WORKSPACE;
@@ -196,7 +205,33 @@ fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, 
   return FP8KV_OK;
 }
 
-// Stage 1 (and the merge unless `app` is given) of one decode call.
+fp8kv_status check_decode_args(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
+                               int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                               const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float sm_scale,
+                               int32_t max_splits, const void* workspace, size_t workspace_bytes) {
+  fp8kv_status st = check_decode_shape(pool, q, batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens,
+                                       max_seq_len, window, sm_scale, max_splits);
+  if (st != FP8KV_OK) return st;
+  return check_decode_workspace(pool, batch, n_qrows, n_q_heads, max_splits, workspace, workspace_bytes);
+}
+
+// Stage 1 (and the merge unless `app` is given) of one decode call, with the
+// geometry and workspace view already fixed.
+fp8kv_status launch_decode(const fp8kv_pool_layer* pool, const uint16_t* q, const fp8kv::DecodeShape& shape,
+                           float sm_scale, const fp8kv::DecodeGeometry& geo, const fp8kv::DecodeWorkspace& ws,
+                           uint16_t* out, const fp8kv::AppendArgs* app, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n_queries = (int64_t)shape.batch * shape.n_qrows;
+  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? shape.n_qrows : 0, s);
+  if (e != hipSuccess) return FP8KV_ERR_HIP;
+  if (app)
+    return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), shape.batch, shape.n_q_heads, ws, geo.n_split,
+                                                      *app, out, s));
+  if (!out) return FP8KV_OK;
+  return from_hip(fp8kv::launch_decode_merge(n_queries * shape.n_q_heads, pool->head_dim, ws, geo.n_split, out, s));
+}
+
+// A decode call over the caller's workspace (split stride = the split cap).
 fp8kv_status run_decode(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch, int32_t n_qrows,
                         int32_t n_q_heads, const int32_t* row_table, int64_t table_stride, const int32_t* seq_lens,
                         int32_t max_seq_len, int32_t window, float sm_scale, int32_t max_splits, void* workspace,
@@ -209,12 +244,7 @@ fp8kv_status run_decode(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t
   const int64_t n_queries = (int64_t)batch * n_qrows;
   const fp8kv::DecodeWorkspace ws = workspace_view(workspace, n_queries, n_q_heads, pool->head_dim, max_splits);
   const fp8kv::DecodeShape shape{batch, n_qrows, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, window};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? n_qrows : 0, s);
-  if (e != hipSuccess) return FP8KV_ERR_HIP;
-  if (app) return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), batch, n_q_heads, ws, geo.n_split, *app, out, s));
-  if (!out) return FP8KV_OK;
-  return from_hip(fp8kv::launch_decode_merge(n_queries * n_q_heads, pool->head_dim, ws, geo.n_split, out, s));
+  return launch_decode(pool, q, shape, sm_scale, geo, ws, out, app, stream);
 }
 
 }  // namespace
@@ -360,7 +390,7 @@ fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q,
   if (n_tokens <= 0 || n_prefix < 0) return FP8KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
   if (!supported_group(n_q_heads, pool->n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
-  if (is_nan(sm_scale)) return FP8KV_ERR_INVALID_ARG;
+  if (!valid_softmax_scale(sm_scale)) return FP8KV_ERR_INVALID_ARG;
   if (n_prefix > 0) {
     if (!prefix_rows) return FP8KV_ERR_INVALID_ARG;
     if (!ws_k || !ws_v || ws_capacity_rows < n_prefix) return FP8KV_ERR_WORKSPACE;

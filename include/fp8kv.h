@@ -34,6 +34,8 @@
  *    launched and nothing is written.  Device-resident contents (row indices in
  *    tables and slot lists, sequence lengths, finiteness of inputs) are
  *    preconditions: an out-of-range row index is undefined behaviour.
+ *  - sm_scale (the softmax scale of the attention calls) must be finite and
+ *    greater than zero; anything else returns FP8KV_ERR_INVALID_ARG.
  *  - Functions are stateless apart from a per-device cache of the compute-unit
  *    count; they are thread-safe and may run concurrently on different streams
  *    as long as their output buffers do not overlap.
@@ -225,7 +227,8 @@ fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer *pool, const uint16_t *q
  * max_splits) by log-sum-exp and writes bf16 out[n_queries][n_q_heads][head_dim].
  * The split count comes from the workspace header that stage 1 wrote; it is
  * clamped to the workspace's split capacity, so a workspace no stage 1 wrote
- * gives meaningless output but no access outside the workspace.
+ * gives meaningless output but no access outside the workspace (a header
+ * holding 0 or less gives all-zero output).
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim), ALIGNMENT, WORKSPACE, HIP.
  */
 fp8kv_status fp8kv_decode_merge(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits,

@@ -111,6 +111,11 @@ def test_decode_validation(lib):
     assert _decode(lib, p, tstride=500) == INVALID                   # table row shorter than max_seq_len
     assert _decode(lib, p, maxlen=-1) == INVALID
     assert _decode(lib, p, sm=float("nan")) == INVALID
+    for bad in (0.0, -0.0, -0.088, float("inf"), float("-inf")):    # softmax scale finite and > 0
+        assert _decode(lib, p, sm=bad) == INVALID, bad
+        assert _append(lib, p, sm=bad) == INVALID, bad
+        assert _rows(lib, p, nq=3, sm=bad) == INVALID, bad
+    assert lib.fp8kv_decode_stage1(ctypes.byref(p), A, 1, 32, A, 1024, A, 1000, 0.0, 0, A, 1 << 30, None) == INVALID
     assert _decode(lib, p, q=A + 2) == ALIGN
     assert _decode(lib, p, out=A + 8) == ALIGN
     assert _decode(lib, p, table=A + 2) == ALIGN
@@ -165,8 +170,8 @@ def _append(lib, p, **kw):
     wsb = lib.fp8kv_decode_workspace_bytes(1, 32, p.head_dim, 0)
     return lib.fp8kv_decode_attn_append(ctypes.byref(p), kw.get("q", A), 1, kw.get("hq", 32), kw.get("kn", A),
                                         kw.get("vn", 2 * A), kw.get("nstride", 512), kw.get("slots", A), A, 1024, A,
-                                        kw.get("maxlen", 1000), 0.088, 0, A, kw.get("wsb", wsb), kw.get("out", A),
-                                        None)
+                                        kw.get("maxlen", 1000), kw.get("sm", 0.088), 0, A, kw.get("wsb", wsb),
+                                        kw.get("out", A), None)
 
 
 def _append_window(lib, p, window, **kw):
@@ -245,6 +250,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, p, wsv=A + 2) == ALIGN
     assert _prefill(lib, p, kc=A + 4) == ALIGN
     assert _prefill(lib, p, sm=float("nan")) == INVALID
+    for bad in (0.0, -0.0, -1.0, float("inf"), float("-inf")):
+        assert _prefill(lib, p, sm=bad) == INVALID, bad
     assert _prefill(lib, _pool(head_dim=256, code_row_stride=1024)) == UNSUPPORTED  # prefill runs at D = 128
 
 

@@ -45,6 +45,8 @@ def test_layer_32k_all_split_caps():
     ref_pools = oracle_pool(case)
     kc, vc, ks, vs = pool_arrays(pool)
     assert_bits_equal(kc, ref_pools[0], "K codes")
+    assert_bits_equal(vc, ref_pools[1], "V codes")
+    assert_bits_equal(ks, ref_pools[2], "K scales")
     assert_bits_equal(vs, ref_pools[3], "V scales")
     ref = _oracle_decode(case, ref_pools)
     outs = {}
@@ -320,3 +322,77 @@ def test_out_of_range_padding_entries_are_clamped():
     got = run_decode(pool, case, table=bad)
     assert torch.equal(got.view(torch.int16), want.view(torch.int16))
     assert_close(bf16_to_f64(got), _oracle_decode(case), "garbage padding")
+
+
+@pytest.mark.parametrize("D_,fmt", [(128, "e4m3"), (256, "e4m3"), (128, "int8")])
+def test_every_code_at_every_channel_through_the_k_path(D_, fmt):
+    """Every finite code at every channel of a key, read through the decode K
+    orientation (FreeToken PR #897, "Regression and CUDA isolation": every
+    finite value must survive both the K and the V orientation).
+
+    Request b tests one (code c, channel d) pair: its 32 keys are an all-zero
+    row (score 0, value 0) except key t_b = (code index + d) % 32, whose K row
+    holds c at channel d and zeros elsewhere, with a K scale chosen so that
+    q . khat * sm_scale = +3 (q = +-1 at channel d, following the code's sign),
+    and whose V row is 1.0 everywhere.  Every output element is then
+    e^3 / (e^3 + 31) = 0.393 for a nonzero code and 1/32 for a zero code; a
+    code decoded as any other value moves the score by at least 1/16 of 3 and
+    the output by at least 0.04.  Compared with the oracle at 1 % relative."""
+    say(f"decode: every finite code at every channel through the K path, D={D_}, {fmt}")
+    Hq, Hkv, L = 8, 1, 32
+    table_v = oracle.code_values(fmt)
+    codes = np.array([c for c in range(256) if np.isfinite(table_v[c])], np.uint8)
+    B = codes.size * D_
+    assert B <= 65535
+    ci, d = np.divmod(np.arange(B), D_)
+    c = codes[ci]
+    val = table_v[c]
+    sm = np.float32(wl.softmax_scale(D_))
+    # K scale: |decode(c)| * s * sm ~= 3 (s = 1 for a zero code)
+    mag = np.where(val != 0, np.abs(val), 1.0).astype(np.float32)
+    s = np.where(val != 0, np.float32(3.0) / (mag * sm), np.float32(1.0)).astype(np.float32)
+    R = B + 1  # row 0 is the all-zero row; request b's key is row b + 1
+    kc = np.zeros((R, Hkv, D_), np.uint8)
+    kc[np.arange(B) + 1, 0, d] = c
+    vc = np.zeros((R, Hkv, D_), np.uint8)
+    one = 0x38 if fmt == "e4m3" else 1
+    vc[1:] = one
+    ks = np.ones((R, Hkv), np.float32)
+    ks[1:, 0] = s
+    vs = np.ones((R, Hkv), np.float32)
+    t = (ci + d) % L
+    table = np.zeros((B, L), np.int32)
+    table[np.arange(B), t] = np.arange(B) + 1
+    lens = np.full(B, L, np.int32)
+    qf = np.zeros((B, Hq, D_), np.float32)
+    qf[np.arange(B), :, d] = np.where(val < 0, -1.0, 1.0)[:, None]
+    q = wl.bf16_bits(qf)
+
+    pool = fk.Fp8KvPool(R, Hkv, device=DEV, head_dim=D_, code_format=fmt)
+    pool.k_codes.copy_(to_dev(kc))
+    pool.v_codes.copy_(to_dev(vc))
+    pool.k_scales.copy_(to_dev(ks))
+    pool.v_scales.copy_(to_dev(vs))
+    out = fk.fp8kv_decode_attn(pool, to_dev_bf16(q), to_dev(table), to_dev(lens), L, float(sm), max_splits=1)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(out)
+    ref = oracle.decode_attention(q, kc, vc, ks, vs, table, lens, sm, Hkv, fmt=fmt)
+    assert np.all(np.isfinite(got))
+    rel = np.abs(got - ref) / np.abs(ref)
+    worst = np.unravel_index(np.argmax(rel), rel.shape)
+    say(f"  worst relative error {rel.max():.3e} at code 0x{codes[worst[0] // D_]:02x}, channel {worst[0] % D_}")
+    assert rel.max() <= 1e-2
+    expect = np.where(val != 0, np.exp(3.0) / (np.exp(3.0) + 31.0), 1.0 / 32.0)
+    assert np.abs(ref[:, 0, 0] - expect).max() <= 1e-5  # the construction itself
+
+
+def test_merge_of_a_workspace_no_stage1_wrote_gives_zeros():
+    """A zero-filled workspace (split count 0 in its header) merges to zeros and
+    reads nothing outside the workspace."""
+    say("decode merge over a zero-filled workspace")
+    for D_ in (128, 256):
+        ws = torch.zeros(fk.fp8kv_decode_workspace_bytes(2, 32, D_, 16), dtype=torch.uint8, device=DEV)
+        out = torch.full((2, 32, D_), 7.0, dtype=torch.bfloat16, device=DEV)
+        fk.fp8kv_decode_merge(ws, 2, 32, max_splits=16, out=out, head_dim=D_)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out.float()).item() == 0

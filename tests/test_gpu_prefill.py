@@ -42,10 +42,13 @@ def _run(case, layout="separate", q_idx=None, check_ws=True, fmt="e4m3"):
         assert_bits_equal(ws_v[:P].view(torch.int16).cpu().numpy().view(np.uint16), ows_v, "ws_v")
     # the chunk's own rows landed in the pool bit-exactly
     ck, cs = oracle.quantize_rows(case.k_cur, fmt)
-    kc_dev, _ = pool.codes()
-    ks_dev, _ = pool.scales()
+    cv, cvs = oracle.quantize_rows(case.v_cur, fmt)
+    kc_dev, vc_dev = pool.codes()
+    ks_dev, vs_dev = pool.scales()
     assert_bits_equal(kc_dev.cpu().numpy()[case.chunk_slots], ck, "chunk K codes")
     assert_bits_equal(ks_dev.cpu().numpy()[case.chunk_slots], cs, "chunk K scales")
+    assert_bits_equal(vc_dev.cpu().numpy()[case.chunk_slots], cv, "chunk V codes")
+    assert_bits_equal(vs_dev.cpu().numpy()[case.chunk_slots], cvs, "chunk V scales")
     idx = np.arange(T, dtype=np.int32) if q_idx is None else np.asarray(q_idx, np.int32)
     ref = oracle.prefill_attention(case.q, ows_k, ows_v, case.k_cur, case.v_cur, case.sm_scale, q_idx=idx)
     got = bf16_to_f64(out)[idx]
@@ -69,14 +72,30 @@ def test_small_prefill_interleaved_pool():
     assert_close(got, ref, "interleaved")
 
 
+def _sampled_tokens(T, stride, offset, bands):
+    """Every `stride`-th chunk token from `offset` (a stride co-prime to 32 meets
+    every token offset inside the kernel's 32-token workgroups at G = 8, so every
+    wave and both of its 16-row blocks), plus whole 32-token workgroup bands and
+    the last 8 tokens."""
+    parts = [np.arange(offset, T, stride), np.arange(T - 8, T)]
+    parts += [np.arange(b, b + 32) for b in bands]
+    return np.unique(np.concatenate(parts)).astype(np.int32)
+
+
+def test_sampled_tokens_cover_every_workgroup_offset():
+    idx = _sampled_tokens(8192, 61, 0, (4096,))
+    assert set(np.arange(32)) <= set((idx[idx < 4096] % 32).tolist())
+
+
 def test_chunked_prefill_8k_prefix_8k_chunk():
     """8,192 historical FP8 rows + 8,192 bf16 chunk tokens, 32 q / 4 KV heads:
-    workspace bit-exact for all rows, attention checked on sampled query rows
-    (every 256th plus the last 8) against the fp64 oracle."""
+    workspace and chunk rows bit-exact for all rows, attention checked against
+    the fp64 oracle on every 61st query token, two whole 32-token workgroup
+    bands and the last 8 tokens."""
     say("prefill 8K prefix + 8K chunk (sampled rows vs oracle)")
     case = wl.chunked_prefill(0)
     T = case.q.shape[0]
-    idx = np.unique(np.concatenate([np.arange(0, T, 256), np.arange(T - 8, T)]))
+    idx = _sampled_tokens(T, 61, 0, (4096, 7904))
     got, ref = _run(case, q_idx=idx)
     assert_close(got, ref, "8K+8K sampled")
 
@@ -93,7 +112,7 @@ def test_chunked_prefill_8k_prefix_8k_chunk_int8_pool():
     say("prefill 8K prefix + 8K chunk over an INT8 pool (sampled rows vs oracle)")
     case = wl.chunked_prefill(2)
     T = case.q.shape[0]
-    idx = np.unique(np.concatenate([np.arange(0, T, 512), np.arange(T - 4, T)]))
+    idx = _sampled_tokens(T, 61, 29, (2048,))
     got, ref = _run(case, q_idx=idx, fmt="int8", layout="interleaved")
     assert_close(got, ref, "int8 8K+8K sampled")
 
