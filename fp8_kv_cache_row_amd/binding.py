@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
     L.fp8kv_decode_attn_append.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, f32, i32, vp, sz,
                                            vp, vp]
     L.fp8kv_decode_attn_append.restype = ctypes.c_int
+    L.fp8kv_decode_attn_append_noalloc.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, f32, i32,
+                                                   vp, vp]
+    L.fp8kv_decode_attn_append_noalloc.restype = ctypes.c_int
     L.fp8kv_decode_attn_append_window.argtypes = [P, vp, i32, i32, vp, vp, i64, vp, vp, i64, vp, i32, i32, f32, i32,
                                                   vp, sz, vp, vp]
     L.fp8kv_decode_attn_append_window.restype = ctypes.c_int
@@ -363,6 +366,44 @@ def fp8kv_decode_attn_append(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tens
                                          a["max_seq_len"], a["sm_scale"], a["max_splits"], a["ws"], a["ws_bytes"],
                                          _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_decode_attn_append")
+    return out
+
+
+def fp8kv_decode_attn_append_noalloc(pool: Fp8KvPool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                     new_slots: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                                     max_seq_len: int, sm_scale: float, max_splits: int = 0,
+                                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp8kv_decode_attn_append without a workspace: the split partials live in the
+    library's fixed per-device array (calls on one device must not overlap)."""
+    _dev_check(q, "q", torch.bfloat16)
+    _dev_check(row_table, "row_table", torch.int32)
+    _dev_check(seq_lens, "seq_lens", torch.int32)
+    D = pool.head_dim
+    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B][Hq][{D}] bf16 tensor")
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if row_table.dim() != 2 or row_table.shape[0] != B or row_table.stride(1) != 1:
+        raise ValueError("row_table must be [B][stride] with unit inner stride")
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    table_stride = row_table.stride(0) if B > 1 else max(int(row_table.shape[1]), 1)
+    _dev_check(k_new, "k_new", torch.bfloat16)
+    _dev_check(v_new, "v_new", torch.bfloat16)
+    shape = (B, pool.n_kv_heads, D)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new/v_new must be {list(shape)}, got {tuple(k_new.shape)} / {tuple(v_new.shape)}")
+    if not k_new.is_contiguous() or not v_new.is_contiguous():
+        raise ValueError("k_new and v_new must be contiguous")
+    _dev_check(new_slots, "new_slots", torch.int32)
+    if new_slots.numel() != B:
+        raise ValueError("new_slots must have B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().fp8kv_decode_attn_append_noalloc(ctypes.byref(pool.layer), _ptr(_bits(q)), B, Hq, _ptr(_bits(k_new)),
+                                                 _ptr(_bits(v_new)), pool.n_kv_heads * D, _ptr(new_slots),
+                                                 _ptr(row_table), table_stride, _ptr(seq_lens), int(max_seq_len),
+                                                 float(sm_scale), int(max_splits), _ptr(_bits(out)), _stream(stream))
+    _check(st, "fp8kv_decode_attn_append_noalloc")
     return out
 
 

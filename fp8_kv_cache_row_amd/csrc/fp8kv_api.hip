@@ -62,6 +62,7 @@ struct DeviceInfo {
   bool known = false;
   bool gfx950 = false;
   int n_cu = 0;
+  void* scratch = nullptr;  // device address of `scratch` on this device, once looked up
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
@@ -247,6 +248,26 @@ fp8kv_status run_decode(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t
   return launch_decode(pool, q, shape, sm_scale, geo, ws, out, app, stream);
 }
 
+// The allocation-free decode step keeps its split partials in this array, one
+// copy per device, instead of a caller's workspace.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[FP8KV_NOALLOC_SCRATCH_BYTES];
+
+fp8kv_status device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8KV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& info = g_dev[dev];
+  if (!info.scratch) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8KV_ERR_HIP;
+    info.scratch = p;
+  }
+  *ptr = info.scratch;
+  return FP8KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,6 +398,42 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer* pool, const uint16
   return fp8kv_decode_attn_append_window(pool, q, batch, n_q_heads, k_new, v_new, new_token_stride, new_slots,
                                          row_table, table_stride, seq_lens, max_seq_len, 0, sm_scale, max_splits,
                                          workspace, workspace_bytes, out, stream);
+}
+
+fp8kv_status fp8kv_decode_attn_append_noalloc(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                                              int32_t n_q_heads, const uint16_t* k_new, const uint16_t* v_new,
+                                              int64_t new_token_stride, const int32_t* new_slots,
+                                              const int32_t* row_table, int64_t table_stride,
+                                              const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                              int32_t max_splits, uint16_t* out, void* stream) {
+  fp8kv_status st = check_decode_shape(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len,
+                                       0, sm_scale, max_splits);
+  if (st != FP8KV_OK) return st;
+  if (!out || !k_new || !v_new || !new_slots || max_seq_len < 1) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(new_slots, 4)) return FP8KV_ERR_ALIGNMENT;
+  if (new_token_stride < (int64_t)pool->n_kv_heads * pool->head_dim) return FP8KV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || (new_token_stride % 8) != 0)
+    return FP8KV_ERR_ALIGNMENT;
+  int n_cu = 0;
+  st = current_device(&n_cu);
+  if (st != FP8KV_OK) return st;
+  // The partials are laid out with a split stride of exactly the split count
+  // this launch uses, so the array holds as many (request, head) rows as fit.
+  const fp8kv::DecodeGeometry geo =
+      choose_geometry(batch, pool->n_kv_heads, pool->head_dim, n_q_heads / pool->n_kv_heads, 1, max_seq_len, 0,
+                      max_splits, n_cu);
+  const size_t need = partial_bytes(batch, n_q_heads, pool->head_dim, geo.n_split);
+  if (need > (size_t)FP8KV_NOALLOC_SCRATCH_BYTES) return FP8KV_ERR_WORKSPACE;
+  void* base = nullptr;
+  st = device_scratch(&base);
+  if (st != FP8KV_OK) return st;
+  char* b = static_cast<char*>(base);
+  float* part_o = reinterpret_cast<float*>(b + fp8kv::kDecodeHeaderBytes);
+  const fp8kv::DecodeWorkspace ws{reinterpret_cast<int32_t*>(b), part_o,
+                                  part_o + (size_t)batch * n_q_heads * geo.n_split * pool->head_dim, geo.n_split};
+  const fp8kv::DecodeShape shape{batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0};
+  const fp8kv::AppendArgs app{q, k_new, v_new, new_token_stride, new_slots, sm_scale, 1, 0};
+  return launch_decode(pool, q, shape, sm_scale, geo, ws, out, &app, stream);
 }
 
 fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q, const uint16_t* k_cur,

@@ -18,6 +18,7 @@
  * (several query rows, sliding window); fp8kv_decode_attn_append,
  * fp8kv_decode_attn_append_window and fp8kv_decode_attn_rows_append (a decode
  * step with its new tokens quantized on write in the same call);
+ * fp8kv_decode_attn_append_noalloc (the same step without a caller workspace);
  * fp8kv_prefill_attn (reconstruct + causal chunk attention);
  * fp8kv_decode_workspace_bytes and fp8kv_status_string.
  *
@@ -65,6 +66,9 @@ extern "C" {
 /* Upper bound on requests per decode call (times ceil(G * n_qrows / 32) for
  * several query rows): they share one launch dimension. */
 #define FP8KV_MAX_DECODE_GROUPS 65535
+/* Bytes of the per-device array that holds the split partials of
+ * fp8kv_decode_attn_append_noalloc (32 MiB). */
+#define FP8KV_NOALLOC_SCRATCH_BYTES 33554432
 /* Code formats of a pool (fp8kv_pool_layer.code_format). */
 #define FP8KV_CODE_E4M3 0 /* OCP E4M3FN, scale amax / 448 */
 #define FP8KV_CODE_INT8 1 /* symmetric INT8, scale amax / 127 */
@@ -303,6 +307,38 @@ fp8kv_status fp8kv_decode_attn_append(const fp8kv_pool_layer *pool, const uint16
                                       int64_t table_stride, const int32_t *seq_lens, int32_t max_seq_len,
                                       float sm_scale, int32_t max_splits, void *workspace,
                                       size_t workspace_bytes, uint16_t *out, void *stream);
+
+/*
+ * fp8kv_decode_attn_append_noalloc -- fp8kv_decode_attn_append for callers
+ * that cannot allocate device memory or pass a workspace (code under HIP
+ * graph capture that must not allocate, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, the same kernels and the same
+ * results bit for bit, with the split partials kept in a fixed array of
+ * FP8KV_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a caller
+ * workspace.  The call allocates nothing and frees nothing.
+ *
+ * The array exists once per GPU the library runs on and is held until the
+ * process ends.  Every call on a GPU uses that GPU's array, which keeps the
+ * previous call's contents (nothing in it needs to start at zero: stage 1
+ * writes every partial the merge reads).  Calls that overlap in time on one
+ * GPU -- on different streams, or from different threads -- race on the
+ * array and must be serialized by the caller.
+ *
+ * The partials need 256 + batch * n_q_heads * S * (head_dim + 1) * 4 bytes,
+ * with S the split count the call chooses (at most max_splits, 0 = chosen
+ * from the device; 64 for one 32K-context request on MI355X); a call that
+ * needs more than FP8KV_NOALLOC_SCRATCH_BYTES returns FP8KV_ERR_WORKSPACE
+ * before launching anything.
+ *
+ * Arguments and the other errors are those of fp8kv_decode_attn_append
+ * without `workspace` / `workspace_bytes`.
+ */
+fp8kv_status fp8kv_decode_attn_append_noalloc(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                                              int32_t n_q_heads, const uint16_t *k_new, const uint16_t *v_new,
+                                              int64_t new_token_stride, const int32_t *new_slots,
+                                              const int32_t *row_table, int64_t table_stride,
+                                              const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                                              int32_t max_splits, uint16_t *out, void *stream);
 
 /*
  * fp8kv_decode_attn_append_window -- fp8kv_decode_attn_append with a sliding
