@@ -6,15 +6,26 @@ head dim 128, 32,768 cached rows scattered over a 33,059-row page-size-1 FP8
 pool (seeded permutation), K ~ N(0,1) with 4 x8 outlier channels per head,
 V ~ 0.5 N(0,1), bf16 before quantization.  One step = one decode layer:
 quantize the new token's K/V row into the pool (its slot is the last table
-entry) and attend over all 32,768 positions.  By default the step is the
-fused call fp8kv_decode_attn_append (split-K stage 1 over the cached rows, then
-a merge that also quantizes, stores and adds the new token: two kernels); the
+entry) and attend over all 32,768 positions, as the fused call
+fp8kv_decode_attn_append (split-K stage 1 over the cached rows, then a merge
+that also quantizes, stores and adds the new token: two kernels); the
 three-call form (fp8kv_quantize_rows, then stage 1 + merge) is timed beside it.
 
-Cold HBM: the step rotates over `--pools` identical copies of the layer's pool
-(12 x 34.9 MB = 419 MB, more than the 256 MB Infinity Cache), as a multi-layer
-model does, so each step reads its KV rows from HBM.  Steps are captured in a
-HIP graph and replayed, so host launch overhead is not timed.
+Protocol: `--rounds` seeded rounds (workload seed r for round r), each with
+its own pool; inside a round the timed items run in a seeded shuffled order,
+each as `--warmup` untimed steps followed by exactly `--steps` timed steps
+(one HIP graph each, HIP events on the graph's stream).  Cold HBM: the steps
+rotate over `--pools` identical copies of the layer's pool (12 x 34.9 MB =
+419 MB, more than the 256 MB Infinity Cache), as the layers of a model do;
+the warm column replays the same step over one pool.  `value` and
+`ms_per_step` are the median over rounds; every sample is kept.
+
+Also timed by default: the 48-layer step at 40,000 context (48 distinct
+40,290-row pools, 2 GB); the 8K FP8 prefix + 8K chunk prefill with a BF16
+prefix beside it; the decode variants (head dim 256, several query rows, a
+sliding window, INT8, a 16-request batch); two floors (a plain 34.6 MB cold
+read by a library reduction, and a dependent kernel launch after stage 1);
+and the CPU oracle on the host cores.
 
 Prints one JSON line.  `value` is the effective KV bandwidth of the whole step
 (algorithmic KV bytes / step time); `roofline` is for the dominant kernel
@@ -27,6 +38,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -38,27 +50,35 @@ METRIC = "FP8-KV GQA decode attention: us/layer and KV HBM GB/s (% of peak) at 3
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 KV_BYTES_PER_ROW_HEAD = 2 * (128 + 4)   # K and V: 128 code bytes + one fp32 scale each
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stage1_32k_traffic.json")
+GUARD_FILE = os.path.join(ROOT, "tests", "golden", "decode_32k_step_seed0.txt")
+LAYOUTS = ["separate", "interleaved", "interleaved64", "interleaved128", "split"]
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=240, help="timed decode steps (layers)")
-    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--steps", type=int, default=240, help="timed decode steps (layers) per round and item")
+    ap.add_argument("--warmup", type=int, default=24, help="untimed steps before each timed run")
+    ap.add_argument("--rounds", type=int, default=5, help="seeded rounds of the headline workload")
     ap.add_argument("--pools", type=int, default=12, help="pool copies rotated per step (cold HBM)")
     ap.add_argument("--max-splits", type=int, default=0)
-    ap.add_argument("--layout", default="interleaved", choices=["separate", "interleaved"],
+    ap.add_argument("--layout", default="interleaved", choices=LAYOUTS,
                     help="pool layout: interleaved 1,056-byte row records (K codes, V codes, K scales, V scales "
-                         "of all KV heads) or four separate arrays")
+                         "of all KV heads), the same padded to 64 / 128 bytes, code records + scale records "
+                         "(split), or four separate arrays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) instead")
+    ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) for everything")
+    ap.add_argument("--no-warm-column", action="store_true",
+                    help="skip the warm (one-pool) column, so a kernel trace holds only cold stage-1 dispatches")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8K-prefix + 8K-chunk prefill timing")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the head-dim-256, multi-row, sliding-window and INT8 decode timings")
-    ap.add_argument("--model-step", action="store_true",
-                    help="also time the 48-layer step at 40,000 context (2 GB of pools; it runs the headline's "
-                         "stage-1 kernel, so profiles of the headline are taken without it)")
+                    help="skip the head-dim-256, multi-row, sliding-window, INT8 and batched decode timings")
+    ap.add_argument("--no-model-step", action="store_true",
+                    help="skip the 48-layer step at 40,000 context (it runs the headline's stage-1 kernel, so "
+                         "kernel traces of the headline are taken without it)")
+    ap.add_argument("--model-step-steps", type=int, default=8, help="timed 48-layer steps")
+    ap.add_argument("--no-floors", action="store_true", help="skip the read-floor and dependent-launch timings")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run plain 64 MiB device copies (a known-size kernel for HBM byte counters)")
     return ap.parse_args()
@@ -121,20 +141,31 @@ def prefill_timing(fk, wl, dev, reps: int = 5):
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
+    bws_k, bws_v = bf(case.prefix_k), bf(case.prefix_v)  # the prefix rows as a BF16 KV cache holds them
+
     def attn(i):
         fk.fp8kv_prefill_attn(pool, q, kc, vc, rows, ws_k, ws_v, case.sm_scale, out=out, stream=stream)
+
+    def attn_bf16(i):
+        fk.fp8kv_prefill_attn_workspace(q, kc, vc, bws_k, bws_v, case.sm_scale, out=out, stream=stream)
 
     def quant(i):
         fk.fp8kv_quantize_rows(pool, kc, vc, slots, stream=stream)
 
     ms, _ = time_graph(stream, capture_graph(stream, attn, reps), reps, reps, 1)
+    bms, _ = time_graph(stream, capture_graph(stream, attn_bf16, reps), reps, reps, 1)
     qms, _ = time_graph(stream, capture_graph(stream, quant, 16), 16, 64, 16)
     pairs = T * P + T * (T + 1) // 2            # causal (query, key) pairs per head
     flop = 4.0 * 128 * pairs * Hq               # QK^T and PV, 2 flop per MAC
     tflops = flop / (ms * 1e-3) / 1e12
     qbytes = T * Hkv * 2 * (128 * 2 + 128 + 4)  # bf16 rows in, codes + scales out
     return {"workload": "8,192 FP8 prefix rows + 8,192-token bf16 chunk, causal, 32 q / 4 KV heads",
-            "reconstruct_plus_attention_ms": round(ms, 4), "attention_flop": flop,
+            "reconstruct_plus_attention_ms": round(ms, 4),
+            "bf16_prefix_attention_ms": round(bms, 4),
+            "bf16_prefix_note": "the same attention kernel over the prefix's bf16 rows (a BF16 KV pool, no "
+                                "reconstruction): fp8kv_prefill_attn_workspace",
+            "fp8_over_bf16": round(ms / bms, 4),
+            "attention_flop": flop,
             "tflops": round(tflops, 2), "mfma_bf16_frac_of_2500": round(tflops / 2500.0, 4),
             "quantize_chunk_us": round(qms * 1e3, 3),
             "quantize_chunk_gbps": round(qbytes / (qms * 1e-3) / 1e9, 1)}
@@ -197,8 +228,7 @@ def variants_timing(fk, wl, dev, args, bf):
     rows per request (and the 8-row step with its new tokens written in the
     same call), the INT8 KV format (fused append step and stage 1
     alone), the 16-request GQA-4 batch (fused step and stage 1 alone), an odd
-    4,095-key sliding window (query rows call, and the fused step), and with
-    --model-step the 48-layer step at 40,000 context."""
+    4,095-key sliding window (query rows call, and the fused step)."""
     import numpy as np
     import torch
     stream = torch.cuda.Stream(device=dev)
@@ -300,8 +330,6 @@ def variants_timing(fk, wl, dev, args, bf):
                            "one decode step with quantize-on-write"})
     run("batched16_stage1", c, stage1_body, kv, copies=min(n, 4))
     del c
-    if args.model_step:
-        res["model_step_48x40k"] = model_step_timing(fk, wl, dev, args, bf, stream)
     c = wl.layer_decode(0, with_new_token=False)
     W = 4095
     run("window4095", c, rows_body(W), W * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD,
@@ -318,7 +346,8 @@ def model_step_timing(fk, wl, dev, args, bf, stream):
     """The 48-layer step at 40,000 context: one fused call per layer over 48
     distinct 40,290-row pools (2 GB, larger than the Infinity Cache, so every
     layer reads its rows from HBM); one layer's draws are copied into all 48
-    pools, which does not change the timing."""
+    pools, which does not change the timing.  One warm-up step, then exactly
+    --model-step-steps timed steps (48 calls each) in one graph."""
     import torch
     table = wl.model_step_table(0)
     c = wl.model_step_layer(0, table)
@@ -329,16 +358,21 @@ def model_step_timing(fk, wl, dev, args, bf, stream):
     slot = torch.from_numpy(c.table[:, -1].copy()).to(dev)
     ws = fk.decode_workspace(1, c.n_q_heads, device=dev)
     out = torch.empty_like(q)
-    g = capture_graph(stream, lambda i: fk.fp8kv_decode_attn_append(pools[i], q, nk, nv, slot, t, sl, c.max_seq_len,
-                                                                    c.sm_scale, workspace=ws, out=out, stream=stream),
-                      layers)
-    ms, _ = time_graph(stream, g, layers, layers * 8, layers)
+    K = max(1, args.model_step_steps)
+    ms = time_exact(stream, lambda i: fk.fp8kv_decode_attn_append(pools[i % layers], q, nk, nv, slot, t, sl,
+                                                                  c.max_seq_len, c.sm_scale, workspace=ws, out=out,
+                                                                  stream=stream),
+                    layers * K, layers)
+    del pools
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     kv = layers * c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+    step_s = ms * layers * 1e-3
     return {"workload": "48-layer decode step at 40,000 context (one token: quantize-on-write + attention per "
-                        "layer), 40,290-row pools, 2.04 GB",
-            "us_per_step": round(ms * layers * 1e3, 2), "us_per_layer": round(ms * 1e3, 3),
-            "kv_bytes": kv, "kv_gbps": round(kv / (ms * layers * 1e-3) / 1e9, 1),
-            "hbm_frac": round(kv / (ms * layers * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                        "layer), 48 x 40,290-row pools, 2.04 GB",
+            "steps": K, "us_per_step": round(step_s * 1e6, 2), "us_per_layer": round(ms * 1e3, 3),
+            "kv_bytes": kv, "kv_gbps": round(kv / step_s / 1e9, 1),
+            "hbm_frac": round(kv / step_s / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def calibration_copies(dev, mib: int = 64, n: int = 4):
@@ -352,44 +386,206 @@ def calibration_copies(dev, mib: int = 64, n: int = 4):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(case, budget_s: float):
+def cpu_baseline(case, budget_s: float, with_model_step: bool = True):
     """The oracle (as it stands) on the host: quantize the new K/V row + fp64
     decode attention over all 32,768 rows, repeated until the time budget, on
-    all host threads and then on one."""
+    all host threads and then on one; and, for the 48-layer 40K step, the same
+    per layer over 40,000 rows (per-step figures are 48 layers' worth)."""
     import oracle
-    kc, ks = oracle.quantize_rows(case.k_rows)
-    vc, vs = oracle.quantize_rows(case.v_rows)
-    row = int(case.table[0, -1])
-    kv = case.max_seq_len * case.n_kv_heads * KV_BYTES_PER_ROW_HEAD
 
-    def timed(budget):
+    def timed_step(c, budget):
+        kc, ks = oracle.quantize_rows(c.k_rows)
+        vc, vs = oracle.quantize_rows(c.v_rows)
+        row = int(c.table[0, -1])
         reps, t0 = 0, time.perf_counter()
         while True:
-            nkc, nks = oracle.quantize_rows(case.new_k)
-            nvc, nvs = oracle.quantize_rows(case.new_v)
+            nkc, nks = oracle.quantize_rows(c.new_k)
+            nvc, nvs = oracle.quantize_rows(c.new_v)
             kc[row], ks[row], vc[row], vs[row] = nkc[0], nks[0], nvc[0], nvs[0]
-            oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale,
-                                    case.n_kv_heads)
+            oracle.decode_attention(c.q, kc, vc, ks, vs, c.table, c.seq_lens, c.sm_scale, c.n_kv_heads)
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget:
                 return reps, el
 
+    kv = case.max_seq_len * case.n_kv_heads * KV_BYTES_PER_ROW_HEAD
     cores = oracle.num_threads()
-    reps, el = timed(budget_s)
+    reps, el = timed_step(case, budget_s)
     oracle.set_num_threads(1)
     try:
-        reps1, el1 = timed(budget_s / 2)
+        reps1, el1 = timed_step(case, budget_s / 2)
     finally:
         oracle.set_num_threads(cores)
-    return {"value": round(kv * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"full 32K-context layer step (quantize new K/V row + fp64 decode attention, "
-                      f"32 q heads x 32,768 rows) repeated {reps} times in {el:.1f} s",
-            "us_per_layer": round(el / reps * 1e6, 1),
-            "single_core": {"value": round(kv * reps1 / el1 / 1e9, 3), "unit": "GB/s",
-                            "us_per_layer": round(el1 / reps1 * 1e6, 1),
-                            "sample": f"the same step repeated {reps1} times in {el1:.1f} s on 1 thread"}}
+    res = {"value": round(kv * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"full 32K-context layer step (quantize new K/V row + fp64 decode attention, "
+                     f"32 q heads x 32,768 rows) repeated {reps} times in {el:.1f} s",
+           "us_per_layer": round(el / reps * 1e6, 1),
+           "single_core": {"value": round(kv * reps1 / el1 / 1e9, 3), "unit": "GB/s",
+                           "us_per_layer": round(el1 / reps1 * 1e6, 1),
+                           "sample": f"the same step repeated {reps1} times in {el1:.1f} s on 1 thread"}}
+    if with_model_step:
+        from fp8_kv_cache_row_amd import workloads as wl
+        c = wl.model_step_layer(0, wl.model_step_table(0))
+        kv3 = c.max_seq_len * c.n_kv_heads * KV_BYTES_PER_ROW_HEAD
+        r3, e3 = timed_step(c, budget_s / 2)
+        res["model_step_48x40k"] = {
+            "value": round(kv3 * r3 / e3 / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "us_per_layer": round(e3 / r3 * 1e6, 1), "us_per_step": round(48 * e3 / r3 * 1e6, 1),
+            "sample": f"one 40,000-row layer of the 48-layer step (quantize new K/V row + fp64 decode attention) "
+                      f"repeated {r3} times in {e3:.1f} s; a step is 48 such layers"}
+    return res
+
+
+def time_exact(stream, body, steps, warmup, offset=0):
+    """ms per call of exactly `steps` calls body(offset + warmup + i), after
+    `warmup` untimed calls body(offset + i): one HIP graph each (captured after
+    an untimed eager pass), HIP events on the graph's stream."""
+    import torch
+    g_w = capture_graph(stream, lambda i: body(offset + i), warmup) if warmup > 0 else None
+    g_k = capture_graph(stream, lambda i: body(offset + warmup + i), steps)
+    torch.cuda.synchronize()
+    if g_w is not None:
+        g_w.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g_k.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g_w, g_k
+    return ms
+
+
+def load_guard():
+    """The oracle's output of the seed-0 fused step (tests/golden), [Hq][128] fp64."""
+    import numpy as np
+    rows = [list(map(float, line.split())) for line in open(GUARD_FILE) if line.strip() and not line.startswith("#")]
+    return np.array(rows, dtype=np.float64)
+
+
+def headline_round(fk, B, wl, dev, args, seed, stream, bf):
+    """One seeded round of the 32K-context layer: per-item ms (exact step counts)."""
+    import numpy as np
+    import torch
+    case = wl.layer_decode(seed)
+    L, Hq, Hkv = case.max_seq_len, case.n_q_heads, case.n_kv_heads
+    n_pools = 1 if args.warm else max(1, args.pools)
+    pools = rotated_pools(fk, case, args.layout, n_pools, dev, bf)
+    q = bf(case.q)
+    table = torch.from_numpy(case.table).to(dev)
+    lens = torch.from_numpy(case.seq_lens).to(dev)
+    new_k, new_v = bf(case.new_k), bf(case.new_v)
+    slot = torch.from_numpy(case.table[:, -1].copy()).to(dev)
+    ws = fk.decode_workspace(1, Hq, args.max_splits, dev)
+    out = torch.empty_like(q)
+    one = torch.zeros(1, device=dev)
+    torch.cuda.synchronize()
+    lib = B.load()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    wsb = ws.numel()
+
+    def chk(st, what):
+        if st:
+            raise B.Fp8KvError(st, what)
+
+    def quant(p):
+        chk(lib.fp8kv_quantize_rows(ctypes.byref(p.layer), new_k.data_ptr(), new_v.data_ptr(), Hkv * 128,
+                                    slot.data_ptr(), 1, sp), "fp8kv_quantize_rows")
+
+    def stage1(p):
+        chk(lib.fp8kv_decode_stage1(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L, lens.data_ptr(),
+                                    L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb, sp), "fp8kv_decode_stage1")
+
+    def stage1_valu(p):
+        chk(lib.fp8kv_decode_stage1_valu(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,
+                                         lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb, sp),
+            "fp8kv_decode_stage1_valu")
+
+    def merge():
+        chk(lib.fp8kv_decode_merge(1, Hq, 128, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp),
+            "fp8kv_decode_merge")
+
+    def decode(p):
+        chk(lib.fp8kv_decode_attn(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L, lens.data_ptr(),
+                                  L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp),
+            "fp8kv_decode_attn")
+
+    def append(p):
+        chk(lib.fp8kv_decode_attn_append(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, new_k.data_ptr(),
+                                         new_v.data_ptr(), Hkv * 128, slot.data_ptr(), table.data_ptr(), L,
+                                         lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb,
+                                         out.data_ptr(), sp), "fp8kv_decode_attn_append")
+
+    def tiny():
+        with torch.cuda.stream(stream):
+            one.add_(1.0)
+
+    P = lambda i: pools[i % n_pools]  # noqa: E731
+    items = {
+        "step": lambda i: append(P(i)),
+        "step_three_calls": lambda i: (quant(P(i)), decode(P(i))),
+        "stage1": lambda i: stage1(P(i)),
+        "stage1_valu": lambda i: stage1_valu(P(i)),
+        "merge": lambda i: merge(),
+        "quantize_new_row": lambda i: quant(P(i)),
+    }
+    if not args.warm and not args.no_warm_column:
+        items["step_warm"] = lambda i: append(pools[0])
+    if not args.no_floors and seed == 0:
+        items["stage1_then_tiny_kernel"] = lambda i: (stage1(P(i)), tiny())
+    order = list(items)
+    np.random.default_rng(1000 + seed).shuffle(order)
+    res = {}
+    for name in order:
+        res[name] = time_exact(stream, items[name], args.steps, args.warmup)
+    res["order"] = order
+
+    # correctness guard on the configuration just timed: the fused step (seed 0)
+    # against the stored oracle output, and against the two-call decode with
+    # another split count over the pool the step has just written into
+    append(pools[0])
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)[0]
+    ref2 = fk.fp8kv_decode_attn(pools[0], q, table, lens, L, case.sm_scale, max_splits=8)
+    torch.cuda.synchronize()
+    if not torch.allclose(out.float(), ref2.float(), atol=2e-2, rtol=0):
+        raise RuntimeError("bench guard: the fused step disagrees with fp8kv_decode_attn (split cap 8)")
+    if seed == 0 and os.path.exists(GUARD_FILE):
+        ref = load_guard()
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        mab = float(np.abs(got - ref).max())
+        res["guard"] = {"rel_l2": rel, "max_abs": mab}
+        if not (rel <= 5e-3 and mab <= 2e-2):
+            raise RuntimeError(f"bench guard: fused step vs the stored oracle output rel_l2={rel:.3e} max_abs={mab:.3e}")
+    del pools
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, case
+
+
+def read_floor(dev, stream, steps, warmup, n=12, nbytes=34603008):
+    """A plain cold read of 34,603,008 bytes by a library reduction: torch.sum
+    over the rows of an fp32 [33,792][256] tensor (one reduction per row inside
+    one workgroup, no cross-workgroup step), rotated over n distinct buffers."""
+    import torch
+    rows = nbytes // (256 * 4)
+    bufs = [torch.full((rows, 256), float(i + 1), dtype=torch.float32, device=dev) for i in range(n)]
+    outs = torch.empty((rows,), dtype=torch.float32, device=dev)
+
+    def body(i):
+        with torch.cuda.stream(stream):
+            torch.sum(bufs[i % n], dim=1, out=outs)
+
+    ms = time_exact(stream, body, steps, warmup)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"us": round(ms * 1e3, 3), "bytes": rows * 256 * 4, "gbps": round(rows * 256 * 4 / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(rows * 256 * 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "op": f"torch.sum(dim=1) of an fp32 [{rows}][256] tensor, {n} rotated buffers, graph replay"}
 
 
 def main():
@@ -398,6 +594,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); this "
               "path has no multi-GPU decomposition to time.", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.rounds < 1:
+        print("bench.py: --steps and --rounds must be >= 1, --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -411,115 +610,35 @@ def main():
     torch.cuda.set_device(dev)
     if args.calibration_copy:
         calibration_copies(dev)
-    case = wl.layer_decode(0)  # 32,768 of 33,059 rows, 32 q / 4 KV heads
-    L, Hq, Hkv = case.max_seq_len, case.n_q_heads, case.n_kv_heads
-    kv_bytes = L * Hkv * KV_BYTES_PER_ROW_HEAD
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    base = fk.Fp8KvPool(case.pool_rows, Hkv, layout=args.layout, device=dev)
-    fk.fp8kv_quantize_rows(base, bf(case.k_rows), bf(case.v_rows),
-                           torch.arange(case.pool_rows, dtype=torch.int32, device=dev))
-    n_pools = 1 if args.warm else max(1, args.pools)
-    pools = [base]
-    for _ in range(n_pools - 1):
-        p = fk.Fp8KvPool(case.pool_rows, Hkv, layout=args.layout, device=dev)
-        for dst, src in zip(p._buffers, base._buffers):
-            dst.copy_(src)
-        pools.append(p)
-    q = bf(case.q)
-    table = torch.from_numpy(case.table).to(dev)
-    lens = torch.from_numpy(case.seq_lens).to(dev)
-    new_k, new_v = bf(case.new_k), bf(case.new_v)
-    slot = torch.from_numpy(case.table[:, -1].copy()).to(dev)
-    ws = fk.decode_workspace(1, Hq, args.max_splits, dev)
-    out = torch.empty_like(q)
-    torch.cuda.synchronize()
-
-    lib = B.load()
     stream = torch.cuda.Stream(device=dev)
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    wsb = ws.numel()
-
-    def quant(p):
-        return lib.fp8kv_quantize_rows(ctypes.byref(p.layer), new_k.data_ptr(), new_v.data_ptr(), Hkv * 128,
-                                       slot.data_ptr(), 1, sp)
-
-    def stage1(p):
-        return lib.fp8kv_decode_stage1(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,
-                                       lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb, sp)
-
-    def merge():
-        return lib.fp8kv_decode_merge(1, Hq, 128, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp)
-
-    def decode(p):
-        return lib.fp8kv_decode_attn(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,
-                                     lens.data_ptr(), L, case.sm_scale, args.max_splits, ws.data_ptr(), wsb,
-                                     out.data_ptr(), sp)
-
-    def append(p):
-        return lib.fp8kv_decode_attn_append(ctypes.byref(p.layer), q.data_ptr(), 1, Hq, new_k.data_ptr(),
-                                            new_v.data_ptr(), Hkv * 128, slot.data_ptr(), table.data_ptr(), L,
-                                            lens.data_ptr(), L,
-                                            case.sm_scale, args.max_splits, ws.data_ptr(), wsb, out.data_ptr(), sp)
-
-    def step(i):
-        st = append(pools[i % n_pools])
-        if st:
-            raise B.Fp8KvError(st, "decode step")
-
-    def step_three_calls(i):
-        p = pools[i % n_pools]
-        st = quant(p) or decode(p)
-        if st:
-            raise B.Fp8KvError(st, "decode step (three calls)")
-
-    def capture(body, n):
-        return capture_graph(stream, body, n)
-
-    def timed(g, per_graph, total):
-        return time_graph(stream, g, per_graph, total, args.warmup)  # ms per call
-
-    per = n_pools if n_pools > 1 else 12
-    g_step = capture(step, per)
-    step_ms, steps_done = timed(g_step, per, args.steps)
-    g_step3 = capture(step_three_calls, per)
-    step3_ms, _ = timed(g_step3, per, args.steps)
-    g_s1 = capture(lambda i: stage1(pools[i % n_pools]), per)
-    s1_ms, _ = timed(g_s1, per, args.steps)
-    g_m = capture(lambda i: merge(), per)
-    m_ms, _ = timed(g_m, per, args.steps)
-    g_q = capture(lambda i: quant(pools[i % n_pools]), per)
-    q_ms, _ = timed(g_q, per, args.steps)
-    # warm column: the same step replayed over one pool (Infinity-Cache resident)
-    def step_warm(i):
-        st = append(pools[0])
-        if st:
-            raise B.Fp8KvError(st, "decode step (warm)")
-
-    g_warm = capture(step_warm, per)
-    warm_ms, _ = timed(g_warm, per, args.steps)
-
-    # correctness guard on the benchmarked configuration (cheap): the fused step
-    # against the two-call decode, with another split count, over the pool the
-    # step has just written the new token into
-    step(0)
-    torch.cuda.synchronize()
-    ref = fk.fp8kv_decode_attn(pools[0], q, table, lens, L, case.sm_scale, max_splits=8)
-    torch.cuda.synchronize()
-    if not torch.allclose(out.float(), ref.float(), atol=2e-2, rtol=0):
-        print("bench: cross-check of the fused step against fp8kv_decode_attn failed", file=sys.stderr)
-        sys.exit(1)
-
+    samples = {}
+    guard = None
+    case0 = None
+    for r in range(args.rounds):
+        res, case = headline_round(fk, B, wl, dev, args, r, stream, bf)
+        if r == 0:
+            case0 = case
+            guard = res.pop("guard", None)
+        for k, v in res.items():
+            samples.setdefault(k, []).append(v)
+    med = {k: statistics.median(v) for k, v in samples.items() if k != "order"}
+    L, Hq, Hkv = case0.max_seq_len, case0.n_q_heads, case0.n_kv_heads
+    kv_bytes = L * Hkv * KV_BYTES_PER_ROW_HEAD
+    step_ms, s1_ms = med["step"], med["stage1"]
     s1_gbps = kv_bytes / (s1_ms * 1e-3) / 1e9
     step_gbps = kv_bytes / (step_ms * 1e-3) / 1e9
+    n_pools = 1 if args.warm else max(1, args.pools)
+    us = lambda ms: round(ms * 1e3, 3)  # noqa: E731
     res = {
         "metric": METRIC,
         "value": round(step_gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps_done,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 6),
         "higher_is_better": True,
@@ -530,19 +649,30 @@ def main():
         "config": {
             "workload": "single-layer batch-1 GQA-8 FP8 decode at 32K context",
             "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "context": L,
-            "pool_rows": case.pool_rows, "page_size": 1, "pool_layout": args.layout,
+            "pool_rows": case0.pool_rows, "page_size": 1, "pool_layout": args.layout,
             "kv_cache": "E4M3FN codes + fp32 per-row scales", "query": "bf16",
             "hbm_state": "warm (one pool)" if args.warm else f"cold ({n_pools} pool copies rotated)",
             "step": "fp8kv_decode_attn_append: stage 1 + merge that quantizes and adds the new K/V row "
                     "(HIP graph replay)",
         },
-        "us_per_layer": round(step_ms * 1e3, 3),
+        "rounds": args.rounds,
+        "round_protocol": f"{args.rounds} seeded rounds (workload seed = round), items in a seeded shuffled order; "
+                          f"each item: {args.warmup} untimed steps, then exactly {args.steps} timed steps in one "
+                          "graph; value and ms_per_step are medians over rounds",
+        "us_per_layer": us(step_ms),
         "pct_hbm_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_layer": kv_bytes,
-        "us_per_layer_three_calls": round(step3_ms * 1e3, 3),
-        "us_per_layer_warm": round(warm_ms * 1e3, 3),
-        "kernels_us": {"quantize_new_row": round(q_ms * 1e3, 3), "decode_stage1": round(s1_ms * 1e3, 3),
-                       "decode_merge": round(m_ms * 1e3, 3)},
+        "us_per_layer_three_calls": us(med["step_three_calls"]),
+        "us_per_layer_warm": us(med["step_warm"]) if "step_warm" in med else None,
+        "kernels_us": {"quantize_new_row": us(med["quantize_new_row"]), "decode_stage1": us(s1_ms),
+                       "decode_merge": us(med["merge"]), "decode_stage1_valu": us(med["stage1_valu"])},
+        "stage1_mfma_vs_valu": {"mfma_us": us(s1_ms), "valu_us": us(med["stage1_valu"]),
+                                "valu_over_mfma": round(med["stage1_valu"] / s1_ms, 3),
+                                "note": "fp8kv_decode_stage1 (bf16 MFMA) against fp8kv_decode_stage1_valu (fp32 "
+                                        "vector FMAs), same grid, same cold rotation, same partials"},
+        "samples_us": {k: [us(x) for x in v] for k, v in samples.items() if k != "order"},
+        "sample_order": samples.get("order"),
+        "guard": guard,
         "roofline": {
             "kernel": "decode_stage1",
             "bound": "hbm",
@@ -553,15 +683,22 @@ def main():
             "traffic": measured_traffic(args.layout, 0 if args.warm else args.pools),
         },
     }
+    if not args.no_floors:
+        fl = read_floor(dev, stream, args.steps, args.warmup)
+        res["roofline"]["read_floor_us"] = fl["us"]
+        res["floors"] = {"read_34.6MB_cold": fl}
+        if "stage1_then_tiny_kernel" in med:
+            res["floors"]["dependent_launch_after_stage1_us"] = us(med["stage1_then_tiny_kernel"] - s1_ms)
+    if not args.no_model_step:
+        res["model_step_48x40k"] = model_step_timing(fk, wl, dev, args, bf, stream)
     if not args.no_prefill:
         res["prefill"] = prefill_timing(fk, wl, dev)
     if not args.no_variants:
-        del g_step, g_step3, g_s1, g_m, g_q, g_warm, pools
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         res["variants"] = variants_timing(fk, wl, dev, args, bf)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(case0, args.cpu_seconds, with_model_step=not args.no_model_step)
     print(json.dumps(res), flush=True)
 
 

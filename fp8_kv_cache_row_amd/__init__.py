@@ -8,10 +8,12 @@ load the library; the first call does, and fails loudly if it is not built.
 from .binding import (Fp8KvError, Fp8KvPool, PoolLayer, decode_workspace, fp8kv_decode_attn,
                       fp8kv_decode_attn_append, fp8kv_decode_attn_rows, fp8kv_decode_attn_rows_append,
                       fp8kv_decode_merge, fp8kv_decode_stage1,
-                      fp8kv_decode_workspace_bytes, fp8kv_prefill_attn, fp8kv_quantize_rows, load, status_string)
+                      fp8kv_decode_workspace_bytes, fp8kv_prefill_attn, fp8kv_prefill_attn_workspace,
+                      fp8kv_quantize_rows, load, status_string)
 
 __all__ = ["Fp8KvError", "Fp8KvPool", "PoolLayer", "decode_workspace", "fp8kv_decode_attn",
            "fp8kv_decode_attn_append", "fp8kv_decode_attn_rows", "fp8kv_decode_attn_rows_append",
            "fp8kv_decode_merge", "fp8kv_decode_stage1",
-           "fp8kv_decode_workspace_bytes", "fp8kv_prefill_attn", "fp8kv_quantize_rows", "load",
+           "fp8kv_decode_workspace_bytes", "fp8kv_prefill_attn", "fp8kv_prefill_attn_workspace",
+           "fp8kv_quantize_rows", "load",
            "status_string"]

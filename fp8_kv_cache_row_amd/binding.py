@@ -91,10 +91,14 @@ def load() -> ctypes.CDLL:
     L.fp8kv_decode_attn_rows_append.restype = ctypes.c_int
     L.fp8kv_decode_stage1.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
     L.fp8kv_decode_stage1.restype = ctypes.c_int
+    L.fp8kv_decode_stage1_valu.argtypes = [P, vp, i32, i32, vp, i64, vp, i32, f32, i32, vp, sz, vp]
+    L.fp8kv_decode_stage1_valu.restype = ctypes.c_int
     L.fp8kv_decode_merge.argtypes = [i32, i32, i32, i32, vp, sz, vp, vp]
     L.fp8kv_decode_merge.restype = ctypes.c_int
     L.fp8kv_prefill_attn.argtypes = [P, vp, vp, vp, i32, i32, vp, i32, vp, vp, i64, f32, vp, vp]
     L.fp8kv_prefill_attn.restype = ctypes.c_int
+    L.fp8kv_prefill_attn_workspace.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, f32, vp, vp]
+    L.fp8kv_prefill_attn_workspace.restype = ctypes.c_int
     L.fp8kv_status_string.argtypes = [ctypes.c_int]
     L.fp8kv_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -149,8 +153,16 @@ class Fp8KvPool:
     layout="interleaved": one record per row holding K codes, V codes, K scales,
       V scales back to back (rounded up to 16 bytes), so every byte of a row is
       in one contiguous span.
+    layout="interleaved64" / "interleaved128": the same record padded to a
+      multiple of 64 / 128 bytes, so every record starts on a 64- / 128-byte
+      boundary (memory-sector alignment; the padding is never read).
+    layout="split": two allocations, one record per row holding the K and V
+      codes of all KV heads (2 * Hkv * D bytes) and one holding its K and V
+      scales (2 * Hkv floats).
     code_format: "e4m3" (OCP E4M3FN, scale amax/448) or "int8" (symmetric, scale amax/127).
     """
+
+    LAYOUTS = ("separate", "interleaved", "interleaved64", "interleaved128", "split")
 
     def __init__(self, num_rows: int, n_kv_heads: int, layout: str = "separate",
                  device: Optional[torch.device] = None, head_dim: int = HEAD_DIM, code_format: str = "e4m3"):
@@ -169,8 +181,11 @@ class Fp8KvPool:
             code_stride, scale_stride = H * D, H
             ptrs = [t.data_ptr() for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales)]
             self._buffers = [self.k_codes, self.v_codes, self.k_scales, self.v_scales]
-        elif layout == "interleaved":
-            rec = -(-(2 * H * D + 2 * H * 4) // 16) * 16
+        elif layout.startswith("interleaved"):
+            align = {"interleaved": 16, "interleaved64": 64, "interleaved128": 128}.get(layout)
+            if align is None:
+                raise ValueError(f"unknown pool layout {layout!r}")
+            rec = -(-(2 * H * D + 2 * H * 4) // align) * align
             self.record = torch.zeros((num_rows, rec), dtype=torch.uint8, device=dev)
             self.k_codes = self.record[:, :H * D].view(num_rows, H, D)
             self.v_codes = self.record[:, H * D:2 * H * D].view(num_rows, H, D)
@@ -180,6 +195,17 @@ class Fp8KvPool:
             code_stride, scale_stride = rec, rec // 4
             ptrs = [base, base + H * D, base + 2 * H * D, base + 2 * H * D + 4 * H]
             self._buffers = [self.record]
+        elif layout == "split":
+            self.codes_record = torch.zeros((num_rows, 2 * H * D), dtype=torch.uint8, device=dev)
+            self.scales_record = torch.zeros((num_rows, 2 * H), dtype=torch.float32, device=dev)
+            self.k_codes = self.codes_record[:, :H * D].view(num_rows, H, D)
+            self.v_codes = self.codes_record[:, H * D:].view(num_rows, H, D)
+            self.k_scales = None  # views of the scale record; read back with scales()
+            self.v_scales = None
+            cb, sb = self.codes_record.data_ptr(), self.scales_record.data_ptr()
+            code_stride, scale_stride = 2 * H * D, 2 * H
+            ptrs = [cb, cb + H * D, sb, sb + 4 * H]
+            self._buffers = [self.codes_record, self.scales_record]
         else:
             raise ValueError(f"unknown pool layout {layout!r}")
         self.layer = PoolLayer(ptrs[0], ptrs[1], ptrs[2], ptrs[3], self.num_rows, H, D,
@@ -190,6 +216,8 @@ class Fp8KvPool:
         if self.layout == "separate":
             return self.k_scales, self.v_scales
         H = self.n_kv_heads
+        if self.layout == "split":
+            return self.scales_record[:, :H].contiguous(), self.scales_record[:, H:].contiguous()
         off = 2 * H * self.head_dim
         ks = self.record[:, off:off + 4 * H].contiguous().view(torch.float32)
         vs = self.record[:, off + 4 * H:off + 8 * H].contiguous().view(torch.float32)
@@ -419,6 +447,19 @@ def fp8kv_decode_stage1(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tenso
     return workspace
 
 
+def fp8kv_decode_stage1_valu(pool: Fp8KvPool, q: torch.Tensor, row_table: torch.Tensor, seq_lens: torch.Tensor,
+                             max_seq_len: int, sm_scale: float, max_splits: int = 0,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Stage 1 on the vector units (no MFMA), same partials as fp8kv_decode_stage1;
+    returns the workspace for fp8kv_decode_merge."""
+    a, workspace = _decode_args(pool, q, row_table, seq_lens, max_seq_len, sm_scale, max_splits, workspace)
+    st = load().fp8kv_decode_stage1_valu(a["pool"], a["q"], a["B"], a["Hq"], a["table"], a["table_stride"],
+                                         a["seq_lens"], a["max_seq_len"], a["sm_scale"], a["max_splits"], a["ws"],
+                                         a["ws_bytes"], _stream(stream))
+    _check(st, "fp8kv_decode_stage1_valu")
+    return workspace
+
+
 def fp8kv_decode_merge(workspace: torch.Tensor, batch: int, n_q_heads: int, max_splits: int = 0,
                        out: Optional[torch.Tensor] = None, stream=None, head_dim: int = HEAD_DIM) -> torch.Tensor:
     """Merge the partials of a preceding fp8kv_decode_stage1 into bf16 out [B][Hq][D]."""
@@ -462,4 +503,35 @@ def fp8kv_prefill_attn(pool: Fp8KvPool, q: torch.Tensor, k_cur: torch.Tensor, v_
                                    _ptr(_bits(ws_k)) if P else None, _ptr(_bits(ws_v)) if P else None, cap,
                                    float(sm_scale), _ptr(_bits(out)), _stream(stream))
     _check(st, "fp8kv_prefill_attn")
+    return out
+
+
+def fp8kv_prefill_attn_workspace(q: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor,
+                                 ws_k: Optional[torch.Tensor], ws_v: Optional[torch.Tensor], sm_scale: float,
+                                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal chunk attention over bf16 prefix rows already in a workspace (ws_k / ws_v
+    [P][Hkv][128], or None for P = 0): step 2 of fp8kv_prefill_attn alone."""
+    for name, t in (("q", q), ("k_cur", k_cur), ("v_cur", v_cur)):
+        _dev_check(t, name, torch.bfloat16)
+        if not t.is_contiguous() or t.dim() != 3 or t.shape[2] != HEAD_DIM:
+            raise ValueError(f"{name} must be a contiguous [T][H][128] bf16 tensor")
+    T, Hq, _ = q.shape
+    Hkv = int(k_cur.shape[1])
+    if k_cur.shape != (T, Hkv, HEAD_DIM) or v_cur.shape != k_cur.shape:
+        raise ValueError("k_cur/v_cur must be [T][Hkv][128]")
+    P = 0
+    if ws_k is not None:
+        for name, t in (("ws_k", ws_k), ("ws_v", ws_v)):
+            _dev_check(t, name, torch.bfloat16)
+            if not t.is_contiguous() or t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, HEAD_DIM):
+                raise ValueError(f"{name} must be a contiguous [P][{Hkv}][128] bf16 tensor")
+        if ws_v.shape != ws_k.shape:
+            raise ValueError("ws_k and ws_v must have the same shape")
+        P = int(ws_k.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().fp8kv_prefill_attn_workspace(_ptr(_bits(q)), _ptr(_bits(k_cur)), _ptr(_bits(v_cur)), T, Hq, Hkv,
+                                             _ptr(_bits(ws_k)) if P else None, _ptr(_bits(ws_v)) if P else None, P,
+                                             float(sm_scale), _ptr(_bits(out)), _stream(stream))
+    _check(st, "fp8kv_prefill_attn_workspace")
     return out

@@ -305,6 +305,25 @@ fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer* pool, const uint16_t* q
                     max_splits, workspace, nullptr, nullptr, stream);
 }
 
+fp8kv_status fp8kv_decode_stage1_valu(const fp8kv_pool_layer* pool, const uint16_t* q, int32_t batch,
+                                      int32_t n_q_heads, const int32_t* row_table, int64_t table_stride,
+                                      const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                      int32_t max_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  fp8kv_status st = check_decode_args(pool, q, batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0,
+                                      sm_scale, max_splits, workspace, workspace_bytes);
+  if (st != FP8KV_OK) return st;
+  if (pool->head_dim != FP8KV_HEAD_DIM || pool->code_format != FP8KV_CODE_E4M3) return FP8KV_ERR_UNSUPPORTED;
+  int n_cu = 0;
+  st = current_device(&n_cu);
+  if (st != FP8KV_OK) return st;
+  const fp8kv::DecodeGeometry geo = choose_geometry(batch, pool->n_kv_heads, pool->head_dim, n_q_heads / pool->n_kv_heads,
+                                                    1, max_seq_len, 0, max_splits, n_cu);
+  const fp8kv::DecodeWorkspace ws = workspace_view(workspace, batch, n_q_heads, pool->head_dim, max_splits);
+  const fp8kv::DecodeShape shape{batch, 1, n_q_heads, row_table, table_stride, seq_lens, max_seq_len, 0};
+  return from_hip(fp8kv::launch_decode_stage1_valu(view_of(pool), q, shape, sm_scale, geo, ws,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 fp8kv_status fp8kv_decode_merge(int32_t n_queries, int32_t n_q_heads, int32_t head_dim, int32_t max_splits,
                                 const void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
   if (n_queries <= 0 || n_q_heads <= 0 || max_splits < 0 || !out) return FP8KV_ERR_INVALID_ARG;
@@ -464,6 +483,25 @@ fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer* pool, const uint16_t* q,
   }
   return from_hip(fp8kv::launch_prefill_attention(q, ws_k, ws_v, k_cur, v_cur, n_prefix, n_tokens, n_q_heads,
                                                   pool->n_kv_heads, sm_scale, out, s));
+}
+
+fp8kv_status fp8kv_prefill_attn_workspace(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                          int32_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                          const uint16_t* ws_k, const uint16_t* ws_v, int32_t n_prefix, float sm_scale,
+                                          uint16_t* out, void* stream) {
+  if (!q || !k_cur || !v_cur || !out) return FP8KV_ERR_INVALID_ARG;
+  if (n_tokens <= 0 || n_prefix < 0 || n_kv_heads <= 0) return FP8KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return FP8KV_ERR_INVALID_ARG;
+  if (!supported_group(n_q_heads, n_kv_heads)) return FP8KV_ERR_UNSUPPORTED;
+  if (!valid_softmax_scale(sm_scale)) return FP8KV_ERR_INVALID_ARG;
+  if (n_prefix > 0 && (!ws_k || !ws_v)) return FP8KV_ERR_WORKSPACE;
+  if (n_prefix > 0 && (!aligned(ws_k, 16) || !aligned(ws_v, 16))) return FP8KV_ERR_ALIGNMENT;
+  if (!aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16) || !aligned(out, 16))
+    return FP8KV_ERR_ALIGNMENT;
+  fp8kv_status st = current_device(nullptr);
+  if (st != FP8KV_OK) return st;
+  return from_hip(fp8kv::launch_prefill_attention(q, ws_k, ws_v, k_cur, v_cur, n_prefix, n_tokens, n_q_heads,
+                                                  n_kv_heads, sm_scale, out, static_cast<hipStream_t>(stream)));
 }
 
 const char* fp8kv_status_string(fp8kv_status status) {

@@ -96,6 +96,12 @@ hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const D
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
                                 hipStream_t stream);
 
+// The VALU-only stage 1 (no matrix instructions), same grid and partials:
+// head dim 128, E4M3 codes, one query row, no window.
+hipError_t launch_decode_stage1_valu(const PoolView& pool, const uint16_t* q, const DecodeShape& shape,
+                                     float sm_scale, const DecodeGeometry& geo, const DecodeWorkspace& ws,
+                                     hipStream_t stream);
+
 // n_split < 0: take the split count the preceding stage 1 wrote into the
 // header.  n_rows_heads = batch * n_qrows * n_q_heads output vectors.
 hipError_t launch_decode_merge(int64_t n_rows_heads, int32_t head_dim, const DecodeWorkspace& ws, int32_t n_split,

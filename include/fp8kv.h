@@ -14,12 +14,16 @@
  * 1/3/8 query rows per request and an odd sliding window.
  *
  * Entry points: fp8kv_quantize_rows (quantize-on-write); fp8kv_decode_attn and
- * its two stages fp8kv_decode_stage1 / fp8kv_decode_merge; fp8kv_decode_attn_rows
+ * its two stages fp8kv_decode_stage1 / fp8kv_decode_merge (and
+ * fp8kv_decode_stage1_valu, stage 1 on the vector units for comparison);
+ * fp8kv_decode_attn_rows
  * (several query rows, sliding window); fp8kv_decode_attn_append,
  * fp8kv_decode_attn_append_window and fp8kv_decode_attn_rows_append (a decode
  * step with its new tokens quantized on write in the same call);
  * fp8kv_decode_attn_append_noalloc (the same step without a caller workspace);
- * fp8kv_prefill_attn (reconstruct + causal chunk attention);
+ * fp8kv_prefill_attn (reconstruct + causal chunk attention) and
+ * fp8kv_prefill_attn_workspace (the attention over an already rebuilt
+ * workspace);
  * fp8kv_decode_workspace_bytes and fp8kv_status_string.
  *
  * Conventions shared by every call
@@ -223,6 +227,24 @@ fp8kv_status fp8kv_decode_stage1(const fp8kv_pool_layer *pool, const uint16_t *q
                                  const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                                  int32_t max_splits, void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/*
+ * fp8kv_decode_stage1_valu -- fp8kv_decode_stage1 computed without matrix
+ * instructions (plain fp32 vector FMAs: one key per lane for the QK^T dot
+ * products, two output elements per lane for P*V), on the same grid and into
+ * the same partials, so fp8kv_decode_merge combines it.  It exists to measure
+ * the decode contraction on the vector units against the bf16 MFMA path of
+ * fp8kv_decode_stage1 on the same inputs (FreeToken PR #897 description: the
+ * RDNA4 reader widens FP8 for the existing matrix math; which unit wins is a
+ * property of the hardware).  Same arguments, checks and errors as
+ * fp8kv_decode_stage1; head_dim 128 and E4M3 pools only (others return
+ * FP8KV_ERR_UNSUPPORTED).
+ */
+fp8kv_status fp8kv_decode_stage1_valu(const fp8kv_pool_layer *pool, const uint16_t *q, int32_t batch,
+                                      int32_t n_q_heads, const int32_t *row_table, int64_t table_stride,
+                                      const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                                      int32_t max_splits, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /*
  * fp8kv_decode_merge -- the merge (stage 2) of the decode calls: combines the
@@ -430,6 +452,35 @@ fp8kv_status fp8kv_prefill_attn(const fp8kv_pool_layer *pool, const uint16_t *q,
                                 const int32_t *prefix_rows, int32_t n_prefix, uint16_t *ws_k,
                                 uint16_t *ws_v, int64_t ws_capacity_rows, float sm_scale,
                                 uint16_t *out, void *stream);
+
+/*
+ * fp8kv_prefill_attn_workspace -- step 2 of fp8kv_prefill_attn alone: causal
+ * attention of one bf16 chunk over bf16 prefix rows that are already in a
+ * workspace (FreeToken PR #853, "What changes": the prefill attends over the
+ * BF16 workspace rebuilt once per layer, followed by the BF16 chunk; "Paired
+ * end-to-end A/B": the same operator over a BF16 KV pool is the comparison
+ * point).  Use it for every further call of a layer whose workspace one
+ * fp8kv_prefill_attn call has already rebuilt, or over the rows of a BF16 KV
+ * cache.
+ *
+ * Chunk query i (absolute position n_prefix + i) attends to keys/values
+ * [ws rows 0..n_prefix-1 ; chunk rows 0..i] with KV head
+ * g = h / (n_q_heads / n_kv_heads) and softmax scale sm_scale; out[i][h] is
+ * rounded to bf16 -- step 2 of fp8kv_prefill_attn, bit for bit.
+ *
+ * q:            device bf16 [n_tokens][n_q_heads][128], contiguous.
+ * k_cur, v_cur: device bf16 [n_tokens][n_kv_heads][128], contiguous.
+ * ws_k, ws_v:   device bf16 [n_prefix][n_kv_heads][128] (may be NULL when
+ *               n_prefix == 0).
+ * out:          device bf16 [n_tokens][n_q_heads][128].
+ * All bf16 bases 16-byte aligned.  n_tokens >= 1, n_prefix >= 0, n_q_heads a
+ * multiple of n_kv_heads with a ratio in {1, 2, 4, 8, 16}.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE (ws missing), HIP.
+ */
+fp8kv_status fp8kv_prefill_attn_workspace(const uint16_t *q, const uint16_t *k_cur, const uint16_t *v_cur,
+                                          int32_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                          const uint16_t *ws_k, const uint16_t *ws_v, int32_t n_prefix,
+                                          float sm_scale, uint16_t *out, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *fp8kv_status_string(fp8kv_status status);

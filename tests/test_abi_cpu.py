@@ -255,6 +255,26 @@ def test_prefill_validation(lib):
     assert _prefill(lib, _pool(head_dim=256, code_row_stride=1024)) == UNSUPPORTED  # prefill runs at D = 128
 
 
+def _prefill_ws(lib, q=A, kc=A, vc=A, T=16, hq=32, hkv=4, wsk=A, wsv=A, P=8, sm=0.088, out=A):
+    return lib.fp8kv_prefill_attn_workspace(q, kc, vc, T, hq, hkv, wsk, wsv, P, sm, out, None)
+
+
+def test_prefill_workspace_validation(lib):
+    assert _prefill_ws(lib, q=0) == INVALID
+    assert _prefill_ws(lib, out=0) == INVALID
+    assert _prefill_ws(lib, T=0) == INVALID
+    assert _prefill_ws(lib, P=-1) == INVALID
+    assert _prefill_ws(lib, hkv=0) == INVALID
+    assert _prefill_ws(lib, hq=30) == INVALID                        # not a multiple of Hkv
+    assert _prefill_ws(lib, hq=12) == UNSUPPORTED                    # G = 3
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _prefill_ws(lib, sm=bad) == INVALID, bad
+    assert _prefill_ws(lib, wsk=0) == WORKSPACE
+    assert _prefill_ws(lib, wsv=A + 2) == ALIGN
+    assert _prefill_ws(lib, q=A + 8) == ALIGN
+    assert _prefill_ws(lib, P=0, wsk=0, wsv=0, q=A + 8) == ALIGN     # no prefix: ws pointers unused
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0,
                     reason="valid-looking fake pointers must never reach a real GPU")
 def test_valid_arguments_reach_the_device_check(lib):
@@ -276,6 +296,8 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert _append(lib, _pool()) == HIP
     assert _append_window(lib, _pool(), 17) == HIP
     assert _rows_append(lib, _pool(), nq=8, window=5) == HIP
+    assert _prefill_ws(lib) == HIP
+    assert _prefill_ws(lib, P=0, wsk=0, wsv=0) == HIP
 
 
 def test_header_is_plain_c99_and_the_library_links(tmp_path, lib):

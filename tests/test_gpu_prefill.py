@@ -148,3 +148,36 @@ def test_prefill_graph_replay_matches_eager():
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}: out"
         assert torch.equal(ws_k.view(torch.int16), ref_k.view(torch.int16)), f"replay {rep}: ws_k"
         assert torch.equal(ws_v.view(torch.int16), ref_v.view(torch.int16)), f"replay {rep}: ws_v"
+
+
+@pytest.mark.parametrize("P,T,Hq,Hkv", [(0, 37, 32, 4), (300, 100, 32, 4), (1000, 300, 8, 8), (777, 513, 16, 2)])
+def test_prefill_over_a_bf16_workspace(P, T, Hq, Hkv):
+    """fp8kv_prefill_attn_workspace over bf16 prefix rows given directly (a BF16
+    KV cache, no reconstruction) against the fp64 oracle on the same rows."""
+    say(f"prefill over a bf16 workspace P={P} T={T} Hq={Hq} Hkv={Hkv}")
+    case = wl.chunked_prefill(seed=P + 3 * T, n_prefix=P, n_chunk=T, n_q_heads=Hq, n_kv_heads=Hkv)
+    ws_k = to_dev_bf16(case.prefix_k) if P else None
+    ws_v = to_dev_bf16(case.prefix_v) if P else None
+    out = fk.fp8kv_prefill_attn_workspace(to_dev_bf16(case.q), to_dev_bf16(case.k_cur), to_dev_bf16(case.v_cur),
+                                          ws_k, ws_v, case.sm_scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_attention(case.q, case.prefix_k if P else None, case.prefix_v if P else None,
+                                   case.k_cur, case.v_cur, case.sm_scale)
+    assert_close(bf16_to_f64(out), ref, f"bf16 workspace P={P} T={T}")
+
+
+def test_prefill_workspace_call_is_step_two_of_the_fp8_call():
+    """Attention over the workspace that fp8kv_prefill_attn rebuilt is that call's
+    output, bit for bit."""
+    say("prefill: fp8kv_prefill_attn_workspace over the rebuilt workspace == fp8kv_prefill_attn")
+    case = wl.chunked_prefill(seed=9, n_prefix=1200, n_chunk=333)
+    P, H = case.prefix_k.shape[0], case.n_kv_heads
+    pool = fk.Fp8KvPool(case.pool_rows, H, device=DEV)
+    fk.fp8kv_quantize_rows(pool, to_dev_bf16(case.prefix_k), to_dev_bf16(case.prefix_v), to_dev(case.prefix_rows))
+    q, kc, vc = to_dev_bf16(case.q), to_dev_bf16(case.k_cur), to_dev_bf16(case.v_cur)
+    ws_k = torch.empty((P, H, D), dtype=torch.bfloat16, device=DEV)
+    ws_v = torch.empty_like(ws_k)
+    a = fk.fp8kv_prefill_attn(pool, q, kc, vc, to_dev(case.prefix_rows), ws_k, ws_v, case.sm_scale)
+    b = fk.fp8kv_prefill_attn_workspace(q, kc, vc, ws_k, ws_v, case.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
