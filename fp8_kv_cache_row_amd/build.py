@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8kv.so")
+# measurement kernels of the benchmark (a contiguous and a gathered read floor), not part of the path
+FLOOR_SRC = os.path.join(PKG, "floor", "read_floor.hip")
+FLOOR_LIB = os.path.join(PKG, "libfp8kv_floor.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -39,7 +42,18 @@ def build(verbose: bool = False, extra=None) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_floor(verbose)
     return LIB
+
+
+def build_floor(verbose: bool = False) -> str:
+    tmp = FLOOR_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, FLOOR_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, FLOOR_LIB)
+    return FLOOR_LIB
 
 
 if __name__ == "__main__":
