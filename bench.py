@@ -596,39 +596,49 @@ def floor_lib():
     return L
 
 
-def read_floors(dev, stream, steps, warmup, n=12, nbytes=34603008):
-    """Cold reads of 34,603,008 bytes rotated over n distinct buffers: a plain
-    contiguous read kernel, and a library reduction (torch.sum over the rows of
-    an fp32 [33,792][256] tensor, one workgroup per row block, no cross-workgroup
-    step) for comparison."""
+def read_floors(dev, stream, steps, warmup, nbytes=34603008):
+    """Cold reads rotated over distinct buffers: a plain contiguous read kernel
+    of 34,603,008 bytes (and of 2x and 8x that, to show how a one-shot read's
+    rate grows with its size), and a library reduction of 34,603,008 bytes
+    (torch.sum over the rows of an fp32 [33,792][256] tensor, one workgroup per
+    row block, no cross-workgroup step) for comparison."""
     import torch
     L = floor_lib()
-    bufs = [torch.full((nbytes // 4,), float(i + 1), dtype=torch.float32, device=dev) for i in range(n)]
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
-
-    def contiguous(i):
-        if L.fp8kv_floor_read(bufs[i % n].data_ptr(), nbytes, 512, sink.data_ptr(), sp):
-            raise RuntimeError("fp8kv_floor_read failed")
-
-    rows = nbytes // (256 * 4)
-    views = [b.view(rows, 256) for b in bufs]
-    outs = torch.empty((rows,), dtype=torch.float32, device=dev)
-
-    def reduction(i):
-        with torch.cuda.stream(stream):
-            torch.sum(views[i % n], dim=1, out=outs)
-
     res = {}
-    for name, body, what in (("contiguous_read", contiguous, "contiguous 16-byte loads, 512 workgroups x 512 lanes, "
-                                                             "eight loads in flight per lane"),
-                             ("library_reduction", reduction, f"torch.sum(dim=1) of an fp32 [{rows}][256] tensor")):
-        ms = time_exact(stream, body, steps, warmup)
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        res[name] = {"us": round(ms * 1e3, 3), "bytes": nbytes, "gbps": round(gbps, 1),
-                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "op": what + f", {n} rotated buffers, graph replay"}
-    del bufs, views
-    torch.cuda.empty_cache()
+
+    def record(name, ms, nb, what):
+        gbps = nb / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 3), "bytes": nb, "gbps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "op": what}
+
+    for mult, n in ((1, 12), (2, 8), (8, 4)):  # every size's rotation exceeds the 256 MB Infinity Cache
+        nb = nbytes * mult
+        bufs = [torch.full((nb // 4,), float(i + 1), dtype=torch.float32, device=dev) for i in range(n)]
+
+        def contiguous(i, bufs=bufs, nb=nb, n=n):
+            if L.fp8kv_floor_read(bufs[i % n].data_ptr(), nb, 512, sink.data_ptr(), sp):
+                raise RuntimeError("fp8kv_floor_read failed")
+
+        name = "contiguous_read" if mult == 1 else f"contiguous_read_x{mult}"
+        record(name, time_exact(stream, contiguous, steps, warmup), nb,
+               f"contiguous 16-byte loads, 512 workgroups x 512 lanes, eight loads in flight per lane, {n} rotated "
+               "buffers, graph replay")
+        if mult == 1:
+            rows = nb // (256 * 4)
+            views = [b.view(rows, 256) for b in bufs]
+            outs = torch.empty((rows,), dtype=torch.float32, device=dev)
+
+            def reduction(i):
+                with torch.cuda.stream(stream):
+                    torch.sum(views[i % n], dim=1, out=outs)
+
+            record("library_reduction", time_exact(stream, reduction, steps, warmup), nb,
+                   f"torch.sum(dim=1) of an fp32 [{rows}][256] tensor, {n} rotated buffers, graph replay")
+            del views
+        del bufs
+        torch.cuda.empty_cache()
     return res
 
 
