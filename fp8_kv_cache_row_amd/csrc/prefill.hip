@@ -26,9 +26,10 @@
 // lane s names row s/4, columns 4(s%4)..+3 of a 4x16 block, and lane i
 // receives column i of its 4 rows.
 //
-// Pipelining: the tiles are double-buffered; the loads of tile t+1 are issued
-// right after the barrier that opens tile t, so one barrier per tile suffices
-// and the load latency hides behind the MFMA work.  Online softmax in log2
+// Pipelining: the tiles are double-buffered, each buffer its own LDS object;
+// the loads of tile t+1 are issued right after the barrier that opens tile t,
+// so one barrier per tile suffices and the load latency hides behind the MFMA
+// work.  Online softmax in log2
 // units with a lazy maximum (O and l are rescaled only when a sub-step's
 // maximum exceeds the running one by more than 8), so the accumulators are
 // normally touched by the MFMA alone; the row sums are an MFMA of P against a
@@ -95,8 +96,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
     const uint16_t* __restrict__ k_cur, const uint16_t* __restrict__ v_cur, int32_t n_prefix, int32_t n_tokens,
     int32_t n_q_heads, int32_t n_kv_heads, float qk_scale_log2, uint16_t* __restrict__ out) {
   constexpr int BQ = kRowsPerWg / G;  // query tokens per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][kTileBytes];
+  // One LDS object per buffer: the compiler then knows that the loads filling
+  // one buffer never write what the reads of the other see, and keeps the
+  // next tile's loads in flight while this tile is computed (with a single
+  // two-buffer array it waited for them before this tile's first LDS read).
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds1[kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -154,9 +161,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
     fofs[i] = (uint32_t)(fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ (fkey[i] & 15)) << 3)) * 2u;
     vfofs[i] = (uint32_t)(fkey[i] * (int)kv_row + g * kHeadDim + (((lane & 15) ^ vswz(fkey[i])) << 3)) * 2u;
   }
-  auto fetch = [&](int buf, int u0) {
-    uint8_t* kd = k_lds[buf] + kLoadsPerWave * wave * 1024;
-    uint8_t* vd = v_lds[buf] + kLoadsPerWave * wave * 1024;
+  auto fetch = [&](auto bufc, int u0) {
+    constexpr int buf = decltype(bufc)::value;
+    uint8_t* kd = (buf == 0 ? k_lds0 : k_lds1) + kLoadsPerWave * wave * 1024;
+    uint8_t* vd = (buf == 0 ? v_lds0 : v_lds1) + kLoadsPerWave * wave * 1024;
     if (u0 + kTileKeys <= n_prefix || (u0 >= n_prefix && u0 + kTileKeys <= n_keys)) {
       // the whole tile comes from one source: one base plus fixed offsets
       const int64_t base = (u0 < n_prefix) ? (int64_t)u0 * kv_row : (int64_t)(u0 - n_prefix) * kv_row;
@@ -201,9 +209,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
     const int u0 = tile * kTileKeys;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `tile` have landed (vmcnt 0)
     __syncthreads();                // every wave's have; the other buffer is free
-    if (tile + 1 < n_tiles) fetch(buf ^ 1, u0 + kTileKeys);
-    const uint8_t* kt = k_lds[buf];
-    const uint8_t* vt = v_lds[buf];
+    if (tile + 1 < n_tiles) fetch(std::integral_constant<int, buf ^ 1>{}, u0 + kTileKeys);
+    const uint8_t* kt = buf == 0 ? k_lds0 : k_lds1;
+    const uint8_t* vt = buf == 0 ? v_lds0 : v_lds1;
 
     const bool tile_mask = (u0 + kTileKeys - 1 > diag) || (u0 + kTileKeys > n_keys);
 #pragma unroll
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
     }
   };
 
-  fetch(0, 0);
+  fetch(std::integral_constant<int, 0>{}, 0);
   // The tile loop is unrolled by the buffer parity so that LDS offsets are
   // compile-time constants.
   for (int tile = 0; tile < n_tiles; tile += 2) {
