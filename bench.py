@@ -79,6 +79,9 @@ def parse():
                          "kernel traces of the headline are taken without it)")
     ap.add_argument("--model-step-steps", type=int, default=8, help="timed 48-layer steps")
     ap.add_argument("--no-floors", action="store_true", help="skip the read-floor and dependent-launch timings")
+    ap.add_argument("--timeline", action="store_true",
+                    help="also run the measurement build with per-wave stage-1 timestamps (libfp8kv_timeline.so) "
+                         "on the headline workload and report when each wave's data arrives and its work ends")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run plain 64 MiB device copies (a known-size kernel for HBM byte counters)")
     return ap.parse_args()
@@ -596,6 +599,73 @@ def floor_lib():
     return L
 
 
+def wave_timeline(fk, B, wl, dev, bf, stream, launches: int = 24, warm_launches: int = 12):
+    """Per-wave timestamps of the 32K-context stage 1 from the measurement
+    build (libfp8kv_timeline.so: the same kernels with the 100 MHz real-time
+    counter recorded at six points by lane 0 of every wave), one launch at a
+    time over the headline's 12 rotated cold pools.  Times are microseconds
+    from the launch's first wave entry; the instrumented kernel runs a little
+    slower than the product one (each point is a scheduling barrier and a
+    counter read)."""
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "fp8_kv_cache_row_amd", "libfp8kv_timeline.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    TL = ctypes.CDLL(path)
+    main_lib = B.load()
+    TL.fp8kv_decode_stage1.argtypes = main_lib.fp8kv_decode_stage1.argtypes
+    TL.fp8kv_decode_stage1.restype = main_lib.fp8kv_decode_stage1.restype
+    TL.fp8kv_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_long]
+    case = wl.layer_decode(0)
+    L, Hq = case.max_seq_len, case.n_q_heads
+    pools = rotated_pools(fk, case, "interleaved", 12, dev, bf)
+    q = bf(case.q)
+    table = torch.from_numpy(case.table).to(dev)
+    lens = torch.from_numpy(case.seq_lens).to(dev)
+    ws = fk.decode_workspace(1, Hq, 0, dev)
+    n_wg, n_w, n_pt = 256, 8, 8  # the 32K layer's grid: 64 splits x 4 KV heads, 8 waves each
+    host = np.zeros(n_wg * n_w * n_pt, np.uint64)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    runs = []
+    for it in range(warm_launches + launches):
+        if TL.fp8kv_timeline_clear() != 0:
+            raise RuntimeError("fp8kv_timeline_clear failed")
+        torch.cuda.synchronize()
+        st = TL.fp8kv_decode_stage1(ctypes.byref(pools[it % 12].layer), q.data_ptr(), 1, Hq, table.data_ptr(), L,
+                                    lens.data_ptr(), L, case.sm_scale, 0, ws.data_ptr(), ws.numel(), sp)
+        if st:
+            raise B.Fp8KvError(st, "fp8kv_decode_stage1 (timeline build)")
+        torch.cuda.synchronize()
+        if TL.fp8kv_timeline_read(host.ctypes.data, host.size) != 0:
+            raise RuntimeError("fp8kv_timeline_read failed")
+        if it >= warm_launches:
+            runs.append(host.reshape(n_wg, n_w, n_pt)[:, :, :6].astype(np.int64).copy())
+    T = np.stack(runs)  # [launch, workgroup, wave, point]
+    if (T == 0).any():
+        raise RuntimeError("timeline: a wave left a point unrecorded")
+    rel = (T - T[..., 0].min(axis=(1, 2))[:, None, None, None]) * 1e-2  # 100 MHz ticks -> us
+    names = ["entry", "row_indices_in", "scales_in", "step0_done", "steps_done", "partials_stored"]
+    by_wave = {nm: [round(float(x), 2) for x in rel[..., k].mean(axis=(0, 1))] for k, nm in enumerate(names)}
+    wg_end = rel[..., 5].max(axis=2)
+    span = rel[..., 5].max(axis=(1, 2))
+    lo, hi = rel[:, :, :4], rel[:, :, 4:]
+    return {
+        "launches": launches,
+        "us_by_wave_index": by_wave,
+        "span_us_median": round(float(np.median(span)), 2),
+        "workgroup_end_us": {"p10": round(float(np.percentile(wg_end, 10)), 2),
+                             "p50": round(float(np.median(wg_end)), 2),
+                             "p90": round(float(np.percentile(wg_end, 90)), 2)},
+        "scales_in_waves_4_7_minus_0_3_us": round(float(hi[..., 2].mean() - lo[..., 2].mean()), 2),
+        "compute_after_scales_in_waves_4_7_us": round(float((hi[..., 4] - hi[..., 2]).mean()), 2),
+        "workgroup_merge_after_last_wave_us": round(float((rel[..., 0, 5] - rel[..., 4].max(axis=2)).mean()), 2),
+        "workgroup_to_xcd": "workgroup x + 32 y runs on XCD x & 7 (split 8y + (x & 7), KV head x >> 3)",
+        "note": "points: wave entry; its first group's row indices in LDS; its scales in (every code load "
+                "issued); its first 32-key step done; all its steps done; the workgroup's partials stored",
+    }
+
+
 def read_floors(dev, stream, steps, warmup, nbytes=34603008):
     """Cold reads rotated over distinct buffers: a plain contiguous read kernel
     of 34,603,008 bytes (and of 2x and 8x that, to show how a one-shot read's
@@ -752,6 +822,8 @@ def main():
                       "page-size-1 reader fetches), 256 workgroups, the headline's rotated pools"}
         if "stage1_then_tiny_kernel" in med:
             res["floors"]["dependent_launch_after_stage1_us"] = us(med["stage1_then_tiny_kernel"] - s1_ms)
+    if args.timeline:
+        res["wave_timeline"] = wave_timeline(fk, B, wl, dev, bf, stream)
     if not args.no_model_step:
         res["model_step_48x40k"] = model_step_timing(fk, wl, dev, args, bf, stream)
     if not args.no_prefill:

@@ -14,6 +14,9 @@ LIB = os.path.join(PKG, "libfp8kv.so")
 # measurement kernels of the benchmark (a contiguous and a gathered read floor), not part of the path
 FLOOR_SRC = os.path.join(PKG, "floor", "read_floor.hip")
 FLOOR_LIB = os.path.join(PKG, "libfp8kv_floor.so")
+# measurement build of the same sources with per-wave stage-1 timestamps (the
+# benchmark's --timeline leg), not part of the path
+TIMELINE_LIB = os.path.join(PKG, "libfp8kv_timeline.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -43,7 +46,18 @@ def build(verbose: bool = False, extra=None) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     build_floor(verbose)
+    build_timeline(verbose)
     return LIB
+
+
+def build_timeline(verbose: bool = False) -> str:
+    tmp = TIMELINE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-DFP8KV_WAVE_TIMELINE", "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, TIMELINE_LIB)
+    return TIMELINE_LIB
 
 
 def build_floor(verbose: bool = False) -> str:

@@ -46,6 +46,29 @@
 
 namespace fp8kv {
 
+// Measurement build only (FP8KV_WAVE_TIMELINE, the benchmark's timeline
+// library; the product library is built without it): each wave of stage 1
+// records the 100 MHz real-time counter at fixed points -- entry, its first
+// group's row indices in, its scales in, its first step done, all steps done,
+// partials stored -- in fp8kv_timeline[(workgroup * waves + wave) * 8 + point]
+// for the first kTimelineWorkgroups workgroups of a launch.
+#ifdef FP8KV_WAVE_TIMELINE
+constexpr int kTimelineWorkgroups = 1024;
+__device__ unsigned long long fp8kv_timeline[kTimelineWorkgroups * 8 * 8];
+#define FP8KV_MARK(point, cond)                                                                           \
+  do {                                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                                   \
+    const unsigned long long t_ = __builtin_amdgcn_s_memrealtime();                                      \
+    const int wg_ = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));              \
+    if ((cond) && lane == 0 && wg_ < kTimelineWorkgroups) fp8kv_timeline[(wg_ * 8 + wave) * 8 + (point)] = t_; \
+    __builtin_amdgcn_sched_barrier(0);                                                                   \
+  } while (0)
+#else
+#define FP8KV_MARK(point, cond) \
+  do {                          \
+  } while (0)
+#endif
+
 namespace {
 
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
@@ -137,6 +160,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
   const int G = C::MULTI ? (1 << g_shift) : C::G;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  FP8KV_MARK(0, true);
   const int n = lane & 15;
   const int j = lane >> 4;
   // Grid (8 * Hkv, ceil(n_split / 8), batch * column groups): workgroup
@@ -184,6 +208,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
       rows_in[c] = (int)min((uint32_t)trow[max(min(k0 + c * kWave + lane, key_bound - 1), 0)], max_row);
 #pragma unroll
     for (int c = 0; c < kRowSlots; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
+    FP8KV_MARK(1, true);
   }
 
   // Q^T operand of tile t: column n is c = (cg * NT + t) * 16 + n (query row
@@ -308,6 +333,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 #pragma unroll
     for (int c = 0; c < kRowSlots; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
     __builtin_amdgcn_wave_barrier();
+    FP8KV_MARK(2, first);
     // Wave-uniform: only groups that reach past the first row's end, or start
     // below the last row's window start, need per-column masks.
     const bool masked = (k0 + kGroupKeys > min(first_end, key_end)) || (C::WINDOW && k0 < last_lo);
@@ -404,11 +430,13 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
       }
     };
     step(std::integral_constant<int, 0>{});
+    FP8KV_MARK(3, first);
     if constexpr (kSteps > 1) step(std::integral_constant<int, 1>{});
     if constexpr (kSteps > 2) step(std::integral_constant<int, 2>{});
     if constexpr (kSteps > 3) step(std::integral_constant<int, 3>{});
     __builtin_amdgcn_wave_barrier();  // this group's LDS is consumed before the next overwrites it
   }
+  FP8KV_MARK(4, true);
 
   // Merge the waves of this workgroup into one partial per column, one pass
   // per (tile, 128 of the D columns of O).  In pass half, LDS column
@@ -468,6 +496,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
   // The split count for a merge launched without one.  Written last: a branch
   // at the top would split the entry block and serialize the argument loads
   // ahead of the first table read.
+  FP8KV_MARK(5, true);
   if (split == 0 && g == 0 && cg == 0 && b == 0 && threadIdx.x == 0) header[0] = n_split;
 }
 
@@ -868,3 +897,19 @@ hipError_t launch_decode_merge_append(const PoolView& pool, int32_t batch, int32
 }
 
 }  // namespace fp8kv
+
+#ifdef FP8KV_WAVE_TIMELINE
+// Measurement build: copy the first n stage-1 timeline slots to host memory /
+// clear all of them.  0 on success, else the HIP error code.
+extern "C" int fp8kv_timeline_read(unsigned long long* host, long n) {
+  if (!host || n < 0 || n > (long)(fp8kv::kTimelineWorkgroups * 64)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(fp8kv::fp8kv_timeline), n * sizeof(unsigned long long), 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int fp8kv_timeline_clear() {
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(fp8kv::fp8kv_timeline));
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemset(p, 0, sizeof(unsigned long long) * fp8kv::kTimelineWorkgroups * 64);
+}
+#endif
