@@ -29,6 +29,20 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_measurement_libraries_load_and_export_their_entry_points(lib):
+    """The benchmark's measurement builds: the read floors, and the per-wave
+    timeline build, which is the same sources (every declared entry point)
+    plus its two timeline accessors."""
+    pkg = os.path.dirname(B.lib_path())
+    floor = ctypes.CDLL(os.path.join(pkg, "libfp8kv_floor.so"))
+    for n in ("fp8kv_floor_read", "fp8kv_floor_gather"):
+        assert hasattr(floor, n), n
+    tl = ctypes.CDLL(os.path.join(pkg, "libfp8kv_timeline.so"))
+    for n in list(B.declared_symbols()) + ["fp8kv_timeline_read", "fp8kv_timeline_clear"]:
+        assert hasattr(tl, n), n
+    assert not hasattr(lib, "fp8kv_timeline_read")  # the product library has no timeline
+
+
 def test_pool_struct_matches_the_header():
     """The ctypes mirror has the C struct's size and field offsets."""
     assert ctypes.sizeof(B.PoolLayer) == 72
