@@ -15,16 +15,19 @@ Protocol: `--rounds` seeded rounds (workload seed r for round r), each with
 its own pool; inside a round the timed items run in a seeded shuffled order,
 each as `--warmup` untimed steps followed by exactly `--steps` timed steps
 (one HIP graph each, HIP events on the graph's stream).  Cold HBM: the steps
-rotate over `--pools` identical copies of the layer's pool (12 x 34.9 MB =
-419 MB, more than the 256 MB Infinity Cache), as the layers of a model do;
+rotate over `--pools` identical copies of the layer's pool (12 x 38.1 MB =
+457 MB of 1,152-byte row records, more than the 256 MB Infinity Cache), as
+the layers of a model do;
 the warm column replays the same step over one pool.  `value` and
 `ms_per_step` are the median over rounds; every sample is kept.
 
 Also timed by default: the 48-layer step at 40,000 context (48 distinct
 40,290-row pools, 2 GB); the 8K FP8 prefix + 8K chunk prefill with a BF16
 prefix beside it; the decode variants (head dim 256, several query rows, a
-sliding window, INT8, a 16-request batch); two floors (a plain 34.6 MB cold
-read by a library reduction, and a dependent kernel launch after stage 1);
+sliding window, INT8, a 16-request batch); read floors (cold contiguous
+reads of 1x, 2x and 8x the layer's bytes, the layer's row records gathered
+through its table, a library reduction, and a dependent kernel launch after
+stage 1);
 and the CPU oracle on the host cores.
 
 Prints one JSON line.  `value` is the effective KV bandwidth of the whole step
@@ -62,10 +65,12 @@ def parse():
     ap.add_argument("--rounds", type=int, default=5, help="seeded rounds of the headline workload")
     ap.add_argument("--pools", type=int, default=12, help="pool copies rotated per step (cold HBM)")
     ap.add_argument("--max-splits", type=int, default=0)
-    ap.add_argument("--layout", default="interleaved", choices=LAYOUTS,
-                    help="pool layout: interleaved 1,056-byte row records (K codes, V codes, K scales, V scales "
-                         "of all KV heads), the same padded to 64 / 128 bytes, code records + scale records "
-                         "(split), or four separate arrays")
+    ap.add_argument("--layout", default="interleaved128", choices=LAYOUTS,
+                    help="pool layout: one row record holding the K codes, V codes, K scales and V scales of all "
+                         "KV heads, padded to 128 bytes (1,152 bytes: every KV head's code rows fill whole "
+                         "128-byte lines, so the decode reads them with non-temporal loads), the same unpadded "
+                         "(1,056 bytes) or padded to 64 bytes, code records + scale records (split), or four "
+                         "separate arrays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="reuse one pool (Infinity-Cache resident) for everything")
@@ -599,7 +604,7 @@ def floor_lib():
     return L
 
 
-def wave_timeline(fk, B, wl, dev, bf, stream, launches: int = 24, warm_launches: int = 12):
+def wave_timeline(fk, B, wl, dev, bf, stream, layout: str, launches: int = 24, warm_launches: int = 12):
     """Per-wave timestamps of the 32K-context stage 1 from the measurement
     build (libfp8kv_timeline.so: the same kernels with the 100 MHz real-time
     counter recorded at six points by lane 0 of every wave), one launch at a
@@ -619,7 +624,7 @@ def wave_timeline(fk, B, wl, dev, bf, stream, launches: int = 24, warm_launches:
     TL.fp8kv_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_long]
     case = wl.layer_decode(0)
     L, Hq = case.max_seq_len, case.n_q_heads
-    pools = rotated_pools(fk, case, "interleaved", 12, dev, bf)
+    pools = rotated_pools(fk, case, layout, 12, dev, bf)
     q = bf(case.q)
     table = torch.from_numpy(case.table).to(dev)
     lens = torch.from_numpy(case.seq_lens).to(dev)
@@ -652,6 +657,7 @@ def wave_timeline(fk, B, wl, dev, bf, stream, launches: int = 24, warm_launches:
     lo, hi = rel[:, :, :4], rel[:, :, 4:]
     return {
         "launches": launches,
+        "pool_layout": layout,
         "us_by_wave_index": by_wave,
         "span_us_median": round(float(np.median(span)), 2),
         "workgroup_end_us": {"p10": round(float(np.percentile(wg_end, 10)), 2),
@@ -823,7 +829,7 @@ def main():
         if "stage1_then_tiny_kernel" in med:
             res["floors"]["dependent_launch_after_stage1_us"] = us(med["stage1_then_tiny_kernel"] - s1_ms)
     if args.timeline:
-        res["wave_timeline"] = wave_timeline(fk, B, wl, dev, bf, stream)
+        res["wave_timeline"] = wave_timeline(fk, B, wl, dev, bf, stream, args.layout)
     if not args.no_model_step:
         res["model_step_48x40k"] = model_step_timing(fk, wl, dev, args, bf, stream)
     if not args.no_prefill:

@@ -128,15 +128,28 @@ struct Stage1 {
   static_assert(kSteps >= 1 && kSteps <= 4, "up to four steps in flight per wave");
 };
 
-template <int W>
+// Code loads, plain or non-temporal (NT: the line is not kept for reuse --
+// for a pool whose KV heads never share a line, where it streams the codes
+// from HBM faster).
+template <bool NT>
+__device__ __forceinline__ u32x4 load_code16(const uint8_t* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int W, bool NT>
 __device__ __forceinline__ void load_v_words(const uint8_t* p, uint32_t (&w)[W]) {
   if constexpr (W == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                       : *reinterpret_cast<const u32x2*>(p);
     w[0] = t.x;
     w[1] = t.y;
   } else {
     static_assert(W == 4, "8 or 16 bytes of V per key and lane");
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const u32x4 t = load_code16<NT>(p);
     w[0] = t.x;
     w[1] = t.y;
     w[2] = t.z;
@@ -144,7 +157,9 @@ __device__ __forceinline__ void load_v_words(const uint8_t* p, uint32_t (&w)[W])
   }
 }
 
-template <class C>
+// NTL: the codes are read with non-temporal loads (a pool whose KV heads never
+// share a 128-byte line).
+template <class C, bool NTL>
 __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kWavesPerEU))) void decode_stage1_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, uint32_t code_row_stride,
@@ -310,24 +325,28 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. Every code load of the group, in step order.
+    // 3. Every code load of the group, in step order; non-temporal (NTL)
+    //    when the pool's KV heads never share a line.
     u32x4 kr[kSteps][2][C::kKC];
     uint32_t vr[kSteps][8][C::kVW];
+    {
 #pragma unroll
-    for (int t = 0; t < kSteps; ++t) {
-      const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
-      const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
-      const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
+      for (int t = 0; t < kSteps; ++t) {
+        const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
+        const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
+        const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
 #pragma unroll
-      for (int c = 0; c < C::kKC; ++c) {
-        kr[t][0][c] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64 * c);
-        kr[t][1][c] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64 * c);
+        for (int c = 0; c < C::kKC; ++c) {
+          kr[t][0][c] = load_code16<NTL>(kbase + r0 + 64 * c);
+          kr[t][1][c] = load_code16<NTL>(kbase + r1 + 64 * c);
+        }
+        const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
+        const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
+        const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          load_v_words<C::kVW, NTL>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
       }
-      const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
-      const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
-      const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-      for (int r = 0; r < 8; ++r) load_v_words(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -754,7 +773,8 @@ hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const Deco
   const dim3 grid((unsigned)(8 * pool.n_kv_heads), (unsigned)((geo.n_split + 7) / 8), (unsigned)z);
   int g_shift = 0;
   while ((1 << g_shift) < sh.n_q_heads / pool.n_kv_heads) ++g_shift;
-  hipLaunchKernelGGL(decode_stage1_kernel<C>, grid, dim3(C::kBlock), 0, stream, pool.k_codes, pool.v_codes,
+  auto kernel = pool.line_rows ? decode_stage1_kernel<C, true> : decode_stage1_kernel<C, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(C::kBlock), 0, stream, pool.k_codes, pool.v_codes,
                      pool.k_scales, pool.v_scales, (uint32_t)pool.code_row_stride, (uint32_t)pool.scale_row_stride,
                      q, sh.n_q_heads, sh.n_qrows, g_shift, sh.row_table, sh.table_stride, sh.seq_lens, sh.max_seq_len,
                      geo.n_split, geo.chunk, ws.split_stride, qk_scale_log2, key_trim, sh.window, geo.n_col_groups,

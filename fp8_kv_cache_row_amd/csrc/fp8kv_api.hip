@@ -53,8 +53,10 @@ fp8kv_status check_pool(const fp8kv_pool_layer* p) {
 }
 
 PoolView view_of(const fp8kv_pool_layer* p) {
+  const bool line_rows = aligned(p->k_codes, 128) && aligned(p->v_codes, 128) && p->code_row_stride % 128 == 0 &&
+                         p->head_dim % 128 == 0;
   return PoolView{p->k_codes, p->v_codes, p->k_scales, p->v_scales, p->code_row_stride, p->scale_row_stride,
-                  p->n_kv_heads, p->head_dim, p->num_rows, p->code_format};
+                  p->n_kv_heads, p->head_dim, p->num_rows, p->code_format, line_rows};
 }
 
 // Per-device facts, queried once: gfx950 or not, and the compute-unit count.

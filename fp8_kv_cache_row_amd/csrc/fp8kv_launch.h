@@ -21,6 +21,11 @@ struct PoolView {
   int32_t head_dim;  // 128 or 256
   int64_t num_rows;
   int32_t format;    // CodeFormat: 0 E4M3FN, 1 INT8
+  // Every KV head's K and V code rows start on a 128-byte line and fill whole
+  // lines (bases and row stride multiples of 128 bytes): no two KV heads read
+  // the same line, so the decode kernels stream the codes with non-temporal
+  // loads.
+  bool line_rows;
 };
 
 // Decode launch geometry: each workgroup covers `chunk` consecutive keys of

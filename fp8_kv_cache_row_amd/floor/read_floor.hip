@@ -6,6 +6,8 @@
 //  * fp8kv_floor_read: a contiguous read of `bytes` bytes, 16 bytes per lane
 //    and eight loads in flight per lane, every loaded word folded into a
 //    checksum (stored only if it equals an unlikely value, so the loads stay).
+//  * Both use non-temporal loads (the lines are not kept for reuse), which
+//    read a cold buffer from HBM ~10 % faster than plain loads here.
 //  * fp8kv_floor_gather: whole row records of `record_bytes` bytes (at most
 //    2 KB) read through a row table -- every byte a page-size-1 reader of
 //    those rows must fetch, in table order, each record by consecutive lanes,
@@ -22,6 +24,12 @@ constexpr int kBlock = 512;
 constexpr int kUnroll = 8;
 constexpr uint32_t kNever = 0x9E3779B9u;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __global__ __launch_bounds__(kBlock) void read_contiguous(const uint4* __restrict__ p, int64_t n_vec,
                                                           uint32_t* __restrict__ sink) {
   int64_t i = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x;
@@ -32,7 +40,7 @@ __global__ __launch_bounds__(kBlock) void read_contiguous(const uint4* __restric
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t k = i + (int64_t)u * kBlock;
-      v[u] = k < n_vec ? p[k] : make_uint4(0, 0, 0, 0);
+      v[u] = k < n_vec ? load_nt(p + k) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -66,7 +74,7 @@ __global__ __launch_bounds__(kBlock) void read_records(const uint8_t* __restrict
 #pragma unroll
       for (int c = 0; c < kMaxChunks; ++c) {
         const int chunk = lane + 64 * c;
-        v[u][c] = (key_ok && chunk < rec_vec) ? rec[chunk] : make_uint4(0, 0, 0, 0);
+        v[u][c] = (key_ok && chunk < rec_vec) ? load_nt(rec + chunk) : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll

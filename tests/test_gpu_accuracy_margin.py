@@ -24,7 +24,7 @@ MARGIN = 0.7  # observed errors must stay below 0.7 x the tolerance
 
 def _step(case, fmt="e4m3"):
     """One fused step (quantize the new token + attention) and the oracle's."""
-    pool = build_pool(case, "interleaved", fmt)
+    pool = build_pool(case, "interleaved128", fmt)  # the benchmark's layout
     last = case.table[np.arange(case.table.shape[0]), case.seq_lens.astype(np.int64) - 1]
     slot = to_dev(np.ascontiguousarray(last, dtype=np.int32))
     out = fk.fp8kv_decode_attn_append(pool, to_dev_bf16(case.q), to_dev_bf16(case.new_k), to_dev_bf16(case.new_v),

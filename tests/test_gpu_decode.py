@@ -29,7 +29,7 @@ def _oracle_decode(case, pools=None, q=None, table=None, seq_lens=None):
                                    case.sm_scale, case.n_kv_heads)
 
 
-@pytest.mark.parametrize("layout", ["separate", "interleaved"])
+@pytest.mark.parametrize("layout", ["separate", "interleaved", "interleaved128"])
 def test_tiny_gqa8(layout):
     say(f"decode tiny GQA-8 256 rows, layout={layout}")
     case = wl.tiny_decode(0)
@@ -63,6 +63,24 @@ def test_layer_32k_interleaved_pool_matches_separate():
     case = wl.layer_decode(1, with_new_token=False)
     pool = build_pool(case, "interleaved")
     assert_close(bf16_to_f64(run_decode(pool, case)), _oracle_decode(case), "32K interleaved")
+
+
+def test_streaming_and_plain_code_loads_agree_bit_for_bit():
+    """Pools whose KV heads' code rows fill whole 128-byte lines (separate
+    arrays, records padded to 128 bytes) are read with non-temporal loads, the
+    1,056-byte records with plain ones; the arithmetic is the same, so the
+    outputs are identical, and both match the oracle."""
+    say("decode 32K: separate / interleaved128 (non-temporal loads) vs interleaved (plain loads)")
+    case = wl.layer_decode(3, with_new_token=False)
+    outs = {}
+    for layout in ("separate", "interleaved128", "interleaved"):
+        pool = build_pool(case, layout)
+        outs[layout] = run_decode(pool, case).cpu()
+        del pool
+        torch.cuda.empty_cache()
+    assert torch.equal(outs["separate"].view(torch.int16), outs["interleaved"].view(torch.int16))
+    assert torch.equal(outs["interleaved128"].view(torch.int16), outs["interleaved"].view(torch.int16))
+    assert_close(bf16_to_f64(outs["interleaved128"]), _oracle_decode(case), "32K interleaved128")
 
 
 @pytest.mark.parametrize("L", [0, 1, 2, 17, 31, 32, 33, 127, 129, 513, 1000, 4097])

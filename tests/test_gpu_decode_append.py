@@ -51,7 +51,7 @@ def _check_pool(pool, ref_pools, what):
         assert_bits_equal(a, b, f"{what}: {name}")
 
 
-@pytest.mark.parametrize("layout", ["separate", "interleaved"])
+@pytest.mark.parametrize("layout", ["separate", "interleaved", "interleaved128"])
 def test_append_32k_layer(layout):
     say(f"decode+append 32K, 32 q / 4 KV heads, layout={layout}")
     case = wl.layer_decode(0)

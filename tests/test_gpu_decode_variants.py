@@ -49,7 +49,7 @@ def _single(pool, case, max_splits=0, seq_lens=None):
 
 # ------------------------------------------------------------- D = 256 --
 
-@pytest.mark.parametrize("layout", ["separate", "interleaved"])
+@pytest.mark.parametrize("layout", ["separate", "interleaved", "interleaved128"])
 def test_d256_32k_layer_pool_bits_and_attention(layout):
     say(f"D=256 decode 32K, 32 q / 4 KV heads, layout={layout}")
     case = wl.layer_decode(0, head_dim=256, with_new_token=False)

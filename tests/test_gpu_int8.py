@@ -35,7 +35,7 @@ def _check_pool(pool, ref_pool, what):
 
 
 @pytest.mark.parametrize("D", [128, 256])
-@pytest.mark.parametrize("layout", ["separate", "interleaved"])
+@pytest.mark.parametrize("layout", ["separate", "interleaved", "interleaved128"])
 def test_int8_32k_layer(D, layout):
     say(f"INT8 decode 32K, D={D}, layout={layout}")
     case = wl.layer_decode(90, head_dim=D, with_new_token=False)
