@@ -110,6 +110,15 @@ typedef enum fp8kv_status {
  * aligned.  code_row_stride >= n_kv_heads * D and scale_row_stride >=
  * n_kv_heads.  Strides let the four arrays be separate allocations or
  * interleave inside one per-row record.
+ *
+ * When k_codes, v_codes and code_row_stride are also multiples of 128 bytes,
+ * every KV head's code rows fill whole 128-byte lines that no other KV head
+ * reads, and the decode calls read the codes with non-temporal loads: faster
+ * for a pool read from HBM (a model's layers, each read once per token),
+ * slower for one read over and over from the Infinity Cache.  A per-row
+ * record of 2 * n_kv_heads * (D + 4) bytes padded to a multiple of 128 (1,152
+ * bytes for 4 KV heads, D = 128) gets this; so do separate arrays with
+ * 128-byte-aligned bases.  Results are the same either way.
  */
 typedef struct fp8kv_pool_layer {
     uint8_t *k_codes;
