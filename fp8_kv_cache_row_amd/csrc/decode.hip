@@ -110,7 +110,12 @@ struct Stage1 {
   // 82 us, against 86 us for two 8-wave workgroups of one step per wave.
   static constexpr int kWaves = STREAM ? 4 : ((NT * D >= 512) ? 4 : kDecodeWaves);
   static constexpr int kBlock = kWaves * kWave;
-  static constexpr int kSteps = STREAM ? 2 : ((D == 128 || kWaves == 4) ? kDecodeTilesPerWave : 1);  // 32-key steps loaded at once
+  // 32-key steps loaded at once: two (a whole 512-key split in one group of
+  // the 8 waves), except at D = 256 for the several-row tiles and G = 1,
+  // whose registers hold one (one row's two steps at D = 256 need all 256,
+  // and at G = 1 the compiler spills two).
+  static constexpr int kSteps =
+      STREAM ? 2 : ((D == 128 || kWaves == 4 || (NT == 1 && !MULTI && G > 1)) ? kDecodeTilesPerWave : 1);
   static constexpr int kWavesPerEU = STREAM ? 3 : 1;  // minimum waves per SIMD the registers allow
   static_assert(!STREAM || (D == 128 && NT == 1 && !MULTI && !WINDOW), "streaming shape: one row, D = 128");
   static constexpr int kGroupKeys = kSteps * kDecodeTileKeys;
