@@ -29,11 +29,21 @@
 // Pipelining: the tiles are double-buffered, each buffer its own LDS object;
 // the loads of tile t+1 are issued right after the barrier that opens tile t,
 // so one barrier per tile suffices and the load latency hides behind the MFMA
-// work.  Online softmax in log2
-// units with a lazy maximum (O and l are rescaled only when a sub-step's
-// maximum exceeds the running one by more than 8), so the accumulators are
-// normally touched by the MFMA alone; the row sums are an MFMA of P against a
-// block of ones, which also normalizes by exactly the bf16 p that P*V uses.  Workgroups with the most keys (the last
+// work.
+//
+// Softmax in log2 units against a fixed reference per query row: the maximum
+// of the row's first 32 keys (key 0 is among them and every row sees it).
+// p = 2^(s - ref) is never rescaled, so between the first sub-step and the
+// end the accumulators are touched by the MFMAs alone -- no rescale branch,
+// and none of the register copies the compiler places at such a branch's
+// join (measured: 1.46 against 1.70 ms for the 8K + 8K operator).  Any key
+// far enough above the reference to overflow p, the row sum or O leaves a
+// non-finite value behind (inf and NaN absorb), so a workgroup whose l and O
+// are finite got the result a running maximum gives, up to rounding; one that
+// is not runs its tiles again with a lazy running maximum (O and l rescaled
+// when a sub-step's maximum passes the running one by more than 8).  The row
+// sums are an MFMA of P against a block of ones, which also normalizes by
+// exactly the bf16 p that P*V uses.  Workgroups with the most keys (the last
 // query tokens) are launched first.
 #include <math.h>
 
@@ -46,7 +56,7 @@ namespace fp8kv {
 namespace {
 
 // 32 query rows per wave (two 16-row blocks share every K/V operand read),
-// 256 rows per workgroup, two waves per SIMD (250 registers, no spills).
+// 256 rows per workgroup, two waves per SIMD (under 256 registers, no spills).
 // Measured on the 8K + 8K operator against 16 rows per wave at four waves
 // per SIMD: 2.06 vs 2.13-2.20 ms.
 #ifndef FP8KV_PREFILL_ROW_BLOCKS
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
     for (int kk = 0; kk < 4; ++kk) qb[cb][kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32 * kk));
   }
 
-  float m_run[kRowBlocks];  // lazy running max of row n (log2 units)
+  float m_run[kRowBlocks];  // softmax reference of row n (log2 units)
   f32x4 o[kRowBlocks][8];   // O[row 4j+i][d = 16nb + n]
   f32x4 lsum[kRowBlocks];   // row sums of bf16(p) (an MFMA against ones): row 4j+i in slot i
 #pragma unroll
@@ -141,7 +151,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const bf16x8 ones = u4_as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  // Four registers of bf16 ones for the row-sum MFMA.  The empty asm hides
+  // that the four are equal; otherwise the compiler keeps one and rebuilds the
+  // other three with a move each before every row-sum MFMA.
+  uint4 ones_u = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+  asm volatile("" : "+v"(ones_u.x), "+v"(ones_u.y), "+v"(ones_u.z), "+v"(ones_u.w));
+  const bf16x8 ones = u4_as_bf16x8(ones_u);
 
   const int64_t kv_row = (int64_t)n_kv_heads * kHeadDim;  // elements between tokens
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
@@ -204,8 +219,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
     for (int nb = 0; nb < 8; ++nb) vofs[nb] = vchunk_at(ka, 2 * nb + ((n & 3) >> 1)) + ((n & 1) << 3);
   }
 
-  auto tile_body = [&](auto bufc, int tile) {
+  // One 64-key tile.  MODE 0: softmax against the fixed per-row reference
+  // m_run (no rescale); MODE 1: the same, with m_run set from the first
+  // sub-step's row maximum (the first tile); MODE 2: lazy running maximum
+  // (O and l rescaled when a sub-step's maximum passes m_run + 8).
+  auto tile_body = [&](auto bufc, auto modec, int tile) {
     constexpr int buf = decltype(bufc)::value;
+    constexpr int MODE = decltype(modec)::value;
     const int u0 = tile * kTileKeys;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `tile` have landed (vmcnt 0)
     __syncthreads();                // every wave's have; the other buffer is free
@@ -253,30 +273,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
         float sc[8] = {s[0][cb][0], s[0][cb][1], s[0][cb][2], s[0][cb][3],
                        s[1][cb][0], s[1][cb][1], s[1][cb][2], s[1][cb][3]};
         if (need_mask) {
-          const int limit = min(n_prefix + row_tok[cb], n_keys - 1);  // last visible key of this row
+          // slot e holds key u0 + 32st + 4j + (e & 3) + 16 (e >> 2); it is
+          // visible when that is at most the row's last visible key
+          const int rel = min(n_prefix + row_tok[cb], n_keys - 1) - (u0 + 32 * st) - 4 * j;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            sc[e] = (u0 + 32 * st + 16 * (e >> 2) + 4 * j + (e & 3) <= limit) ? sc[e] : -INFINITY;
+          for (int e = 0; e < 8; ++e) sc[e] = ((e & 3) + 16 * (e >> 2) <= rel) ? sc[e] : -INFINITY;
         }
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = max_over_row_groups(tmax);
-        tmax *= qk_scale_log2;  // the scale is positive: max commutes with it
-        // Lazy maximum.  The first sub-step holds key 0, which every row
-        // sees, so m_run is finite from then on.  A sub-step whose keys are
-        // all masked for a row has tmax = -inf and p = 0.
-        if (__any(tmax > m_run[cb] + kLazyMaxSlack)) {
-          const float m_new = fmaxf(m_run[cb], tmax);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 on the first sub-step
-          m_run[cb] = m_new;
-          float ai[4];
+        if (MODE == 2 || (MODE == 1 && st == 0)) {
+          float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+          tmax = max_over_row_groups(tmax);
+          tmax *= qk_scale_log2;  // the scale is positive: max commutes with it
+          if (MODE == 1) {
+            // Key 0 is in this sub-step and every row sees it: finite.
+            m_run[cb] = tmax;
+          } else if (__any(tmax > m_run[cb] + kLazyMaxSlack)) {
+            // Lazy maximum.  The first sub-step holds key 0, which every row
+            // sees, so m_run is finite from then on.  A sub-step whose keys
+            // are all masked for a row has tmax = -inf and p = 0.
+            const float m_new = fmaxf(m_run[cb], tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 on the first sub-step
+            m_run[cb] = m_new;
+            float ai[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+            for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lsum[cb][i] *= ai[i];
+            for (int i = 0; i < 4; ++i) lsum[cb][i] *= ai[i];
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb)
+            for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[cb][nb][i] *= ai[i];
+              for (int i = 0; i < 4; ++i) o[cb][nb][i] *= ai[i];
+          }
         }
         const float neg_m = -m_run[cb];
         float p[8];
@@ -295,13 +321,45 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
       }
     }
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
-  fetch(std::integral_constant<int, 0>{}, 0);
-  // The tile loop is unrolled by the buffer parity so that LDS offsets are
-  // compile-time constants.
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    tile_body(std::integral_constant<int, 0>{}, tile);
-    if (tile + 1 < n_tiles) tile_body(std::integral_constant<int, 1>{}, tile + 1);
+  // Fixed reference: m_run is the maximum of each row's first 32 keys, and
+  // no later key rescales anything, so the accumulators see only the MFMAs.
+  fetch(B0{}, 0);
+  tile_body(B0{}, std::integral_constant<int, 1>{}, 0);
+  for (int tile = 1; tile < n_tiles; tile += 2) {
+    tile_body(B1{}, B0{}, tile);
+    if (tile + 1 < n_tiles) tile_body(B0{}, B0{}, tile + 1);
+  }
+  // A later key can exceed the reference by enough that some p (<= l) or a
+  // partial sum of O overflows; non-finite results are kept as such (inf
+  // absorbs), so finite l and O mean that nothing overflowed and the result
+  // is as exact as with a running maximum.  Otherwise the workgroup runs the
+  // tiles again with the lazy running maximum.
+  uint32_t worst = 0;
+#pragma unroll
+  for (int cb = 0; cb < kRowBlocks; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      worst = max(worst, __float_as_uint(lsum[cb][i]) & 0x7fffffffu);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) worst = max(worst, __float_as_uint(o[cb][nb][i]) & 0x7fffffffu);
+    }
+  }
+  if (__syncthreads_or(worst >= 0x7f800000u)) {
+#pragma unroll
+    for (int mb = 0; mb < kRowBlocks; ++mb) {
+      m_run[mb] = -INFINITY;
+      lsum[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    fetch(B0{}, 0);
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      tile_body(B0{}, std::integral_constant<int, 2>{}, tile);
+      if (tile + 1 < n_tiles) tile_body(B1{}, std::integral_constant<int, 2>{}, tile + 1);
+    }
   }
 
   // ---- normalize and store: lane (n, j) holds rows 4j+i of block cb, d = 16nb + n

@@ -100,6 +100,29 @@ def test_chunked_prefill_8k_prefix_8k_chunk():
     assert_close(got, ref, "8K+8K sampled")
 
 
+@pytest.mark.parametrize("where,k0", [("chunk", 1024.0), ("prefix", 1024.0), ("chunk", 196.0)])
+def test_prefill_key_far_above_each_rows_first_keys(where, k0):
+    """Every query has q[0] = 4 and one key has k[0] = k0, so that key's score
+    lies ~4 k0 / sqrt(128) log2 e above the scores of a row's first 32 keys
+    (the kernel's softmax reference): ~520 log2 units for k0 = 1024, past
+    where p = 2^(s - ref) overflows, so every workgroup that sees the key
+    (the chunk key: the tokens from it on; a prefix key: all) must fall back
+    to a running maximum, while the others keep the fixed reference; ~100
+    units for k0 = 196, large but finite p on the fixed reference.  Checked
+    on every row against the fp64 oracle."""
+    say(f"prefill with one key far above the first keys ({where}, k[0] = {k0})")
+    case = wl.chunked_prefill(seed=21, n_prefix=600, n_chunk=300)
+    case.q[:, :, 0] = wl.bf16_bits(np.float32([4.0]))[0]
+    big = wl.bf16_bits(np.float32([k0]))[0]
+    if where == "chunk":
+        case.k_cur[200, :, 0] = big
+    else:
+        case.prefix_k[450, :, 0] = big
+    got, ref = _run(case)
+    assert np.isfinite(got).all()
+    assert_close(got, ref, f"one key far above ({where}, {k0})")
+
+
 @pytest.mark.parametrize("P,T,Hq,Hkv", [(0, 37, 32, 4), (100, 37, 32, 4), (257, 130, 16, 4), (1000, 300, 8, 8)])
 def test_small_prefills_int8_pool(P, T, Hq, Hkv):
     say(f"prefill over an INT8 pool P={P} T={T} Hq={Hq} Hkv={Hkv}")
