@@ -28,10 +28,18 @@
 //    column maximum needs two cross-lane steps, and those 8 keys are exactly
 //    the k-slots this lane feeds to the P*V MFMA, so P never moves between
 //    lanes.  The per-row K scale and the softmax scale multiply the score tile
-//    after the MFMA; the per-row V scale is folded into P.
-//  * Online softmax in log2 units with a lazy maximum: the running maximum
-//    moves (and O is rescaled) only when a step's maximum exceeds it by more
-//    than 8, so p stays below 2^8 and most steps skip the rescale.
+//    after the MFMA (one FMA with the reference); the per-row V scale is
+//    folded into P.
+//  * Softmax in log2 units against a fixed reference per column: the maximum
+//    of the column's first visible step.  p = 2^(s - ref) is never rescaled,
+//    so after that step there is no maximum and no rescale branch (whose
+//    join costs register copies of O) -- 9.7-9.8 against 10.1-10.2 us for
+//    the 32K stage 1.  A key far enough above the reference overflows p, l
+//    or O into inf or NaN, which then stays; a wave whose l and O are not
+//    finite sums its keys again with a lazy running maximum (moved, with O
+//    rescaled, only when a step's maximum passes it by more than 8).  At head
+//    dim 256 the registers leave no room for the second pass's code and the
+//    lazy maximum is the only one.
 //  * Waves merge through LDS; one (o, log2-sum-exp) partial per split.
 //  * The grid places the KV heads of one split on one XCD, next to each other
 //    in dispatch order, so they share that XCD's L2 lines of the table and of
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
   const int32_t* trow = table + (int64_t)b * table_stride;
   int key_begin = split * chunk;
   int key_bound = min(key_begin + chunk, max_seq_len);  // host-side bound on this split's keys
-  int k0 = key_begin + wave * kGroupKeys;
+  int k_first = key_begin + wave * kGroupKeys;  // the wave's first key
   int rows_in[kRowSlots];
   if constexpr (!C::WINDOW) {
     // Row indices of the first group, read up to the host-side bound before
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
     // compiler from sinking the read below the length's wait.
 #pragma unroll
     for (int c = 0; c < kRowSlots; ++c)
-      rows_in[c] = (int)min((uint32_t)trow[max(min(k0 + c * kWave + lane, key_bound - 1), 0)], max_row);
+      rows_in[c] = (int)min((uint32_t)trow[max(min(k_first + c * kWave + lane, key_bound - 1), 0)], max_row);
 #pragma unroll
     for (int c = 0; c < kRowSlots; ++c) s_rows[wave][c * kWave + lane] = rows_in[c];
     FP8KV_MARK(1, true);
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
     last_lo = max(0, len - window);
     key_begin = first_lo + split * chunk;
     key_bound = min(key_begin + chunk, len);
-    k0 = key_begin + wave * kGroupKeys;
+    k_first = key_begin + wave * kGroupKeys;
   }
   const int key_end = min(key_begin + chunk, len - key_trim);  // keys this split covers
   if constexpr (C::STREAM) {
@@ -297,168 +305,241 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
   const uint8_t* kbase = k_codes + g * D + 16 * j;
   const uint8_t* vbase = v_codes + g * D + (D / 16) * n;
 
-  float m_run[NT], l_part[NT];  // running (lazy) max in log2 units, and the sum of p, of column n
-  f32x4 o[NT][kNB];             // O[column 4j+i][d = kNB*n + nb]
+  // Softmax reference of column n in log2 units (see run_groups), the sum of
+  // p, and O[column 4j+i][d = kNB*n + nb].
+  float m_run[NT], l_part[NT];
+  f32x4 o[NT][kNB];
+  auto reset = [&]() {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    m_run[t] = kNoMax;
-    l_part[t] = 0.0f;
+    for (int t = 0; t < NT; ++t) {
+      m_run[t] = kNoMax;
+      l_part[t] = 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+      for (int nb = 0; nb < kNB; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  reset();
 
-  for (bool first = true; k0 < key_end; k0 += kWaves * kGroupKeys, first = false) {
-    // 1. Row indices of the group's keys through LDS (per-wave region).
-    if (C::WINDOW || !first) {
+  // The wave's groups of keys.  LAZY = false: p = 2^(s - ref) against a fixed
+  // reference per column, the maximum over its visible keys of the first of
+  // the wave's steps in which it sees any, never rescaled -- no rescale
+  // branch, and no maximum once every column has its reference.
+  // LAZY = true: a running maximum, moved (with O and l rescaled) only when a
+  // step's maximum passes it by more than kLazyMaxSlack.  reread: the first
+  // group's row indices are read again (a second pass).
+  auto run_groups = [&](auto lazyc, bool reread) {
+    constexpr bool LAZY = decltype(lazyc)::value;
+    int k0 = k_first;
+    for (bool first = true; k0 < key_end; k0 += kWaves * kGroupKeys, first = false) {
+      // 1. Row indices of the group's keys through LDS (per-wave region).
+      if (C::WINDOW || !first || reread) {
+#pragma unroll
+        for (int c = 0; c < kRowSlots; ++c) {
+          rows_in[c] = (int)min((uint32_t)trow[max(min(k0 + c * kWave + lane, key_bound - 1), 0)], max_row);
+          s_rows[wave][c * kWave + lane] = rows_in[c];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+
+      // 2. Scale loads, issued before the code loads: loads complete in issue
+      //    order, so writing the scales to LDS waits for them alone.
+      float ksc[kRowSlots], vsc[kRowSlots];
 #pragma unroll
       for (int c = 0; c < kRowSlots; ++c) {
-        rows_in[c] = (int)min((uint32_t)trow[max(min(k0 + c * kWave + lane, key_bound - 1), 0)], max_row);
-        s_rows[wave][c * kWave + lane] = rows_in[c];
+        const uint32_t row = (uint32_t)rows_in[c];
+        const uint64_t off = (uint64_t)row * scale_row_stride + g;
+        ksc[c] = k_scales[off];
+        vsc[c] = v_scales[off];
       }
-    }
-    __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 
-    // 2. Scale loads, issued before the code loads: loads complete in issue
-    //    order, so writing the scales to LDS waits for them alone.
-    float ksc[kRowSlots], vsc[kRowSlots];
+      // 3. Every code load of the group, in step order; non-temporal (NTL)
+      //    when the pool's KV heads never share a line.
+      u32x4 kr[kSteps][2][C::kKC];
+      uint32_t vr[kSteps][8][C::kVW];
+      {
 #pragma unroll
-    for (int c = 0; c < kRowSlots; ++c) {
-      const uint32_t row = (uint32_t)rows_in[c];
-      const uint64_t off = (uint64_t)row * scale_row_stride + g;
-      ksc[c] = k_scales[off];
-      vsc[c] = v_scales[off];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 3. Every code load of the group, in step order; non-temporal (NTL)
-    //    when the pool's KV heads never share a line.
-    u32x4 kr[kSteps][2][C::kKC];
-    uint32_t vr[kSteps][8][C::kVW];
-    {
+        for (int t = 0; t < kSteps; ++t) {
+          const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
+          const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
+          const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
 #pragma unroll
-      for (int t = 0; t < kSteps; ++t) {
-        const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
-        const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
-        const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
+          for (int c = 0; c < C::kKC; ++c) {
+            kr[t][0][c] = load_code16<NTL>(kbase + r0 + 64 * c);
+            kr[t][1][c] = load_code16<NTL>(kbase + r1 + 64 * c);
+          }
+          const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
+          const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
+          const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-        for (int c = 0; c < C::kKC; ++c) {
-          kr[t][0][c] = load_code16<NTL>(kbase + r0 + 64 * c);
-          kr[t][1][c] = load_code16<NTL>(kbase + r1 + 64 * c);
+          for (int r = 0; r < 8; ++r)
+            load_v_words<C::kVW, NTL>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
         }
-        const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
-        const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
-        const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          load_v_words<C::kVW, NTL>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // (With the fixed reference the K scale carries the softmax scale.)
 #pragma unroll
-    for (int c = 0; c < kRowSlots; ++c) s_sc[wave][c * kWave + lane] = make_float2(ksc[c], vsc[c]);
-    __builtin_amdgcn_wave_barrier();
-    FP8KV_MARK(2, first);
-    // Wave-uniform: only groups that reach past the first row's end, or start
-    // below the last row's window start, need per-column masks.
-    const bool masked = (k0 + kGroupKeys > min(first_end, key_end)) || (C::WINDOW && k0 < last_lo);
+      for (int c = 0; c < kRowSlots; ++c) s_sc[wave][c * kWave + lane] = make_float2(LAZY ? ksc[c] : ksc[c] * qk_scale_log2, vsc[c]);
+      __builtin_amdgcn_wave_barrier();
+      FP8KV_MARK(2, first);
+      // Wave-uniform: only groups that reach past the first row's end, or start
+      // below the last row's window start, need per-column masks.
+      const bool masked = (k0 + kGroupKeys > min(first_end, key_end)) || (C::WINDOW && k0 < last_lo);
 
-    // One 32-key step; st is a compile-time constant so kr/vr stay in
-    // registers.  Steps are not skipped (no branch the loads could sink
-    // into); keys a column does not see are masked out of its softmax.
-    auto step = [&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      const int t0 = k0 + st * kDecodeTileKeys;
-      // S^T = K * Q^T: lane (n, j) holds chunks j + 4c of keys n (block 0)
-      // and 16+n (block 1).  Each K operand is widened once for all tiles.
-      f32x4 s0[NT], s1[NT];
+      // One 32-key step; st is a compile-time constant so kr/vr stay in
+      // registers.  Steps are not skipped (no branch the loads could sink
+      // into); keys a column does not see are masked out of its softmax.
+      auto step = [&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        const int t0 = k0 + st * kDecodeTileKeys;
+        // S^T = K * Q^T: lane (n, j) holds chunks j + 4c of keys n (block 0)
+        // and 16+n (block 1).  Each K operand is widened once for all tiles.
+        f32x4 s0[NT], s1[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s0[t] = s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) s0[t] = s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < C::kQK; ++kk) {
-        const u32x4 w0 = kr[st][0][kk >> 1], w1 = kr[st][1][kk >> 1];
-        const bf16x8 a0 = (kk & 1) ? C::Code::widen8(w0.z, w0.w) : C::Code::widen8(w0.x, w0.y);
-        const bf16x8 a1 = (kk & 1) ? C::Code::widen8(w1.z, w1.w) : C::Code::widen8(w1.x, w1.y);
+        for (int kk = 0; kk < C::kQK; ++kk) {
+          const u32x4 w0 = kr[st][0][kk >> 1], w1 = kr[st][1][kk >> 1];
+          const bf16x8 a0 = (kk & 1) ? C::Code::widen8(w0.z, w0.w) : C::Code::widen8(w0.x, w0.y);
+          const bf16x8 a1 = (kk & 1) ? C::Code::widen8(w1.z, w1.w) : C::Code::widen8(w1.x, w1.y);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            s0[t] = mfma16x16x32(a0, qb[t][kk], s0[t]);
+            s1[t] = mfma16x16x32(a1, qb[t][kk], s1[t]);
+          }
+        }
+        const float2* scp = &s_sc[wave][st * kDecodeTileKeys];
+        const float4 c01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
+        const float4 c23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
+        const float4 c45 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j]);
+        const float4 c67 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j + 2]);
+
+        bf16x8 pa[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          s0[t] = mfma16x16x32(a0, qb[t][kk], s0[t]);
-          s1[t] = mfma16x16x32(a1, qb[t][kk], s1[t]);
+          // Scores in log2 units for column n, keys step_key(j, r); keys the
+          // column does not see get -inf.
+          const float raw[8] = {s0[t][0], s0[t][1], s0[t][2], s0[t][3], s1[t][0], s1[t][1], s1[t][2], s1[t][3]};
+          const float kq[8] = {c01.x, c01.z, c23.x, c23.z, c45.x, c45.z, c67.x, c67.z};
+          auto mask = [&](float (&x)[8]) {
+            if (masked) {
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const int key = t0 + step_key(j, r);
+                const bool vis = key < cend[t] && (!C::WINDOW || key >= clo[t]);
+                x[r] = vis ? x[r] : -INFINITY;
+              }
+            }
+          };
+          auto column_max = [&](const float (&x)[8]) {
+            const float m = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            return max_over_row_groups(m);
+          };
+          float p[8];
+          if constexpr (LAZY) {
+            float sv[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) sv[r] = raw[r] * kq[r] * qk_scale_log2;
+            mask(sv);
+            const float tmax = column_max(sv);
+            // Lazy maximum: move it (and rescale O and l) only when this step's
+            // maximum exceeds it by more than the slack; otherwise p <= 2^slack.
+            // A column with no visible key keeps m_run = kNoMax and gets p = 0.
+            if (__any(tmax > m_run[t] + kLazyMaxSlack)) {
+              const float m_new = fmaxf(m_run[t], tmax);
+              const float alpha = fast_exp2(m_run[t] - m_new);
+              m_run[t] = m_new;
+              l_part[t] *= alpha;
+              float ai[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+              for (int nb = 0; nb < kNB; ++nb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[t][nb][i] *= ai[i];
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) p[r] = fast_exp2(sv[r] - m_run[t]);
+          } else {
+            if (__any(m_run[t] == kNoMax)) {
+              // A column without a reference takes this step's maximum over
+              // its visible keys (it keeps kNoMax if it sees none); its O and l
+              // are still zero.
+              float sv[8];
+#pragma unroll
+              for (int r = 0; r < 8; ++r) sv[r] = raw[r] * kq[r];
+              mask(sv);
+              const float tmax = column_max(sv);
+              m_run[t] = (m_run[t] == kNoMax) ? fmaxf(tmax, kNoMax) : m_run[t];
+            }
+            float x[8];  // score - reference
+#pragma unroll
+            for (int r = 0; r < 8; ++r) x[r] = fmaf(raw[r], kq[r], -m_run[t]);
+            mask(x);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r]);
+          }
+          l_part[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          // P' = p * v_scale as the bf16 A operand (row = column n, k-slots = keys).
+          const uint4 pu = make_uint4(f32x2_to_bf16x2(p[0] * c01.y, p[1] * c01.w), f32x2_to_bf16x2(p[2] * c23.y, p[3] * c23.w),
+                                      f32x2_to_bf16x2(p[4] * c45.y, p[5] * c45.w), f32x2_to_bf16x2(p[6] * c67.y, p[7] * c67.w));
+          pa[t] = u4_as_bf16x8(pu);
         }
-      }
-      const float2* scp = &s_sc[wave][st * kDecodeTileKeys];
-      const float4 c01 = *reinterpret_cast<const float4*>(&scp[4 * j]);
-      const float4 c23 = *reinterpret_cast<const float4*>(&scp[4 * j + 2]);
-      const float4 c45 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j]);
-      const float4 c67 = *reinterpret_cast<const float4*>(&scp[16 + 4 * j + 2]);
 
-      bf16x8 pa[NT];
+        // 4. V operand for column block nb: byte nb of each key's D/16 bytes,
+        //    i.e. V[key][d = kNB*n + nb] for the lane's 8 keys (byte-transposed
+        //    in registers), shared by all tiles.
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        // Scores in log2 units for column n, keys step_key(j, r).
-        float sv[8] = {s0[t][0] * c01.x, s0[t][1] * c01.z, s0[t][2] * c23.x, s0[t][3] * c23.z,
-                       s1[t][0] * c45.x, s1[t][1] * c45.z, s1[t][2] * c67.x, s1[t][3] * c67.z};
+        for (int w = 0; w < C::kVW; ++w) {
+          uint32_t lo[4], hi[4];
+          transpose4x4_bytes(vr[st][0][w], vr[st][1][w], vr[st][2][w], vr[st][3][w], lo[0], lo[1], lo[2], lo[3]);
+          transpose4x4_bytes(vr[st][4][w], vr[st][5][w], vr[st][6][w], vr[st][7][w], hi[0], hi[1], hi[2], hi[3]);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) sv[r] *= qk_scale_log2;
-        if (masked) {
+          for (int e = 0; e < 4; ++e) {
+            const bf16x8 vb = C::Code::widen8(lo[e], hi[e]);
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int key = t0 + step_key(j, r);
-            const bool vis = key < cend[t] && (!C::WINDOW || key >= clo[t]);
-            sv[r] = vis ? sv[r] : -INFINITY;
+            for (int t = 0; t < NT; ++t) o[t][4 * w + e] = mfma16x16x32(pa[t], vb, o[t][4 * w + e]);
           }
         }
-        float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        tmax = max_over_row_groups(tmax);
-
-        // Lazy maximum: move it (and rescale O and l) only when this step's
-        // maximum exceeds it by more than the slack; otherwise p <= 2^slack.
-        // A column with no visible key keeps m_run = kNoMax and gets p = 0.
-        if (__any(tmax > m_run[t] + kLazyMaxSlack)) {
-          const float m_new = fmaxf(m_run[t], tmax);
-          const float alpha = fast_exp2(m_run[t] - m_new);
-          m_run[t] = m_new;
-          l_part[t] *= alpha;
-          float ai[4];
+      };
+      step(std::integral_constant<int, 0>{});
+      FP8KV_MARK(3, first);
+      if constexpr (kSteps > 1) step(std::integral_constant<int, 1>{});
+      if constexpr (kSteps > 2) step(std::integral_constant<int, 2>{});
+      if constexpr (kSteps > 3) step(std::integral_constant<int, 3>{});
+      __builtin_amdgcn_wave_barrier();  // this group's LDS is consumed before the next overwrites it
+    }
+  };
+  if constexpr (D == 256) {
+    // The registers are full at D = 256: a second pass's code would spill.
+    run_groups(std::true_type{}, false);
+  } else {
+    run_groups(std::false_type{}, false);
+    // A key far enough above the reference overflows p, l or O and leaves a
+    // non-finite value (inf and NaN absorb); finite l and O mean the result
+    // is a running maximum's, up to rounding.  Otherwise the wave's keys are
+    // read and summed again with the running maximum.
+    // One sum over l and O is finite exactly when they all are, or else
+    // overflows itself, which only sends the wave round again.
+    float total = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+    for (int t = 0; t < NT; ++t) {
+      total += l_part[t];
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) {
+      for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[t][nb][i] *= ai[i];
-          }
-        }
-
-        float p[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) p[r] = fast_exp2(sv[r] - m_run[t]);
-        l_part[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        // P' = p * v_scale as the bf16 A operand (row = column n, k-slots = keys).
-        const uint4 pu = make_uint4(f32x2_to_bf16x2(p[0] * c01.y, p[1] * c01.w), f32x2_to_bf16x2(p[2] * c23.y, p[3] * c23.w),
-                                    f32x2_to_bf16x2(p[4] * c45.y, p[5] * c45.w), f32x2_to_bf16x2(p[6] * c67.y, p[7] * c67.w));
-        pa[t] = u4_as_bf16x8(pu);
-      }
-
-      // 4. V operand for column block nb: byte nb of each key's D/16 bytes,
-      //    i.e. V[key][d = kNB*n + nb] for the lane's 8 keys (byte-transposed
-      //    in registers), shared by all tiles.
-#pragma unroll
-      for (int w = 0; w < C::kVW; ++w) {
-        uint32_t lo[4], hi[4];
-        transpose4x4_bytes(vr[st][0][w], vr[st][1][w], vr[st][2][w], vr[st][3][w], lo[0], lo[1], lo[2], lo[3]);
-        transpose4x4_bytes(vr[st][4][w], vr[st][5][w], vr[st][6][w], vr[st][7][w], hi[0], hi[1], hi[2], hi[3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x8 vb = C::Code::widen8(lo[e], hi[e]);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) o[t][4 * w + e] = mfma16x16x32(pa[t], vb, o[t][4 * w + e]);
-        }
-      }
-    };
-    step(std::integral_constant<int, 0>{});
-    FP8KV_MARK(3, first);
-    if constexpr (kSteps > 1) step(std::integral_constant<int, 1>{});
-    if constexpr (kSteps > 2) step(std::integral_constant<int, 2>{});
-    if constexpr (kSteps > 3) step(std::integral_constant<int, 3>{});
-    __builtin_amdgcn_wave_barrier();  // this group's LDS is consumed before the next overwrites it
+        for (int i = 0; i < 4; ++i) total += o[t][nb][i];
+    }
+    // The test is on the bits, out of the compiler's sight: as a floating-
+    // point class test it could be folded away for NaN (the build assumes no
+    // NaN operands), and inf * 0 in the MFMAs makes NaN from an overflow.
+    uint32_t total_bits = __float_as_uint(total);
+    asm volatile("" : "+v"(total_bits));
+    if (__any((total_bits & 0x7fffffffu) >= 0x7f800000u)) {
+      reset();
+      run_groups(std::true_type{}, true);
+    }
   }
   FP8KV_MARK(4, true);
 

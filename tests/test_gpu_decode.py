@@ -195,6 +195,39 @@ def test_batched_16_requests_gqa4():
             assert_close(out[b], ref[b], f"  request {b} (L={case.seq_lens[b]})")
 
 
+@pytest.mark.parametrize("kind", ["layer", "batch"])
+@pytest.mark.parametrize("k0", [1024.0, 196.0])
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+def test_key_far_above_a_waves_first_keys(kind, k0, fmt):
+    """Every query has q[0] = 4 and a few keys have k[0] = k0, each placed in
+    the second 32-key step of a wave (positions 40 and 2,600 of every request
+    long enough), so it scores ~4 k0 / sqrt(128) log2 e above the keys of the
+    wave's first step, the kernel's softmax reference: ~520 log2 units for
+    k0 = 1024, where p = 2^(s - ref) overflows and those waves must sum their
+    keys again with a running maximum; ~100 for k0 = 196, a large but finite
+    p on the fixed reference.  The one-layer case runs the 8-wave shape, the
+    batch the streaming one; against the fp64 oracle, every request."""
+    say(f"decode with a key far above its wave's first keys ({kind}, k[0] = {k0}, {fmt})")
+    if kind == "layer":
+        case = wl.layer_decode(4, ctx=6000, pool_rows=6100, with_new_token=False)
+    else:
+        case = wl.batched_decode(4, n_req=6, lo=1024, hi=6000)
+    case.q[..., 0] = wl.bf16_bits(np.float32([4.0]))[0]
+    big = wl.bf16_bits(np.float32([k0]))[0]
+    for b in range(case.batch):
+        for pos in (40, 2600):
+            if pos < case.seq_lens[b]:
+                case.k_rows[case.table[b, pos], :, 0] = big
+    pool = build_pool(case, fmt=fmt)
+    kc, vc, ks, vs = oracle_pool(case, fmt)
+    ref = oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale,
+                                  case.n_kv_heads, fmt=fmt)
+    out = bf16_to_f64(run_decode(pool, case))
+    assert np.isfinite(out).all()
+    for b in range(case.batch):
+        assert_close(out[b], ref[b], f"{kind} request {b} (L={case.seq_lens[b]})")
+
+
 def test_model_step_48_layers_40k():
     """48 layers x (quantize the new token's K/V into slot table[39999], then
     decode over 40,000 rows); the pool holds 40,290 rows per layer."""
