@@ -488,16 +488,24 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
         }
 
         // 4. V operand for column block nb: byte nb of each key's D/16 bytes,
-        //    i.e. V[key][d = kNB*n + nb] for the lane's 8 keys (byte-transposed
-        //    in registers), shared by all tiles.
+        //    i.e. V[key][d = kNB*n + nb] for the lane's 8 keys, shared by all
+        //    tiles.
 #pragma unroll
         for (int w = 0; w < C::kVW; ++w) {
-          uint32_t lo[4], hi[4];
-          transpose4x4_bytes(vr[st][0][w], vr[st][1][w], vr[st][2][w], vr[st][3][w], lo[0], lo[1], lo[2], lo[3]);
-          transpose4x4_bytes(vr[st][4][w], vr[st][5][w], vr[st][6][w], vr[st][7][w], hi[0], hi[1], hi[2], hi[3]);
+          // pr[q][h]: keys 2q and 2q+1 at channels 4w + 2h and 4w + 2h + 1,
+          // interleaved -- one byte permute per dword, and the widening
+          // convert picks the channel's half.
+          uint32_t pr[4][2];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pr[q][0] = __builtin_amdgcn_perm(vr[st][2 * q + 1][w], vr[st][2 * q][w], 0x05010400u);
+            pr[q][1] = __builtin_amdgcn_perm(vr[st][2 * q + 1][w], vr[st][2 * q][w], 0x07030602u);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bf16x8 vb = C::Code::widen8(lo[e], hi[e]);
+            const int h = e >> 1;
+            const bf16x8 vb = (e & 1) ? C::Code::template widen_pairs<true>(pr[0][h], pr[1][h], pr[2][h], pr[3][h])
+                                      : C::Code::template widen_pairs<false>(pr[0][h], pr[1][h], pr[2][h], pr[3][h]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) o[t][4 * w + e] = mfma16x16x32(pa[t], vb, o[t][4 * w + e]);
           }

@@ -104,6 +104,14 @@ struct Codec<kE4M3> {
     return f32x2_to_fp8x2<HI>(a, b, old);
   }
   static __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) { return fp8x8_to_bf16x8(lo, hi); }
+  // Four dwords of two keys' codes at two channels each ([a c b d]: key 0 and
+  // key 1 at channel 0, then at channel 1) -> the eight keys at channel HI.
+  template <bool HI>
+  static __device__ __forceinline__ bf16x8 widen_pairs(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+    const uint4 u = make_uint4(fp8x2_to_bf16x2<HI>(p0), fp8x2_to_bf16x2<HI>(p1), fp8x2_to_bf16x2<HI>(p2),
+                               fp8x2_to_bf16x2<HI>(p3));
+    return __builtin_bit_cast(bf16x8, u);
+  }
   static __device__ __forceinline__ void widen4(uint32_t w, float* o) { fp8x4_to_f32x4(w, o); }
 };
 
@@ -121,6 +129,13 @@ struct Codec<kInt8> {
   static __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
     const uint4 u = make_uint4(f32x2_to_bf16x2(i8_at(lo, 0), i8_at(lo, 1)), f32x2_to_bf16x2(i8_at(lo, 2), i8_at(lo, 3)),
                                f32x2_to_bf16x2(i8_at(hi, 0), i8_at(hi, 1)), f32x2_to_bf16x2(i8_at(hi, 2), i8_at(hi, 3)));
+    return __builtin_bit_cast(bf16x8, u);
+  }
+  template <bool HI>
+  static __device__ __forceinline__ bf16x8 widen_pairs(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+    constexpr int b = HI ? 2 : 0;
+    const uint4 u = make_uint4(f32x2_to_bf16x2(i8_at(p0, b), i8_at(p0, b + 1)), f32x2_to_bf16x2(i8_at(p1, b), i8_at(p1, b + 1)),
+                               f32x2_to_bf16x2(i8_at(p2, b), i8_at(p2, b + 1)), f32x2_to_bf16x2(i8_at(p3, b), i8_at(p3, b + 1)));
     return __builtin_bit_cast(bf16x8, u);
   }
   static __device__ __forceinline__ void widen4(uint32_t w, float* o) {
@@ -183,21 +198,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   x += dpp_f32<kDppRowHalfMirror>(x);
   x += dpp_f32<kDppRowMirror>(x);
   return sum_over_row_groups(x);
-}
-
-// 4x4 byte transpose across four dwords: out[k] byte r = in[r] byte k.
-__device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                                   uint32_t& o0, uint32_t& o1, uint32_t& o2,
-                                                   uint32_t& o3) {
-  // __builtin_amdgcn_perm(hi, lo, sel): bytes 0-3 come from lo, 4-7 from hi.
-  uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
-  uint32_t ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
-  uint32_t cd01 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
-  uint32_t cd23 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
-  o0 = __builtin_amdgcn_perm(cd01, ab01, 0x05040100u);       // a0 b0 c0 d0
-  o1 = __builtin_amdgcn_perm(cd01, ab01, 0x07060302u);       // a1 b1 c1 d1
-  o2 = __builtin_amdgcn_perm(cd23, ab23, 0x05040100u);       // a2 b2 c2 d2
-  o3 = __builtin_amdgcn_perm(cd23, ab23, 0x07060302u);       // a3 b3 c3 d3
 }
 
 }  // namespace fp8kv

@@ -215,6 +215,28 @@ def test_window(D, nq, W):
     assert_close(out, ref, f"D={D} rows={nq} W={W}")
 
 
+@pytest.mark.parametrize("nq,W", [(3, 0), (8, 0), (1, 4095), (3, 4095)])
+@pytest.mark.parametrize("k0", [1024.0, 196.0])
+def test_rows_and_window_with_a_key_far_above_a_waves_first_keys(nq, W, k0):
+    """Several query rows and a window, D = 128: every query has q[0] = 4 and
+    the keys at positions 40, 2,600 and 5,900 have k[0] = k0, so they score
+    ~520 (k0 = 1024: p = 2^(s - ref) overflows against the reference the
+    kernel takes from a wave's first visible step, and those waves sum their
+    keys again with a running maximum) or ~100 (k0 = 196: large finite p)
+    log2 units above their neighbours.  Against the fp64 oracle."""
+    say(f"rows/window with a key far above its wave's first keys (nq={nq}, W={W}, k[0] = {k0})")
+    case = wl.layer_decode(5, ctx=6000, pool_rows=6100, with_new_token=False, n_qrows=nq)
+    case.q[..., 0] = wl.bf16_bits(np.float32([4.0]))[0]
+    big = wl.bf16_bits(np.float32([k0]))[0]
+    for pos in (40, 2600, 5900):
+        case.k_rows[case.table[0, pos], :, 0] = big
+    pool = build_pool(case)
+    out = bf16_to_f64(_rows(pool, case, window=W))
+    assert np.isfinite(out).all()
+    ref = _oracle(case, window=W)
+    assert_close(out.reshape(ref.shape), ref, f"rows nq={nq} W={W} k0={k0}")
+
+
 def test_window_covering_everything_is_bit_identical_to_no_window():
     say("window >= length == no window, bit for bit")
     case = wl.layer_decode(75, ctx=3000, pool_rows=3100, with_new_token=False, n_qrows=3)
