@@ -268,56 +268,88 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FP8KV_PR
       }
       const bool need_mask = tile_mask && (u0 + 32 * st + 31 > diag || u0 + 32 * st + 32 > n_keys);
       bf16x8 pa[kRowBlocks];
+      if constexpr (MODE == 0) {
+        // Masks of both row blocks first, then straight-line code: a row
+        // block's exponentials and P*V MFMAs, then the next's (2 % faster
+        // than masking and exponentiating each block between branches).
+        float sc[kRowBlocks][8];
 #pragma unroll
-      for (int cb = 0; cb < kRowBlocks; ++cb) {
-        float sc[8] = {s[0][cb][0], s[0][cb][1], s[0][cb][2], s[0][cb][3],
-                       s[1][cb][0], s[1][cb][1], s[1][cb][2], s[1][cb][3]};
+        for (int cb = 0; cb < kRowBlocks; ++cb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[cb][e] = s[e >> 2][cb][e & 3];
         if (need_mask) {
-          // slot e holds key u0 + 32st + 4j + (e & 3) + 16 (e >> 2); it is
-          // visible when that is at most the row's last visible key
-          const int rel = min(n_prefix + row_tok[cb], n_keys - 1) - (u0 + 32 * st) - 4 * j;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sc[e] = ((e & 3) + 16 * (e >> 2) <= rel) ? sc[e] : -INFINITY;
-        }
-        if (MODE == 2 || (MODE == 1 && st == 0)) {
-          float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-          tmax = max_over_row_groups(tmax);
-          tmax *= qk_scale_log2;  // the scale is positive: max commutes with it
-          if (MODE == 1) {
-            // Key 0 is in this sub-step and every row sees it: finite.
-            m_run[cb] = tmax;
-          } else if (__any(tmax > m_run[cb] + kLazyMaxSlack)) {
-            // Lazy maximum.  The first sub-step holds key 0, which every row
-            // sees, so m_run is finite from then on.  A sub-step whose keys
-            // are all masked for a row has tmax = -inf and p = 0.
-            const float m_new = fmaxf(m_run[cb], tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 on the first sub-step
-            m_run[cb] = m_new;
-            float ai[4];
+          for (int cb = 0; cb < kRowBlocks; ++cb) {
+            // slot e holds key u0 + 32st + 4j + (e & 3) + 16 (e >> 2); it is
+            // visible when that is at most the row's last visible key
+            const int rel = min(n_prefix + row_tok[cb], n_keys - 1) - (u0 + 32 * st) - 4 * j;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lsum[cb][i] *= ai[i];
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o[cb][nb][i] *= ai[i];
+            for (int e = 0; e < 8; ++e) sc[cb][e] = ((e & 3) + 16 * (e >> 2) <= rel) ? sc[cb][e] : -INFINITY;
           }
         }
-        const float neg_m = -m_run[cb];
-        float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], qk_scale_log2, neg_m));
-        pa[cb] = u4_as_bf16x8(make_uint4(f32x2_to_bf16x2(p[0], p[1]), f32x2_to_bf16x2(p[2], p[3]),
-                                         f32x2_to_bf16x2(p[4], p[5]), f32x2_to_bf16x2(p[6], p[7])));
-        lsum[cb] = mfma16x16x32(pa[cb], ones, lsum[cb]);
-      }
-
-      // ---- O += P * V with the operands read above.
+        for (int cb = 0; cb < kRowBlocks; ++cb) {
+          const float neg_m = -m_run[cb];
+          float p[8];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
+          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[cb][e], qk_scale_log2, neg_m));
+          pa[cb] = u4_as_bf16x8(make_uint4(f32x2_to_bf16x2(p[0], p[1]), f32x2_to_bf16x2(p[2], p[3]),
+                                           f32x2_to_bf16x2(p[4], p[5]), f32x2_to_bf16x2(p[6], p[7])));
+          lsum[cb] = mfma16x16x32(pa[cb], ones, lsum[cb]);
 #pragma unroll
-        for (int cb = 0; cb < kRowBlocks; ++cb) o[cb][nb] = mfma16x16x32(pa[cb], bvs[nb], o[cb][nb]);
+          for (int nb = 0; nb < 8; ++nb) o[cb][nb] = mfma16x16x32(pa[cb], bvs[nb], o[cb][nb]);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < kRowBlocks; ++cb) {
+          float sc[8] = {s[0][cb][0], s[0][cb][1], s[0][cb][2], s[0][cb][3],
+                         s[1][cb][0], s[1][cb][1], s[1][cb][2], s[1][cb][3]};
+          if (need_mask) {
+            // slot e holds key u0 + 32st + 4j + (e & 3) + 16 (e >> 2); it is
+            // visible when that is at most the row's last visible key
+            const int rel = min(n_prefix + row_tok[cb], n_keys - 1) - (u0 + 32 * st) - 4 * j;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = ((e & 3) + 16 * (e >> 2) <= rel) ? sc[e] : -INFINITY;
+          }
+          if (MODE == 2 || (MODE == 1 && st == 0)) {
+            float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            tmax = max_over_row_groups(tmax);
+            tmax *= qk_scale_log2;  // the scale is positive: max commutes with it
+            if (MODE == 1) {
+              // Key 0 is in this sub-step and every row sees it: finite.
+              m_run[cb] = tmax;
+            } else if (__any(tmax > m_run[cb] + kLazyMaxSlack)) {
+              // Lazy maximum.  The first sub-step holds key 0, which every row
+              // sees, so m_run is finite from then on.  A sub-step whose keys
+              // are all masked for a row has tmax = -inf and p = 0.
+              const float m_new = fmaxf(m_run[cb], tmax);
+              const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 on the first sub-step
+              m_run[cb] = m_new;
+              float ai[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) lsum[cb][i] *= ai[i];
+#pragma unroll
+              for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[cb][nb][i] *= ai[i];
+            }
+          }
+          const float neg_m = -m_run[cb];
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], qk_scale_log2, neg_m));
+          pa[cb] = u4_as_bf16x8(make_uint4(f32x2_to_bf16x2(p[0], p[1]), f32x2_to_bf16x2(p[2], p[3]),
+                                           f32x2_to_bf16x2(p[4], p[5]), f32x2_to_bf16x2(p[6], p[7])));
+          lsum[cb] = mfma16x16x32(pa[cb], ones, lsum[cb]);
+        }
+        // ---- O += P * V with the operands read above.
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+          for (int cb = 0; cb < kRowBlocks; ++cb) o[cb][nb] = mfma16x16x32(pa[cb], bvs[nb], o[cb][nb]);
+        }
       }
     }
   };
