@@ -191,6 +191,13 @@ size_t fp8kv_decode_workspace_bytes(int32_t n_queries, int32_t n_q_heads, int32_
  * merge combines them by log-sum-exp.  Results agree to rounding for every
  * split count.
  *
+ * Timing depends on the data in one case: stage 1 measures each key's weight
+ * against the largest score among the first keys it reads (D = 128), and
+ * when a later score is so much larger that a weight or a sum overflows
+ * (about 128 powers of two in exp2 units), that part of the keys is read and
+ * summed a second time with a running maximum.  The result is the same up to
+ * rounding either way.  The prefill attention does the same per workgroup.
+ *
  * q:            device bf16 [batch][n_q_heads][D], contiguous, 16-byte aligned
  *               (D = pool->head_dim).
  * row_table:    device int32, row b at row_table + b * table_stride; all
