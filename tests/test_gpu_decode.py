@@ -195,7 +195,7 @@ def test_batched_16_requests_gqa4():
             assert_close(out[b], ref[b], f"  request {b} (L={case.seq_lens[b]})")
 
 
-@pytest.mark.parametrize("kind", ["layer", "batch"])
+@pytest.mark.parametrize("kind", ["layer", "batch", "layer_one_split"])
 @pytest.mark.parametrize("k0", [1024.0, 196.0])
 @pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 def test_key_far_above_a_waves_first_keys(kind, k0, fmt):
@@ -205,10 +205,12 @@ def test_key_far_above_a_waves_first_keys(kind, k0, fmt):
     wave's first step, the kernel's softmax reference: ~520 log2 units for
     k0 = 1024, where p = 2^(s - ref) overflows and those waves must sum their
     keys again with a running maximum; ~100 for k0 = 196, a large but finite
-    p on the fixed reference.  The one-layer case runs the 8-wave shape, the
-    batch the streaming one; against the fp64 oracle, every request."""
+    p on the fixed reference.  The one-layer case runs the 8-wave shape (with
+    one split, a wave covers a dozen groups and its second pass re-reads every
+    group's rows), the batch the streaming one; against the fp64 oracle,
+    every request."""
     say(f"decode with a key far above its wave's first keys ({kind}, k[0] = {k0}, {fmt})")
-    if kind == "layer":
+    if kind.startswith("layer"):
         case = wl.layer_decode(4, ctx=6000, pool_rows=6100, with_new_token=False)
     else:
         case = wl.batched_decode(4, n_req=6, lo=1024, hi=6000)
@@ -222,7 +224,7 @@ def test_key_far_above_a_waves_first_keys(kind, k0, fmt):
     kc, vc, ks, vs = oracle_pool(case, fmt)
     ref = oracle.decode_attention(case.q, kc, vc, ks, vs, case.table, case.seq_lens, case.sm_scale,
                                   case.n_kv_heads, fmt=fmt)
-    out = bf16_to_f64(run_decode(pool, case))
+    out = bf16_to_f64(run_decode(pool, case, max_splits=1 if kind == "layer_one_split" else 0))
     assert np.isfinite(out).all()
     for b in range(case.batch):
         assert_close(out[b], ref[b], f"{kind} request {b} (L={case.seq_lens[b]})")

@@ -100,8 +100,9 @@ def test_chunked_prefill_8k_prefix_8k_chunk():
     assert_close(got, ref, "8K+8K sampled")
 
 
-@pytest.mark.parametrize("where,k0", [("chunk", 1024.0), ("prefix", 1024.0), ("chunk", 196.0)])
-def test_prefill_key_far_above_each_rows_first_keys(where, k0):
+@pytest.mark.parametrize("where,k0,fmt", [("chunk", 1024.0, "e4m3"), ("prefix", 1024.0, "e4m3"), ("chunk", 196.0, "e4m3"),
+                                          ("prefix", 1024.0, "int8")])
+def test_prefill_key_far_above_each_rows_first_keys(where, k0, fmt):
     """Every query has q[0] = 4 and one key has k[0] = k0, so that key's score
     lies ~4 k0 / sqrt(128) log2 e above the scores of a row's first 32 keys
     (the kernel's softmax reference): ~520 log2 units for k0 = 1024, past
@@ -118,9 +119,9 @@ def test_prefill_key_far_above_each_rows_first_keys(where, k0):
         case.k_cur[200, :, 0] = big
     else:
         case.prefix_k[450, :, 0] = big
-    got, ref = _run(case)
+    got, ref = _run(case, fmt=fmt)
     assert np.isfinite(got).all()
-    assert_close(got, ref, f"one key far above ({where}, {k0})")
+    assert_close(got, ref, f"one key far above ({where}, {k0}, {fmt})")
 
 
 @pytest.mark.parametrize("P,T,Hq,Hkv", [(0, 37, 32, 4), (100, 37, 32, 4), (257, 130, 16, 4), (1000, 300, 8, 8)])
