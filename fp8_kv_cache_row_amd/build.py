@@ -38,36 +38,49 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def _compile_flags():
+    return [f for f in FLAGS if f != "-shared"]
+
+
+def _library(srcs, out, defines, objdir, pool, verbose):
+    """Compile each source to an object (in parallel) and link them into `out`."""
+    tag = os.path.basename(out).replace(".", "_")
+    objs = [os.path.join(objdir, f"{tag}_{os.path.basename(src)}.o") for src in srcs]
+    jobs = [pool.submit(_run, [HIPCC, *_compile_flags(), *defines, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj],
+                        verbose) for src, obj in zip(srcs, objs)]
+
+    def link():
+        for j in jobs:
+            j.result()
+        tmp = out + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, out)
+        return out
+    return link
+
+
 def build(verbose: bool = False, extra=None) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    build_floor(verbose)
-    build_timeline(verbose)
+    """The product library, the read-floor library and the timeline build,
+    every source compiled as its own job."""
+    import concurrent.futures
+    import tempfile
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with tempfile.TemporaryDirectory(prefix="fp8kv_build_") as objdir, \
+            concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+        links = [_library(sources(), LIB, list(extra or []), objdir, pool, verbose),
+                 _library(sources(), TIMELINE_LIB, ["-DFP8KV_WAVE_TIMELINE"], objdir, pool, verbose)]
+        floor = pool.submit(_run, [HIPCC, *FLAGS, FLOOR_SRC, "-o", FLOOR_LIB + ".tmp"], verbose)
+        for link in links:
+            link()
+        floor.result()
+        os.replace(FLOOR_LIB + ".tmp", FLOOR_LIB)
     return LIB
-
-
-def build_timeline(verbose: bool = False) -> str:
-    tmp = TIMELINE_LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-DFP8KV_WAVE_TIMELINE", "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, TIMELINE_LIB)
-    return TIMELINE_LIB
-
-
-def build_floor(verbose: bool = False) -> str:
-    tmp = FLOOR_LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, FLOOR_SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, FLOOR_LIB)
-    return FLOOR_LIB
 
 
 if __name__ == "__main__":

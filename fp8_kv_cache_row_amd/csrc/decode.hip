@@ -41,6 +41,12 @@
 //    dim 256 the registers leave no room for the second pass's code and the
 //    lazy maximum is the only one.
 //  * Waves merge through LDS; one (o, log2-sum-exp) partial per split.
+//  * An appending decode step (the new token quantized on write) with one row
+//    per request and one workgroup round lets stage 1 take the new token:
+//    one wave of split 0's workgroup quantizes it into its pool row while
+//    that wave would otherwise wait on the other waves' rows, scores it and
+//    folds it into split 0's partial, so the merge is the plain one -- 12.9
+//    against 13.2 us for the 32K step with the merge taking the token.
 //  * The grid places the KV heads of one split on one XCD, next to each other
 //    in dispatch order, so they share that XCD's L2 lines of the table and of
 //    the rows' scales; grids of several rounds (batches, long contexts) use
@@ -91,6 +97,67 @@ constexpr float kNoMax = -1.0e30f;
 __device__ __forceinline__ int step_key(int j, int r) { return (r < 4) ? 4 * j + r : 12 + 4 * j + r; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// E consecutive values per lane: bf16 bit patterns in E/2 dwords, fp32 in a vector.
+template <int E>
+struct LaneVec {
+  typedef float F __attribute__((ext_vector_type(E)));
+  typedef uint32_t U __attribute__((ext_vector_type(E / 2)));
+};
+
+// One new token's K and V rows of a KV head, spread over a wave (lane l holds
+// d = E*l .. E*l + E-1 as bf16 pairs), quantized exactly as the
+// quantize-on-write kernel does it (the same codec functions and a wave-wide
+// amax): the codes (byte e of kc / vc is element e), the fp32 scales, and the
+// values the codes decode to (before the scale).
+template <int E>
+struct NewTokenCodes {
+  uint32_t kc, vc;
+  float sk, sv;
+  float kd[4], vd[4];
+};
+template <int E, int F>
+__device__ __forceinline__ NewTokenCodes<E> quantize_new_token(typename LaneVec<E>::U k2, typename LaneVec<E>::U v2) {
+  using Code = Codec<F>;
+  NewTokenCodes<E> r;
+  float kx[E], vx[E];
+#pragma unroll
+  for (int e = 0; e < E; e += 2) {
+    kx[e] = bf16lo_to_f32(k2[e / 2]);
+    kx[e + 1] = bf16hi_to_f32(k2[e / 2]);
+    vx[e] = bf16lo_to_f32(v2[e / 2]);
+    vx[e + 1] = bf16hi_to_f32(v2[e / 2]);
+  }
+  float ka = 0.f, va = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ka = fmaxf(ka, fabsf(kx[e]));
+    va = fmaxf(va, fabsf(vx[e]));
+  }
+  ka = wave_max(ka);
+  va = wave_max(va);
+  r.sk = Code::scale(ka);
+  r.sv = Code::scale(va);
+  r.kc = Code::template pack2<false>(Code::prescale(kx[0], ka, r.sk), Code::prescale(kx[1], ka, r.sk), 0u);
+  r.vc = Code::template pack2<false>(Code::prescale(vx[0], va, r.sv), Code::prescale(vx[1], va, r.sv), 0u);
+  if constexpr (E == 4) {
+    r.kc = Code::template pack2<true>(Code::prescale(kx[2], ka, r.sk), Code::prescale(kx[3], ka, r.sk), r.kc);
+    r.vc = Code::template pack2<true>(Code::prescale(vx[2], va, r.sv), Code::prescale(vx[3], va, r.sv), r.vc);
+  }
+  Code::widen4(r.kc, r.kd);
+  Code::widen4(r.vc, r.vd);
+  return r;
+}
+
+// The new token of a single-row appending call when stage 1 takes it
+// (k_new null: it does not): bf16 K/V rows [B][new_token_stride], head g at
+// g * D, quantized into pool row new_slots[b].
+struct FoldKernelArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_token_stride;
+  const int32_t* new_slots;
+};
 
 // Compile-time shape of one stage-1 instantiation.
 //   D       head dim (128 or 256).
@@ -171,8 +238,10 @@ __device__ __forceinline__ void load_v_words(const uint8_t* p, uint32_t (&w)[W])
 }
 
 // NTL: the codes are read with non-temporal loads (a pool whose KV heads never
-// share a 128-byte line).
-template <class C, bool NTL>
+// share a 128-byte line).  FOLD: the launch also takes each request's new
+// token (see kFold below); a separate instantiation, so that the plain stage 1
+// keeps its registers and schedule.
+template <class C, bool NTL, bool FOLD>
 __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kWavesPerEU))) void decode_stage1_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, uint32_t code_row_stride,
@@ -180,7 +249,7 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
     const int32_t* __restrict__ table, int64_t table_stride, const int32_t* __restrict__ seq_lens,
     int32_t max_seq_len, int32_t n_split, int32_t chunk, int32_t split_stride, float qk_scale_log2,
     int32_t key_trim, int32_t window, int32_t n_col_groups, uint32_t max_row, int32_t* __restrict__ header,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ part_o, float* __restrict__ part_lse, FoldKernelArgs fold_args) {
   constexpr int D = C::D, NT = C::NT, kWaves = C::kWaves, kBlock = C::kBlock;
   constexpr int kSteps = C::kSteps, kGroupKeys = C::kGroupKeys, kRowSlots = C::kRowSlots;
   constexpr int kNB = C::kNB, kPassCols = C::kPassCols;
@@ -219,6 +288,22 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
   __shared__ __attribute__((aligned(16))) float sm_o[kWaves][kPassCols][128];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
+  // The new token of an appending call, one row per request (head dim 128,
+  // one workgroup round): wave 3 of split 0's workgroup of each (request, KV
+  // head) quantizes its K and V rows into the pool, scores them against the
+  // group's G query heads and folds the token into the split's partial as one
+  // more key; the merge is then the plain one.  Waves 0-3 get their rows
+  // first and would otherwise wait on the later waves' rows, and wave 3 has
+  // a single key group even when a split's keys outnumber one round of the
+  // waves (waves 0 and 1 take the extra groups): 15.2 against 15.5 us per
+  // layer on the 48-layer 40K step with wave 0.
+  constexpr bool kFold = FOLD;
+  static_assert(!FOLD || (D == 128 && !C::MULTI && !C::STREAM), "the new token is folded at head dim 128, one row, one round");
+  constexpr int kFE = D / kWave;  // new-token values per lane
+  constexpr int kFoldWave = kWaves / 2 - 1;
+  __shared__ float s_fold_lse[kFold ? C::G : 1];
+  __shared__ __attribute__((aligned(16))) float s_fold_v[kFold ? D : 4];
+  const bool fold = kFold && fold_args.k_new != nullptr && split_raw == 0;
 
   const int32_t* trow = table + (int64_t)b * table_stride;
   int key_begin = split * chunk;
@@ -256,6 +341,24 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 #pragma unroll
     for (int kk = 0; kk < C::kQK; ++kk)
       qb[t][kk] = u4_as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * (kk >> 1) + 8 * (kk & 1)));
+  }
+  // The new token's rows and the group's query heads, in the layout of the
+  // quantize-on-write kernel (E values per lane), requested now so that they
+  // land with this wave's first rows.
+  typedef typename LaneVec<kFE>::U fvecu;
+  fvecu fk2 = {}, fv2 = {};
+  fvecu fq2[kFold ? C::G : 1] = {};
+  int64_t fslot = 0;
+  if constexpr (kFold) {
+    if (fold && wave == kFoldWave) {
+      fslot = min((uint32_t)fold_args.new_slots[b], max_row);  // out-of-range slots are clamped, never followed
+      const int64_t src = (int64_t)b * fold_args.new_token_stride + g * D + kFE * lane;
+      fk2 = *reinterpret_cast<const fvecu*>(fold_args.k_new + src);
+      fv2 = *reinterpret_cast<const fvecu*>(fold_args.v_new + src);
+#pragma unroll
+      for (int hh = 0; hh < C::G; ++hh)
+        fq2[hh] = *reinterpret_cast<const fvecu*>(q + ((int64_t)b * n_q_heads + h0 + hh) * D + kFE * lane);
+    }
   }
 
   // Positions: request length len; query row i sits at p_i = len - n_qrows + i
@@ -551,6 +654,40 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
   }
   FP8KV_MARK(4, true);
 
+  if constexpr (kFold) {
+    if (fold && wave == kFoldWave) {
+      // Quantize the new token's rows into its pool row; its score against
+      // each query head (log2 units) and its value, from the decoded codes,
+      // go to LDS for the partial below.
+      const NewTokenCodes<kFE> nt = quantize_new_token<kFE, C::F>(fk2, fv2);
+#pragma unroll
+      for (int hh = 0; hh < C::G; ++hh) {
+        float qx[kFE];
+#pragma unroll
+        for (int e = 0; e < kFE; e += 2) {
+          qx[e] = bf16lo_to_f32(fq2[hh][e / 2]);
+          qx[e + 1] = bf16hi_to_f32(fq2[hh][e / 2]);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < kFE; ++e) part += qx[e] * nt.kd[e];
+        const float dot = wave_sum(part);
+        if (lane == 0) s_fold_lse[hh] = dot * nt.sk * qk_scale_log2;
+      }
+#pragma unroll
+      for (int e = 0; e < kFE; ++e) s_fold_v[kFE * lane + e] = nt.vd[e] * nt.sv;
+      uint8_t* kdst = const_cast<uint8_t*>(k_codes) + fslot * code_row_stride + g * D + kFE * lane;
+      uint8_t* vdst = const_cast<uint8_t*>(v_codes) + fslot * code_row_stride + g * D + kFE * lane;
+      static_assert(kFE == 2, "two codes per lane at head dim 128");
+      *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)nt.kc;
+      *reinterpret_cast<uint16_t*>(vdst) = (uint16_t)nt.vc;
+      if (lane == 0) {
+        const_cast<float*>(k_scales)[fslot * scale_row_stride + g] = nt.sk;
+        const_cast<float*>(v_scales)[fslot * scale_row_stride + g] = nt.sv;
+      }
+    }
+  }
+
   // Merge the waves of this workgroup into one partial per column, one pass
   // per (tile, 128 of the D columns of O).  In pass half, LDS column
   // d' = 8 n' + e holds d = kNB n' + 8 half + e.
@@ -586,6 +723,9 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
         float M = sm_m[0][col];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][col]);
+        if constexpr (kFold) {
+          if (fold) M = fmaxf(M, s_fold_lse[col]);
+        }
         float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
         float den = 0.f;
 #pragma unroll
@@ -597,6 +737,17 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
           num.z += wt * v.z;
           num.w += wt * v.w;
           den += wt * sm_l[w][col];
+        }
+        if constexpr (kFold) {
+          if (fold) {  // the new token: one key of weight 2^(score - M) and value v
+            const float wt = fast_exp2(s_fold_lse[col] - M);
+            const float4 v = *reinterpret_cast<const float4*>(&s_fold_v[d]);
+            num.x += wt * v.x;
+            num.y += wt * v.y;
+            num.z += wt * v.z;
+            num.w += wt * v.w;
+            den += wt;
+          }
         }
         const float inv = (den > 0.f) ? 1.0f / den : 0.0f;
         const int64_t bh = ((int64_t)b * n_qrows + i) * n_q_heads + h0 + (c - i * G);
@@ -621,8 +772,10 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 // LDS -- a single memory round trip.  Lane l owns d = E*l .. E*l + E-1
 // (E = D / 64).
 //
-// With APPEND, the request's last n_qrows positions are new tokens, left out
-// of stage 1; in the workgroup of query row i, wave j <= i takes new token j:
+// With APPEND (the appending calls whose new tokens stage 1 does not take:
+// several query rows, head dim 256, or several workgroup rounds), the
+// request's last n_qrows positions are new tokens, left out of stage 1; in
+// the workgroup of query row i, wave j <= i takes new token j:
 // it quantizes the token's bf16 K and V rows of the head group exactly as the
 // quantize-on-write kernel does (same codec functions), scores q against the
 // decoded codes, and, when the token lies inside the row's window, folds it in
@@ -655,13 +808,6 @@ struct AppendKernelArgs {
   float qk_scale_log2;
   int32_t n_qrows;  // new tokens (and query rows) per request
   int32_t window;   // 0: every new token j <= i is visible to query row i
-};
-
-// E consecutive values per lane: bf16 bit patterns in E/2 dwords, fp32 in a vector.
-template <int E>
-struct LaneVec {
-  typedef float F __attribute__((ext_vector_type(E)));
-  typedef uint32_t U __attribute__((ext_vector_type(E / 2)));
 };
 
 template <int D, bool APPEND, int F = kE4M3>
@@ -754,45 +900,24 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
   vecf o_new = {};
   if constexpr (APPEND) {
     if (wave < n_new) {
-      // Quantize the K and V rows (D values over the wave, E per lane).
-      float kx[E], vx[E], qx[E];
-      float ka = 0.f, va = 0.f;
+      // Quantize the K and V rows (D values over the wave, E per lane); score
+      // and value from the decoded codes, as stage 1 sees every other row.
+      const NewTokenCodes<E> nt = quantize_new_token<E, F>(k2, v2);
+      const uint32_t kc = nt.kc, vc = nt.vc;
+      const float sk = nt.sk, sv = nt.sv;
+      float qx[E];
 #pragma unroll
       for (int e = 0; e < E; e += 2) {
-        kx[e] = bf16lo_to_f32(k2[e / 2]);
-        kx[e + 1] = bf16hi_to_f32(k2[e / 2]);
-        vx[e] = bf16lo_to_f32(v2[e / 2]);
-        vx[e + 1] = bf16hi_to_f32(v2[e / 2]);
         qx[e] = bf16lo_to_f32(q2[e / 2]);
         qx[e + 1] = bf16hi_to_f32(q2[e / 2]);
       }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ka = fmaxf(ka, fabsf(kx[e]));
-        va = fmaxf(va, fabsf(vx[e]));
-      }
-      ka = wave_max(ka);
-      va = wave_max(va);
-      using Code = Codec<F>;
-      const float sk = Code::scale(ka), sv = Code::scale(va);
-      uint32_t kc = 0u, vc = 0u;  // E codes, byte e = element e
-      kc = Code::template pack2<false>(Code::prescale(kx[0], ka, sk), Code::prescale(kx[1], ka, sk), kc);
-      vc = Code::template pack2<false>(Code::prescale(vx[0], va, sv), Code::prescale(vx[1], va, sv), vc);
-      if constexpr (E == 4) {
-        kc = Code::template pack2<true>(Code::prescale(kx[2], ka, sk), Code::prescale(kx[3], ka, sk), kc);
-        vc = Code::template pack2<true>(Code::prescale(vx[2], va, sv), Code::prescale(vx[3], va, sv), vc);
-      }
-      // Score and value from the decoded codes, as stage 1 sees every other row.
-      float kd[4], vd[4];
-      Code::widen4(kc, kd);
-      Code::widen4(vc, vd);
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) part += qx[e] * kd[e];
+      for (int e = 0; e < E; ++e) part += qx[e] * nt.kd[e];
       const float dot = wave_sum(part);
       lse_new = dot * sk * app.qk_scale_log2;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o_new[e] = vd[e] * sv;
+      for (int e = 0; e < E; ++e) o_new[e] = nt.vd[e] * sv;
       // One workgroup per (request, KV head) stores the rows: the one of the
       // group's first query head and the last query row, which holds every
       // new token.
@@ -861,18 +986,22 @@ __global__ __launch_bounds__(kMergeBlock) void decode_merge_kernel(const int32_t
 
 template <class C>
 hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk_scale_log2,
-                             const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim, hipStream_t stream) {
+                             const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
+                             const FoldKernelArgs& fold, hipStream_t stream) {
   const int64_t z = (int64_t)sh.batch * geo.n_col_groups;
   if (z > FP8KV_MAX_DECODE_GROUPS_INTERNAL) return hipErrorInvalidValue;  // the entry points reject it first
   const dim3 grid((unsigned)(8 * pool.n_kv_heads), (unsigned)((geo.n_split + 7) / 8), (unsigned)z);
   int g_shift = 0;
   while ((1 << g_shift) < sh.n_q_heads / pool.n_kv_heads) ++g_shift;
-  auto kernel = pool.line_rows ? decode_stage1_kernel<C, true> : decode_stage1_kernel<C, false>;
+  auto kernel = pool.line_rows ? decode_stage1_kernel<C, true, false> : decode_stage1_kernel<C, false, false>;
+  if constexpr (C::D == 128 && !C::MULTI && !C::STREAM) {
+    if (fold.k_new) kernel = pool.line_rows ? decode_stage1_kernel<C, true, true> : decode_stage1_kernel<C, false, true>;
+  }
   hipLaunchKernelGGL(kernel, grid, dim3(C::kBlock), 0, stream, pool.k_codes, pool.v_codes,
                      pool.k_scales, pool.v_scales, (uint32_t)pool.code_row_stride, (uint32_t)pool.scale_row_stride,
                      q, sh.n_q_heads, sh.n_qrows, g_shift, sh.row_table, sh.table_stride, sh.seq_lens, sh.max_seq_len,
                      geo.n_split, geo.chunk, ws.split_stride, qk_scale_log2, key_trim, sh.window, geo.n_col_groups,
-                     (uint32_t)(pool.num_rows - 1), ws.header, ws.part_o, ws.part_lse);
+                     (uint32_t)(pool.num_rows - 1), ws.header, ws.part_o, ws.part_lse, fold);
   return hipGetLastError();
 }
 
@@ -880,26 +1009,26 @@ hipError_t launch_stage1_cfg(const PoolView& pool, const uint16_t* q, const Deco
 template <int D, bool WINDOW, int F>
 hipError_t launch_stage1_single(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
-                                hipStream_t stream) {
+                                const FoldKernelArgs& fold, hipStream_t stream) {
   // The streaming shape exists for head dim 128 without a window.
   constexpr bool kCanStream = D == 128 && !WINDOW;
   const bool st = kCanStream && geo.stream;
   switch (sh.n_q_heads / pool.n_kv_heads) {
     case 1:
-      return st ? launch_stage1_cfg<Stage1<1, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                : launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return st ? launch_stage1_cfg<Stage1<1, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                : launch_stage1_cfg<Stage1<1, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     case 2:
-      return st ? launch_stage1_cfg<Stage1<2, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                : launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return st ? launch_stage1_cfg<Stage1<2, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                : launch_stage1_cfg<Stage1<2, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     case 4:
-      return st ? launch_stage1_cfg<Stage1<4, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                : launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return st ? launch_stage1_cfg<Stage1<4, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                : launch_stage1_cfg<Stage1<4, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     case 8:
-      return st ? launch_stage1_cfg<Stage1<8, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                : launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return st ? launch_stage1_cfg<Stage1<8, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                : launch_stage1_cfg<Stage1<8, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     case 16:
-      return st ? launch_stage1_cfg<Stage1<16, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                : launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return st ? launch_stage1_cfg<Stage1<16, D, 1, false, false, F, kCanStream>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                : launch_stage1_cfg<Stage1<16, D, 1, false, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -908,13 +1037,13 @@ hipError_t launch_stage1_single(const PoolView& pool, const uint16_t* q, const D
 template <int D, bool WINDOW, int F>
 hipError_t launch_stage1_multi(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
                                const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
-                               hipStream_t stream) {
+                               const FoldKernelArgs& fold, hipStream_t stream) {
   switch (geo.col_tiles) {
-    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
-    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    case 1: return launch_stage1_cfg<Stage1<16, D, 1, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
+    case 2: return launch_stage1_cfg<Stage1<16, D, 2, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     case 4:
       if constexpr (D == 128)
-        return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, stream);
+        return launch_stage1_cfg<Stage1<16, D, 4, true, WINDOW, F>>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -924,23 +1053,23 @@ hipError_t launch_stage1_multi(const PoolView& pool, const uint16_t* q, const De
 template <int F>
 hipError_t launch_stage1_format(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float qk,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
-                                hipStream_t stream) {
+                                const FoldKernelArgs& fold, hipStream_t stream) {
   const bool window = sh.window > 0;
   if (sh.n_qrows == 1 && geo.n_col_groups == 1 && geo.col_tiles == 1) {
     if (pool.head_dim == 128)
-      return window ? launch_stage1_single<128, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                    : launch_stage1_single<128, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return window ? launch_stage1_single<128, true, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                    : launch_stage1_single<128, false, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     if (pool.head_dim == 256)
-      return window ? launch_stage1_single<256, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                    : launch_stage1_single<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
+      return window ? launch_stage1_single<256, true, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                    : launch_stage1_single<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
     return hipErrorInvalidValue;
   }
   if (pool.head_dim == 128)
-    return window ? launch_stage1_multi<128, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                  : launch_stage1_multi<128, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    return window ? launch_stage1_multi<128, true, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                  : launch_stage1_multi<128, false, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
   if (pool.head_dim == 256)
-    return window ? launch_stage1_multi<256, true, F>(pool, q, sh, qk, geo, ws, key_trim, stream)
-                  : launch_stage1_multi<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, stream);
+    return window ? launch_stage1_multi<256, true, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream)
+                  : launch_stage1_multi<256, false, F>(pool, q, sh, qk, geo, ws, key_trim, fold, stream);
   return hipErrorInvalidValue;
 }
 
@@ -968,12 +1097,21 @@ int32_t decode_max_col_tiles(int32_t head_dim) {
   return head_dim == 128 ? FP8KV_DECODE_MAX_TILES_128 : FP8KV_DECODE_MAX_TILES_256;
 }
 
+bool decode_stage1_takes_new_token(const PoolView& pool, const DecodeShape& sh, const DecodeGeometry& geo) {
+  // The instantiations that fold it: head dim 128, one query row per request
+  // (one 16-column tile), one workgroup round (not the streaming shape).
+  return pool.head_dim == 128 && sh.n_qrows == 1 && geo.n_col_groups == 1 && geo.col_tiles == 1 && !geo.stream;
+}
+
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const DecodeShape& sh, float sm_scale,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
-                                hipStream_t stream) {
+                                const AppendArgs* fold, hipStream_t stream) {
   const float qk = sm_scale * kLog2e;
-  if (pool.format == kInt8) return launch_stage1_format<kInt8>(pool, q, sh, qk, geo, ws, key_trim, stream);
-  if (pool.format == kE4M3) return launch_stage1_format<kE4M3>(pool, q, sh, qk, geo, ws, key_trim, stream);
+  if (fold && (!decode_stage1_takes_new_token(pool, sh, geo) || key_trim != 1)) return hipErrorInvalidValue;
+  const FoldKernelArgs fa = fold ? FoldKernelArgs{fold->k_new, fold->v_new, fold->new_token_stride, fold->new_slots}
+                                 : FoldKernelArgs{nullptr, nullptr, 0, nullptr};
+  if (pool.format == kInt8) return launch_stage1_format<kInt8>(pool, q, sh, qk, geo, ws, key_trim, fa, stream);
+  if (pool.format == kE4M3) return launch_stage1_format<kE4M3>(pool, q, sh, qk, geo, ws, key_trim, fa, stream);
   return hipErrorInvalidValue;
 }
 

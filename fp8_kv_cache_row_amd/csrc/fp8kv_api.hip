@@ -225,9 +225,13 @@ fp8kv_status launch_decode(const fp8kv_pool_layer* pool, const uint16_t* q, cons
                            uint16_t* out, const fp8kv::AppendArgs* app, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t n_queries = (int64_t)shape.batch * shape.n_qrows;
-  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? shape.n_qrows : 0, s);
+  // One query row per request in one workgroup round: stage 1 takes the new
+  // token and the plain merge follows; otherwise the appending merge takes it.
+  const bool fold = app && fp8kv::decode_stage1_takes_new_token(view_of(pool), shape, geo);
+  hipError_t e = fp8kv::launch_decode_stage1(view_of(pool), q, shape, sm_scale, geo, ws, app ? shape.n_qrows : 0,
+                                             fold ? app : nullptr, s);
   if (e != hipSuccess) return FP8KV_ERR_HIP;
-  if (app)
+  if (app && !fold)
     return from_hip(fp8kv::launch_decode_merge_append(view_of(pool), shape.batch, shape.n_q_heads, ws, geo.n_split,
                                                       *app, out, s));
   if (!out) return FP8KV_OK;

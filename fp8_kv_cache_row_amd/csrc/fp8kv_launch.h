@@ -95,11 +95,18 @@ constexpr size_t kDecodeHeaderBytes = 256;
 // Column tiles one stage-1 workgroup can hold at this head dim.
 int32_t decode_max_col_tiles(int32_t head_dim);
 
-// key_trim = 1 (one query row per request) leaves each request's last key
-// (position seq_lens[b] - 1) to the appending merge below.
+struct AppendArgs;
+
+// key_trim = n_qrows (an appending call) leaves each request's last n_qrows
+// keys, its new tokens, out of the cached keys.  Those are then taken by the
+// appending merge below, or, with `fold` (one query row per request, where
+// decode_stage1_takes_new_token holds), by stage 1 itself: split 0's
+// workgroup of each (request, KV head) quantizes the new token into its pool
+// row and folds it into that split's partial, and the plain merge follows.
+bool decode_stage1_takes_new_token(const PoolView& pool, const DecodeShape& shape, const DecodeGeometry& geo);
 hipError_t launch_decode_stage1(const PoolView& pool, const uint16_t* q, const DecodeShape& shape, float sm_scale,
                                 const DecodeGeometry& geo, const DecodeWorkspace& ws, int32_t key_trim,
-                                hipStream_t stream);
+                                const AppendArgs* fold, hipStream_t stream);
 
 // The VALU-only stage 1 (no matrix instructions), same grid and partials:
 // head dim 128, E4M3 codes, one query row, no window.
@@ -113,8 +120,9 @@ hipError_t launch_decode_merge(int64_t n_rows_heads, int32_t head_dim, const Dec
                                uint16_t* out, hipStream_t stream);
 
 // The new token of each request: bf16 K/V rows [B][token_stride] (head g at
-// g * head_dim), quantized into pool row new_slots[b] and folded into the
-// merge as one more single-key partial.
+// g * head_dim), quantized into pool row new_slots[b] and folded in as one
+// more key, by stage 1 (see above) or by the merge as one more single-key
+// partial.
 struct AppendArgs {
   const uint16_t* q;
   const uint16_t* k_new;

@@ -323,9 +323,11 @@ fp8kv_status fp8kv_decode_attn_rows(const fp8kv_pool_layer *pool, const uint16_t
  * followed by fp8kv_decode_attn with the same arguments: the token's codes and
  * scales land in its row bit for bit as fp8kv_quantize_rows would write them,
  * and `out` is attention over positions [0, seq_lens[b]) including the token.
- * The token's row is never read back: stage 1 covers [0, p_b) and the merge
- * quantizes the token itself and adds it as a single-key partial, which saves
- * a launch per step.
+ * The token's row is never read back: stage 1 covers [0, p_b), and the token
+ * is quantized and added as one more key inside the call, which saves a launch
+ * per step -- by stage 1 (its first split's workgroup, folded into that
+ * split's partial) when D = 128 and the call's splits fit one round of
+ * workgroups, otherwise by the merge as a single-key partial.
  *
  * k_new, v_new:      device bf16, token b at k_new + b * new_token_stride,
  *                    [n_kv_heads][D] each; 16-byte aligned, stride a
