@@ -247,3 +247,41 @@ def test_append_window_int8_pool(D):
     out = bf16_to_f64(_run_append_window(pool, case, 255))
     _check_pool(pool, ref_pools, f"int8 window D={D}")
     assert_close(out, ref, f"int8 window D={D}")
+
+
+@pytest.mark.parametrize("kind,new_k0,cached_k0", [
+    ("layer", 1024.0, None), ("layer", -1024.0, None), ("layer", 1024.0, 1024.0),
+    ("batch6", 1024.0, None), ("batch6", -1024.0, None), ("batch6", 1024.0, 1024.0),
+    ("batch16", 1024.0, 1024.0)])
+def test_append_with_keys_far_apart(kind, new_k0, cached_k0):
+    """Every query has q[0] = 4; the new token's K has k[0] = new_k0 in every KV
+    head (~520 log2 units above, or below, every cached key), and with
+    cached_k0 the cached keys at positions 40 and 2,600 have k[0] = cached_k0
+    (far above their wave's first keys: those waves sum their keys again with
+    a running maximum).  The one-request layer and the 6-request batch run in
+    one workgroup round, where stage 1 takes the new token and folds it into
+    split 0's partial; the 16-request batch runs the streaming shape, where
+    the merge takes it.  Pool bit-exact and output against the fp64 oracle,
+    every request."""
+    say(f"decode+append, keys far apart ({kind}, new k[0] = {new_k0}, cached k[0] = {cached_k0})")
+    if kind == "layer":
+        case = wl.layer_decode(4, ctx=6000, pool_rows=6100)
+    elif kind == "batch6":
+        case = wl.batched_decode(5, n_req=6, lo=1024, hi=6000, with_new_token=True)
+    else:
+        case = wl.batched_decode(6, with_new_token=True)
+    case.q[..., 0] = wl.bf16_bits(np.float32([4.0]))[0]
+    case.new_k[:, :, 0] = wl.bf16_bits(np.float32([new_k0]))[0]
+    if cached_k0 is not None:
+        big = wl.bf16_bits(np.float32([cached_k0]))[0]
+        for b in range(case.batch):
+            for pos in (40, 2600):
+                if pos < case.seq_lens[b] - 1:
+                    case.k_rows[case.table[b, pos], :, 0] = big
+    pool = build_pool(case)
+    ref_pools, ref = _oracle_step(case)
+    out = bf16_to_f64(_run_append(pool, case))
+    assert np.isfinite(out).all()
+    _check_pool(pool, ref_pools, kind)
+    for b in range(case.batch):
+        assert_close(out[b], ref[b], f"{kind} request {b} (L={case.seq_lens[b]})")
