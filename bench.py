@@ -344,6 +344,25 @@ def variants_timing(fk, wl, dev, args, bf):
         extra={"workload": "16 requests, lengths 1,024-32,768 (272,568 rows), GQA 4 (16 q / 4 KV heads), "
                            "one decode step with quantize-on-write"})
     run("batched16_stage1", c, stage1_body, kv, copies=min(n, 4))
+    if args.layout.startswith("interleaved"):
+        # the same rows' whole records gathered through the tables by the read-floor kernel
+        FL = floor_lib()
+        flat = np.concatenate([c.table[b, :c.seq_lens[b]] for b in range(c.batch)]).astype(np.int32)
+        tflat = torch.from_numpy(flat).to(dev)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+        def gather_body(case, pools):
+            rec = pools[0].record.shape[1]
+            sp = ctypes.c_void_p(stream.cuda_stream)
+
+            def call(i):
+                if FL.fp8kv_floor_gather(pools[i % len(pools)].record.data_ptr(), case.pool_rows, rec,
+                                         tflat.data_ptr(), len(flat), 1024, sink.data_ptr(), sp):
+                    raise RuntimeError("fp8kv_floor_gather failed")
+            return call
+        run("batched16_floor_gather_records", c, gather_body, kv, copies=min(n, 4),
+            extra={"op": "whole row records of the batch's 272,568 rows read through the tables by the "
+                         "read-floor kernel (every byte a page-size-1 reader fetches), 1,024 workgroups"})
     del c
     c = wl.layer_decode(0, with_new_token=False)
     W = 4095

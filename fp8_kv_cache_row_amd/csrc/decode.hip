@@ -237,6 +237,14 @@ __device__ __forceinline__ void load_v_words(const uint8_t* p, uint32_t (&w)[W])
   }
 }
 
+// Lanes i and i ^ 8 of each 16-lane row exchange a dword: lanes in the banks
+// of BANKS (bit b: lanes 4b .. 4b+3 of the row) take src from their partner,
+// the others keep old.
+template <int BANKS>
+__device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x128 /* row_ror:8 */, 0xF, BANKS, false);
+}
+
 // NTL: the codes are read with non-temporal loads (a pool whose KV heads never
 // share a 128-byte line).  FOLD: the launch also takes each request's new
 // token (see kFold below); a separate instantiation, so that the plain stage 1
@@ -464,19 +472,49 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
 #pragma unroll
         for (int t = 0; t < kSteps; ++t) {
           const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
-          const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
-          const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
+          if constexpr (C::STREAM) {
+            // Whole 128-byte lines per load (measured faster for grids of
+            // several rounds): K load h of 16-key block b reads keys
+            // 16b + 8h + (n & 7), 16-byte chunk j + 4 (n >> 3) -- 8 keys x 128 B;
+            // V load q reads keys 2q + (n >> 3) (k-slot order), 16 bytes at
+            // 16 (n & 7) -- 8 keys x 128 B.  Lanes n and n ^ 8 then trade the
+            // halves each needs (see the swaps after the loads land).
+            const int hi = n >> 3;
+            const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
+            const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
+            const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-          for (int c = 0; c < C::kKC; ++c) {
-            kr[t][0][c] = load_code16<NTL>(kbase + r0 + 64 * c);
-            kr[t][1][c] = load_code16<NTL>(kbase + r1 + 64 * c);
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const uint64_t r = (uint64_t)(uint32_t)rw[16 * b + 8 * h + (n & 7)] * code_row_stride;
+                kr[t][b][h] = load_code16<NTL>(k_codes + g * D + r + 16 * j + 64 * hi);
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = hi ? vrow[2 * q + 1] : vrow[2 * q];
+              const u32x4 u = load_code16<NTL>(v_codes + g * D + (uint64_t)(uint32_t)row * code_row_stride + 16 * (n & 7));
+              vr[t][2 * q][0] = u.x;
+              vr[t][2 * q][1] = u.y;
+              vr[t][2 * q + 1][0] = u.z;
+              vr[t][2 * q + 1][1] = u.w;
+            }
+          } else {
+            const uint64_t r0 = (uint64_t)(uint32_t)rw[n] * code_row_stride;
+            const uint64_t r1 = (uint64_t)(uint32_t)rw[16 + n] * code_row_stride;
+#pragma unroll
+            for (int c = 0; c < C::kKC; ++c) {
+              kr[t][0][c] = load_code16<NTL>(kbase + r0 + 64 * c);
+              kr[t][1][c] = load_code16<NTL>(kbase + r1 + 64 * c);
+            }
+            const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
+            const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
+            const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              load_v_words<C::kVW, NTL>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
           }
-          const int4 va = *reinterpret_cast<const int4*>(rw + 4 * j);
-          const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
-          const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-          for (int r = 0; r < 8; ++r)
-            load_v_words<C::kVW, NTL>(vbase + (uint64_t)(uint32_t)vrow[r] * code_row_stride, vr[t][r]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -495,6 +533,36 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
       auto step = [&](auto stc) {
         constexpr int st = decltype(stc)::value;
         const int t0 = k0 + st * kDecodeTileKeys;
+        if constexpr (C::STREAM) {
+          // Whole-line loads: lane n < 8 holds its own K chunk j (load 0) and
+          // chunk j of key n + 8 (load 1); lane n + 8 holds chunk j + 4 of key
+          // n (load 0) and its own chunk j + 4 (load 1).  After the trade every
+          // lane holds chunks j and j + 4 of key n, as the MFMA rows need.
+          // V: lane n < 8 loaded bytes 16 (n & 7) .. + 15 of key 2q, lane n + 8
+          // those of key 2q + 1; lane n keeps columns d = 16 (n & 7) + 8 (n >> 3)
+          // .. + 7 of both keys.
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const u32x4 l0 = kr[st][b][0], l1 = kr[st][b][1];
+            u32x4 a, c;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              a[w] = swap8_into<0xC>(l0[w], l1[w]);
+              c[w] = swap8_into<0x3>(l1[w], l0[w]);
+            }
+            kr[st][b][0] = a;
+            kr[st][b][1] = c;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo0 = vr[st][2 * q][0], lo1 = vr[st][2 * q][1];
+            const uint32_t hi0 = vr[st][2 * q + 1][0], hi1 = vr[st][2 * q + 1][1];
+            vr[st][2 * q][0] = swap8_into<0xC>(lo0, hi0);
+            vr[st][2 * q][1] = swap8_into<0xC>(lo1, hi1);
+            vr[st][2 * q + 1][0] = swap8_into<0x3>(hi0, lo0);
+            vr[st][2 * q + 1][1] = swap8_into<0x3>(hi1, lo1);
+          }
+        }
         // S^T = K * Q^T: lane (n, j) holds chunks j + 4c of keys n (block 0)
         // and 16+n (block 1).  Each K operand is widened once for all tiles.
         f32x4 s0[NT], s1[NT];
@@ -719,7 +787,10 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
         if (c >= n_cols || !owner) continue;
         const int i = C::MULTI ? (c >> g_shift) : 0;
         const int dp = 4 * (idx & 31);
-        const int d = kNB * (dp >> 3) + 8 * half + (dp & 7);
+        // LDS column 8 n' + e holds lane n''s O column: d = kNB n' + 8 half + e,
+        // or 16 (n' & 7) + 8 (n' >> 3) + e for the whole-line V loads.
+        const int d = C::STREAM ? 16 * ((dp >> 3) & 7) + 8 * (dp >> 6) + (dp & 7)
+                                : kNB * (dp >> 3) + 8 * half + (dp & 7);
         float M = sm_m[0][col];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][col]);
