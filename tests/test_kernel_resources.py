@@ -16,7 +16,7 @@ from fp8_kv_cache_row_amd import build as B
 def _resources(src, tmp_path):
     out = tmp_path / (os.path.basename(src) + ".o")
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
-    cmd = [B.HIPCC, *flags, "-c", "-I", B.INCLUDE, "-I", B.CSRC, src, "-o", str(out),
+    cmd = [B.HIPCC, *flags, *B.source_flags(src), "-c", "-I", B.INCLUDE, "-I", B.CSRC, src, "-o", str(out),
            "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
