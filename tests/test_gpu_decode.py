@@ -195,6 +195,24 @@ def test_batched_16_requests_gqa4():
             assert_close(out[b], ref[b], f"  request {b} (L={case.seq_lens[b]})")
 
 
+def test_batched_16_requests_every_pool_layout():
+    """The batch runs the streaming stage-1 shape, which reads whole 128-byte
+    key lines and trades halves between lanes: with non-temporal loads where
+    every KV head's rows fill whole lines (the 1,152-byte records, the split
+    code record, the separate arrays) and plain loads otherwise (the unpadded
+    1,056-byte and the 1,088-byte records).  Every layout against the oracle."""
+    case = wl.batched_decode(0)
+    ref = _oracle_decode(case)
+    for layout in ("interleaved128", "interleaved", "interleaved64", "split"):
+        say(f"decode 16 requests, GQA 4, layout={layout}")
+        pool = build_pool(case, layout)
+        out = bf16_to_f64(run_decode(pool, case))
+        assert_close(out, ref, f"batched layout={layout}")
+        for b in range(case.batch):
+            assert_close(out[b], ref[b], f"  {layout} request {b} (L={case.seq_lens[b]})")
+        del pool
+
+
 @pytest.mark.parametrize("kind", ["layer", "batch", "layer_one_split"])
 @pytest.mark.parametrize("k0", [1024.0, 196.0])
 @pytest.mark.parametrize("fmt", ["e4m3", "int8"])
