@@ -474,8 +474,8 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
           const int32_t* rw = &s_rows[wave][t * kDecodeTileKeys];
           if constexpr (C::STREAM) {
             // Whole 128-byte lines per load (measured faster for grids of
-            // several rounds): K load h of 16-key block b reads keys
-            // 16b + 8h + (n & 7), 16-byte chunk j + 4 (n >> 3) -- 8 keys x 128 B;
+            // several rounds): K load h of 16-key block kb reads keys
+            // 16 kb + 8h + (n & 7), 16-byte chunk j + 4 (n >> 3) -- 8 keys x 128 B;
             // V load q reads keys 2q + (n >> 3) (k-slot order), 16 bytes at
             // 16 (n & 7) -- 8 keys x 128 B.  Lanes n and n ^ 8 then trade the
             // halves each needs (see the swaps after the loads land).
@@ -484,11 +484,11 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
             const int4 vb = *reinterpret_cast<const int4*>(rw + 16 + 4 * j);
             const int vrow[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
-                const uint64_t r = (uint64_t)(uint32_t)rw[16 * b + 8 * h + (n & 7)] * code_row_stride;
-                kr[t][b][h] = load_code16<NTL>(k_codes + g * D + r + 16 * j + 64 * hi);
+                const uint64_t r = (uint64_t)(uint32_t)rw[16 * kb + 8 * h + (n & 7)] * code_row_stride;
+                kr[t][kb][h] = load_code16<NTL>(k_codes + g * D + r + 16 * j + 64 * hi);
               }
             }
 #pragma unroll
@@ -542,16 +542,16 @@ __global__ __launch_bounds__(C::kBlock) __attribute__((amdgpu_waves_per_eu(C::kW
           // those of key 2q + 1; lane n keeps columns d = 16 (n & 7) + 8 (n >> 3)
           // .. + 7 of both keys.
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const u32x4 l0 = kr[st][b][0], l1 = kr[st][b][1];
+          for (int kb = 0; kb < 2; ++kb) {
+            const u32x4 l0 = kr[st][kb][0], l1 = kr[st][kb][1];
             u32x4 a, c;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
               a[w] = swap8_into<0xC>(l0[w], l1[w]);
               c[w] = swap8_into<0x3>(l1[w], l0[w]);
             }
-            kr[st][b][0] = a;
-            kr[st][b][1] = c;
+            kr[st][kb][0] = a;
+            kr[st][kb][1] = c;
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
